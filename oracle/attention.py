@@ -1,0 +1,168 @@
+"""fp64 reference attention (test infrastructure only; see the package docstring).
+
+Every function here is the textbook definition written out, with no tiling,
+no online softmax and no reordering: a row's logits are formed in full, the
+row maximum is subtracted (which leaves softmax unchanged), exponentiated,
+normalised and multiplied by V.  Query rows are processed in chunks only to
+bound memory; rows are independent, so chunking changes nothing.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact upcast of an fp16/bf16/fp32/fp64 tensor or array to float64."""
+    if isinstance(x, np.ndarray):
+        return x.astype(np.float64)
+    return x.detach().to("cpu").to(torch.float64).numpy()
+
+
+def n_visible(Sq: int, Skv: int, causal: bool) -> np.ndarray:
+    """Number of leading keys each query row may attend to.
+
+    Non-causal: all Skv keys.  Causal, bottom-right aligned: query i sees keys
+    j <= i + (Skv - Sq), i.e. ``i + Skv - Sq + 1`` keys, clipped to [0, Skv].
+    When Sq == Skv this is the usual lower-triangular mask.
+    """
+    i = np.arange(Sq, dtype=np.int64)
+    if not causal:
+        return np.full(Sq, Skv, dtype=np.int64)
+    return np.clip(i + (Skv - Sq) + 1, 0, Skv)
+
+
+def attention_probs(q_rows: np.ndarray, keys: np.ndarray, scale: float,
+                    visible: np.ndarray) -> np.ndarray:
+    """Softmax weights P [n, Skv] of query rows [n, D] against keys [Skv, D].
+
+    Row r attends to keys 0 .. visible[r]-1.  A row with no visible key gets
+    all-zero weights (its output is defined as 0).
+    """
+    skv = keys.shape[0]
+    logits = scale * (q_rows @ keys.T)
+    mask = np.arange(skv)[None, :] < np.asarray(visible)[:, None]
+    logits = np.where(mask, logits, -np.inf)
+    row_max = logits.max(axis=1, keepdims=True) if skv else np.full((len(q_rows), 1), -np.inf)
+    row_max = np.where(np.isfinite(row_max), row_max, 0.0)
+    w = np.exp(logits - row_max)
+    denom = w.sum(axis=1, keepdims=True)
+    return np.divide(w, denom, out=np.zeros_like(w), where=denom > 0)
+
+
+def attend_rows(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
+                visible: np.ndarray) -> np.ndarray:
+    """O rows [n, D] = P @ V for query rows [n, D] (all float64)."""
+    p = attention_probs(q_rows, keys, scale, visible)
+    return p @ values
+
+
+def _bhsd(x: np.ndarray, layout: str) -> np.ndarray:
+    if layout == "BHSD":
+        return x
+    if layout == "BSHD":
+        return x.transpose(0, 2, 1, 3)
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def sdpa(q, k, v, *, causal: bool, scale: float | None = None, layout: str = "BHSD",
+         chunk: int = 2048) -> np.ndarray:
+    """Full attention output in float64, in the inputs' layout.
+
+    q: [B,H,Sq,D] (BHSD) or [B,Sq,H,D] (BSHD); k, v likewise with Skv.
+    """
+    qf, kf, vf = (_bhsd(to_f64(t), layout) for t in (q, k, v))
+    B, H, Sq, D = qf.shape
+    Skv = kf.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    out = np.zeros((B, H, Sq, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Sq, chunk):
+                r1 = min(Sq, r0 + chunk)
+                out[b, h, r0:r1] = attend_rows(qf[b, h, r0:r1], kf[b, h], vf[b, h], scale, vis[r0:r1])
+    return _bhsd(out, layout)
+
+
+def sdpa_rows(q, k, v, rows, *, causal: bool, scale: float | None = None,
+              layout: str = "BHSD") -> np.ndarray:
+    """Attention output [len(rows), D] for selected query rows ``(b, h, i)``.
+
+    Used at full problem size, where the whole output is too costly for the
+    CPU: each selected row is computed exactly as ``sdpa`` would.
+    """
+    rows = [tuple(int(x) for x in r) for r in rows]
+    if layout == "BHSD":
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+
+        def head(t, b, h):
+            return t[b, h]
+    elif layout == "BSHD":
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+
+        def head(t, b, h):
+            return t[b, :, h]
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    groups: dict = {}
+    for n, (b, h, i) in enumerate(rows):
+        groups.setdefault((b, h), []).append((n, i))
+    for (b, h), items in groups.items():
+        kf = to_f64(head(k, b, h))
+        vf = to_f64(head(v, b, h))
+        qh = head(q, b, h)
+        idx = np.array([i for _, i in items])
+        qf = to_f64(qh[torch.as_tensor(idx)] if isinstance(qh, torch.Tensor) else qh[idx])
+        res = attend_rows(qf, kf, vf, scale, vis[idx])
+        for (n, _), r in zip(items, res):
+            out[n] = r
+    return out
+
+
+def gather_sequence(cache, page_row, n_tokens: int, page_size: int):
+    """Token-major [n_tokens, H, D] view of one sequence in a paged cache.
+
+    Token t lives in page ``page_row[t // page_size]`` at slot ``t % page_size``;
+    only the first ceil(n_tokens / page_size) page-table entries are read.
+    """
+    n_pages = -(-n_tokens // page_size)
+    pages = torch.as_tensor(np.asarray(page_row[:n_pages], dtype=np.int64))
+    sel = cache[pages]                       # [n_pages, page_size, H, D]
+    return sel.reshape(n_pages * page_size, *sel.shape[2:])[:n_tokens]
+
+
+def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: float | None = None,
+                 batch_indices=None) -> np.ndarray:
+    """Decode attention (one query per sequence) through a page table, float64.
+
+    q: [B, H, D]; k_cache, v_cache: [num_pages, page_size, H, D];
+    page_table: [B, max_pages] int; seq_lens: [B] int.  Returns [B, H, D]
+    (or [len(batch_indices), H, D]).
+    """
+    B, H, D = q.shape
+    page_size = int(k_cache.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    table = np.asarray(page_table.cpu() if isinstance(page_table, torch.Tensor) else page_table)
+    lens = np.asarray(seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens)
+    bs = range(B) if batch_indices is None else list(batch_indices)
+    out = np.zeros((len(bs), H, D), dtype=np.float64)
+    for n_out, b in enumerate(bs):
+        n = int(lens[b])
+        kf = to_f64(gather_sequence(k_cache, table[b], n, page_size))   # [n, H, D]
+        vf = to_f64(gather_sequence(v_cache, table[b], n, page_size))
+        qf = to_f64(q[b])                                                # [H, D]
+        for h in range(H):
+            out[n_out, h] = attend_rows(qf[h:h + 1], kf[:, h], vf[:, h], scale,
+                                        np.array([n]))[0]
+    return out

@@ -1,0 +1,44 @@
+"""Writes tests/golden/oracle_tiny.json: fp64 oracle outputs on tiny seeded inputs.
+
+Calls only ``oracle`` and ``workloads``.  The stored values guard the oracle
+against silent drift: a later change to its arithmetic must change this file
+in the same commit, with the reason.  Run from the repository root:
+
+    python tests/golden/make_golden.py
+"""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle      # noqa: E402
+import workloads   # noqa: E402
+
+CASES = [
+    dict(B=1, H=2, Sq=5, Skv=7, D=4, dtype="f16", layout="BHSD", causal=True, seed=1001),
+    dict(B=1, H=1, Sq=6, Skv=6, D=8, dtype="bf16", layout="BSHD", causal=False, seed=1002),
+]
+DECODE = dict(B=3, H=2, D=4, dtype="f16", page_size=16, num_pages=8, seed=1003,
+              seq_lens=[1, 16, 21])
+
+
+def build():
+    out = {"prefill": [], "decode": None}
+    for c in CASES:
+        q, k, v = workloads.prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                           c["layout"], seed=c["seed"])
+        o = oracle.sdpa(q, k, v, causal=c["causal"], layout=c["layout"])
+        out["prefill"].append(dict(case=c, out=o.round(15).tolist()))
+    b = workloads.paged_decode_inputs(**DECODE)
+    o = oracle.paged_decode(b.q, b.k_cache, b.v_cache, b.page_table, b.seq_lens)
+    out["decode"] = dict(case=DECODE, out=o.round(15).tolist())
+    return out
+
+
+if __name__ == "__main__":
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_tiny.json")
+    with open(path, "w") as f:
+        json.dump(build(), f, indent=1)
+    print("wrote", path)

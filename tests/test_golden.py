@@ -1,0 +1,17 @@
+"""The oracle still reproduces the stored outputs of tests/golden/make_golden.py (CPU only)."""
+import json
+import os
+
+import numpy as np
+
+import golden_loader
+
+
+def test_oracle_matches_stored_golden():
+    stored = golden_loader.load()
+    fresh = golden_loader.rebuild()
+    for s, f in zip(stored["prefill"], fresh["prefill"]):
+        assert s["case"] == f["case"]
+        np.testing.assert_allclose(np.array(f["out"]), np.array(s["out"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(np.array(fresh["decode"]["out"]), np.array(stored["decode"]["out"]),
+                               rtol=0, atol=1e-14)

@@ -1,0 +1,96 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Every mutation below is a plausible slip in an attention reference: a
+top-left instead of bottom-right causal offset, an off-by-one in the visible
+key count, a dropped or negated scale, K and V swapped, softmax over the wrong
+axis, and two wrong page-table gathers.  The test patches the mutated
+function into the oracle module, runs the pins named for it, and requires at
+least one of them to raise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as oa
+import oracle_pins as pins
+
+_orig_n_visible = oa.n_visible
+_orig_probs = oa.attention_probs
+_orig_attend = oa.attend_rows
+
+
+def _top_left(Sq, Skv, causal):
+    i = np.arange(Sq, dtype=np.int64)
+    return np.full(Sq, Skv, dtype=np.int64) if not causal else np.clip(i + 1, 0, Skv)
+
+
+def _off_by_one(Sq, Skv, causal):
+    v = _orig_n_visible(Sq, Skv, causal)
+    return np.clip(v - 1, 0, Skv) if causal else v
+
+
+def _no_scale(q_rows, keys, scale, visible):
+    return _orig_probs(q_rows, keys, 1.0, visible)
+
+
+def _neg_scale(q_rows, keys, scale, visible):
+    return _orig_probs(q_rows, keys, -scale, visible)
+
+
+def _swap_kv(q_rows, keys, values, scale, visible):
+    return _orig_probs(q_rows, values, scale, visible) @ keys
+
+
+def _wrong_axis(q_rows, keys, scale, visible):
+    skv = keys.shape[0]
+    logits = scale * (q_rows @ keys.T)
+    mask = np.arange(skv)[None, :] < np.asarray(visible)[:, None]
+    w = np.where(mask, np.exp(logits - logits.max()), 0.0)
+    return w / w.sum(axis=0, keepdims=True).clip(min=1e-300)
+
+
+def _gather_slot_major(cache, page_row, n_tokens, page_size):
+    n_pages = -(-n_tokens // page_size)
+    pages = torch.as_tensor(np.asarray(page_row[:n_pages], dtype=np.int64))
+    sel = cache[pages].transpose(0, 1)          # slot-major: wrong token order
+    return sel.reshape(n_pages * page_size, *sel.shape[2:])[:n_tokens]
+
+
+def _gather_from_end(cache, page_row, n_tokens, page_size):
+    n_pages = -(-n_tokens // page_size)
+    pages = torch.as_tensor(np.asarray(page_row[len(page_row) - n_pages:], dtype=np.int64))
+    sel = cache[pages]
+    return sel.reshape(n_pages * page_size, *sel.shape[2:])[:n_tokens]
+
+
+MUTATIONS = [
+    ("n_visible", _top_left, [pins.check_library_sdpa, pins.check_bruteforce]),
+    ("n_visible", _off_by_one, [pins.check_causal_row0, pins.check_library_sdpa]),
+    ("attention_probs", _no_scale, [pins.check_library_sdpa, pins.check_two_keys]),
+    ("attention_probs", _neg_scale, [pins.check_library_sdpa, pins.check_dominant_key]),
+    ("attend_rows", _swap_kv, [pins.check_ones_v, pins.check_library_sdpa]),
+    ("attention_probs", _wrong_axis, [pins.check_ones_v, pins.check_probs_rows_sum_to_one]),
+    ("gather_sequence", _gather_slot_major, [pins.check_decode_library]),
+    ("gather_sequence", _gather_from_end, [pins.check_decode_library,
+                                           pins.check_decode_matches_prefill_row]),
+]
+
+
+@pytest.mark.parametrize("name,bad,checks", MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, bad, checks):
+    monkeypatch.setattr(oa, name, bad)
+    caught = []
+    for check in checks:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError, RuntimeError) as e:
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"planted mistake {bad.__name__} in {name} passed every pin"
+
+
+def test_unmutated_oracle_passes_the_same_checks():
+    for _, _, checks in MUTATIONS:
+        for check in checks:
+            check()
