@@ -1,0 +1,195 @@
+"""Python binding of the MI355X attention library (libmi355attn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``.  PyTorch supplies
+device memory and the current stream; nothing here computes attention, and
+there is no CPU fallback: if the shared library is missing the calls raise.
+
+Low-level functions carry the C names (``attn_prefill``,
+``attn_paged_decode``, ``attn_paged_decode_workspace_size``,
+``attn_paged_decode_num_splits``, ``attn_status_string``) and take tensors
+or raw integer pointers; ``prefill`` and ``paged_decode`` are conveniences
+that derive the sizes from tensor shapes and allocate the output.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmi355attn.so")
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = range(5)
+ATTN_BHSD, ATTN_BSHD = 0, 1
+ATTN_F16, ATTN_BF16 = 0, 1
+LAYOUTS = {"BHSD": ATTN_BHSD, "BSHD": ATTN_BSHD}
+
+# Every symbol include/attn.h declares, with its ctypes signature.
+_VP, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_prefill": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
+    "attn_paged_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "attn_paged_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
+                               _VP, _SZ, _VP]),
+    "attn_paged_decode_num_splits": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I)]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+
+
+def load_library(path: str | None = None):
+    """Load libmi355attn.so (built by ``build()``); raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with "
+                          "`python -m attention_flash_attn_prefill_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 or bfloat16)")
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_prefill(q, k, v, o, B, H, Sq, Skv, D, layout, dtype, causal, scale, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Sq, Skv, D,
+                                       layout, dtype, int(bool(causal)), float(scale),
+                                       _stream(stream))
+
+
+def attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size) -> int:
+    return int(load_library().attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq,
+                                                               page_size))
+
+
+def attn_paged_decode_num_splits(B, H, max_pages_per_seq, page_size):
+    """(n_splits, tokens_per_split) of the decode split plan."""
+    tps = ctypes.c_int(0)
+    n = load_library().attn_paged_decode_num_splits(B, H, max_pages_per_seq, page_size,
+                                                    ctypes.byref(tps))
+    return int(n), int(tps.value)
+
+
+def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, o, B, H, D, page_size,
+                      num_pages, max_pages_per_seq, dtype, scale, workspace, workspace_bytes,
+                      stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_paged_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H, D,
+                                            page_size, num_pages, max_pages_per_seq, dtype,
+                                            float(scale), _ptr(workspace), int(workspace_bytes),
+                                            _stream(stream))
+
+
+def _check(status, where):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, stream=None):
+    """O = softmax(Q K^T * scale [+ causal mask]) V on the GPU.
+
+    q: [B,H,Sq,D] (layout "BHSD") or [B,Sq,H,D] ("BSHD"); k, v likewise with
+    Skv keys; fp16 or bf16 CUDA tensors, contiguous.  Returns o like q.
+    """
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if layout == "BHSD":
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+        kv_shape = (B, H, Skv, D)
+    else:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+        kv_shape = (B, Skv, H, D)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"k and v must have shape {kv_shape}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    _check(attn_prefill(q, k, v, o, B, H, Sq, Skv, D, LAYOUTS[layout], _dtype_code(q),
+                        causal, scale, stream), "attn_prefill")
+    return o
+
+
+def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=None,
+                 workspace=None, stream=None):
+    """Decode attention of q [B,H,D] against a paged cache [num_pages, 16, H, D].
+
+    page_table [B, max_pages] and seq_lens [B] are int32 GPU tensors.  The
+    workspace (a uint8 GPU tensor) is allocated here if not given.
+    """
+    import torch
+    B, H, D = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (num_pages, page_size, H, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H, D]")
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("page_table and seq_lens must be int32")
+    for t in (q, k_cache, v_cache, page_table, seq_lens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous GPU tensors")
+    max_pages = page_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = attn_paged_decode_workspace_size(B, H, D, max_pages, page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check(attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, o, B, H, D, page_size,
+                             num_pages, max_pages, _dtype_code(q), scale, workspace,
+                             workspace.numel() * workspace.element_size(), stream),
+           "attn_paged_decode")
+    return o

@@ -1,0 +1,176 @@
+// C ABI of the attention library (include/attn.h): argument validation, launch
+// planning and kernel dispatch.  Every check runs before the first HIP call,
+// and nothing here allocates, synchronises or reads device memory, so the
+// entry points are safe under HIP graph capture (the pages' lesson on launch
+// paths that break stream capture: "[FlyDSL] FP8 MQA logits improvements for
+// gfx950", Known limitation).
+#include "attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace mi355_attn;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Softmax scale -> exponent multiplier c = scale * log2(e).  A zero scale
+// (uniform weights) becomes the smallest positive normal float, which gives
+// the same result (every score * c rounds exp2 to exactly 1) while keeping
+// masked scores at -inf rather than -inf * 0 = NaN.
+float exp2_multiplier(float scale) {
+  const float c = scale * kLog2e;
+  return c > 0.f ? c : 1.17549435e-38f;
+}
+
+struct SplitPlan {
+  int n_splits;
+  int tokens_per_split;
+};
+
+// Tokens per split: a multiple of two pages (the kernel's batch), chosen so
+// the grid holds enough work items to fill 256 CUs even when sequences are
+// short, while keeping the partial-result traffic (one D+1 fp32 row per
+// split) below about 2% of the KV bytes at the default of 256 tokens.
+SplitPlan plan_splits(int B, int H, int max_pages, int page_size) {
+  SplitPlan p{0, 0};
+  if (B <= 0 || H <= 0 || max_pages <= 0 || page_size != kDecodePageSize) return p;
+  const int64_t max_tokens = (int64_t)max_pages * page_size;
+  const int64_t head_groups = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
+  int tps = 256;
+  auto splits = [&](int t) { return (max_tokens + t - 1) / t; };
+  while (tps > 2 * kDecodePageSize && (int64_t)B * head_groups * splits(tps) < 8192) tps /= 2;
+  while (splits(tps) > 4096) tps *= 2;
+  p.tokens_per_split = tps;
+  p.n_splits = (int)splits(tps);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                 int Skv, int D, int layout, int dtype, int causal, float scale,
+                 hipStream_t stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
+  if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * Sq == 0) return ATTN_OK;  // nothing to compute
+  if (!q || !o) return ATTN_E_INVALID;
+  if (Skv > 0 && (!k || !v)) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(o) || (Skv > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_E_INVALID;
+
+  // In-head offsets (row * row_stride) are 32-bit in the kernel.
+  const int64_t row_stride = layout == ATTN_BHSD ? D : (int64_t)H * D;
+  const int64_t smax = Sq > Skv ? Sq : Skv;
+  if (smax * row_stride >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  const int64_t n_mtiles = (Sq + kPrefillBM - 1) / kPrefillBM;
+  const int64_t total = (int64_t)B * H * n_mtiles;
+  if (total >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.H = H;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.n_mtiles = (int)n_mtiles;
+  a.total_tiles = (int)total;
+  if (layout == ATTN_BHSD) {
+    a.q_sb = (int64_t)H * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)H * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
+  } else {
+    a.q_sb = (int64_t)Sq * H * D; a.q_sh = D; a.q_ss = H * D;
+    a.k_sb = (int64_t)Skv * H * D; a.k_sh = D; a.k_ss = H * D;
+  }
+  a.c = exp2_multiplier(scale);
+  a.causal_off = Skv - Sq;
+  hipError_t e = launch_prefill(D, dtype == ATTN_BF16, causal != 0, a, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
+                                 int* tokens_per_split) {
+  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+  if (tokens_per_split) *tokens_per_split = p.tokens_per_split;
+  return p.n_splits;
+}
+
+size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
+                                        int page_size) {
+  if (D != 64 && D != 128) return 0;
+  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+  if (p.n_splits == 0) return 0;
+  const size_t rows = (size_t)B * H * p.n_splits;
+  // partial outputs [B,H,S,D] fp32, then log-sum-exps [B,H,S] fp32, 256-B aligned
+  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
+  return o_bytes + rows * sizeof(float);
+}
+
+int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, void* o, int B, int H,
+                      int D, int page_size, int num_pages, int max_pages_per_seq, int dtype,
+                      float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return ATTN_OK;
+  if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
+  if (B > 65535) return ATTN_E_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return ATTN_E_INVALID;
+  if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
+
+  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+  if (p.n_splits == 0 || p.n_splits > 65535) return ATTN_E_UNSUPPORTED;
+  const size_t need = attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size);
+  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_E_INVALID;
+
+  const size_t rows = (size_t)B * H * p.n_splits;
+  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.o = static_cast<uint16_t*>(o);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  a.B = B;
+  a.H = H;
+  a.max_pages = max_pages_per_seq;
+  a.n_splits = p.n_splits;
+  a.tokens_per_split = p.tokens_per_split;
+  a.c = exp2_multiplier(scale);
+  hipError_t e = launch_paged_decode(D, dtype == ATTN_BF16, a, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI host code (api.cpp) and the HIP kernel
+// translation units (prefill.hip, decode.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mi355_attn {
+
+// Query rows per prefill workgroup, keys per KV tile, threads per workgroup.
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 64;
+constexpr int kPrefillThreads = 256;
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int H, Sq, Skv;
+  int n_mtiles;        // ceil(Sq / kPrefillBM)
+  int total_tiles;     // B * H * n_mtiles  (= grid size)
+  int64_t q_sb, q_sh;  // element strides of q and o between batches / heads
+  int q_ss;            // element stride between query rows
+  int64_t k_sb, k_sh;  // element strides of k and v
+  int k_ss;
+  float c;             // scale * log2(e)
+  int causal_off;      // Skv - Sq (bottom-right causal alignment)
+};
+
+hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, hipStream_t s);
+
+// Paged decode: one wave per (sequence, head, split); four heads per workgroup.
+constexpr int kDecodeHeadsPerWG = 4;
+constexpr int kDecodePageSize = 16;
+
+struct DecodeArgs {
+  const uint16_t* q;          // [B, H, D]
+  const uint16_t* k_cache;    // [num_pages, 16, H, D]
+  const uint16_t* v_cache;
+  const int32_t* page_table;  // [B, max_pages]
+  const int32_t* seq_lens;    // [B]
+  uint16_t* o;                // [B, H, D]
+  float* part_o;              // [B, H, n_splits, D]   (workspace)
+  float* part_lse;            // [B, H, n_splits]      (workspace; log2 domain)
+  int B, H, max_pages, n_splits, tokens_per_split;
+  float c;                    // scale * log2(e)
+};
+
+hipError_t launch_paged_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t s);
+
+}  // namespace mi355_attn

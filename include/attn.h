@@ -1,0 +1,137 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused-attention library.
+ *
+ * Two operations, both the plain scaled-dot-product attention
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * <q_i, k_j> + M_ij) * v_j
+ *
+ * (flash-style prefill: "WAVE: A Symbolic Python DSL and Compiler for High
+ * Performance Machine Learning (MLSys 2026)", core method, and its attention
+ * experiments over BHSD and BSHD layouts; paged flash decoding: "Wave February
+ * 2025 Release", FlashDecoding list).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a device pointer owned by the caller.  The library never
+ *     allocates, frees, synchronises, or reads device memory on the host, so
+ *     every call is safe inside HIP graph capture.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous;
+ *     a kernel fault surfaces at the caller's next synchronisation.
+ *   - Return codes are synchronous.  All argument checks run before any HIP
+ *     call, so they also work on a host without a GPU.  After a launch,
+ *     hipGetLastError() is mapped to ATTN_E_HIP.
+ *   - Tensors are densely packed in the stated layout; outputs must not alias
+ *     inputs; pointers are 16-byte aligned.
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,      /* null pointer, negative size, bad scale, misaligned pointer */
+  ATTN_E_UNSUPPORTED = 2,  /* valid request this build does not implement (head dim, page size) */
+  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than attn_paged_decode_workspace_size */
+  ATTN_E_HIP = 4           /* the HIP runtime reported an error at launch */
+};
+
+/* Memory layouts of q, k, v and o. */
+enum {
+  ATTN_BHSD = 0,  /* [B, H, S, D], D contiguous */
+  ATTN_BSHD = 1   /* [B, S, H, D], D contiguous */
+};
+
+/* Element types of q, k, v, o (and of the KV cache). */
+enum {
+  ATTN_F16 = 0,
+  ATTN_BF16 = 1
+};
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * Fused scaled-dot-product attention prefill.
+ *
+ *   q: [B, H, Sq, D] (BHSD) or [B, Sq, H, D] (BSHD)
+ *   k, v: the same with Skv keys
+ *   o: output, same shape, layout and dtype as q
+ *   D: head dimension, 64 or 128 (else ATTN_E_UNSUPPORTED)
+ *   dtype: ATTN_F16 or ATTN_BF16 (q, k, v and o share it)
+ *   causal: nonzero for the causal mask, aligned bottom-right: query i sees
+ *           keys j <= i + (Skv - Sq).  A query that sees no key gets O = 0.
+ *   scale: softmax scale, finite and >= 0 (commonly 1/sqrt(D)).
+ *
+ * Arithmetic: Q.K^T in the input dtype on MFMA with fp32 accumulation; the
+ * online softmax in fp32 (base-2 exponent, scale folded in fp32, never into
+ * the fp16/bf16 inputs); P rounded to fp16 (round to nearest even) and P.V on
+ * fp16 MFMA with fp32 accumulation; O rounded to the input dtype.  For bf16
+ * inputs V is converted to fp16 when it is staged, which is exact for
+ * 2^-14 <= |v| <= 65504; precondition for bf16: |v| <= 65504.
+ *
+ * B, H, Sq or Skv equal to 0 is valid: with B*H*Sq = 0 nothing is launched and
+ * q/k/v/o may be NULL; with Skv = 0 (and Sq > 0) o is filled with zeros.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 int B, int H, int Sq, int Skv, int D, int layout, int dtype,
+                 int causal, float scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace attn_paged_decode needs for these sizes: the
+ * per-split partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
+ */
+size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
+                                        int page_size);
+
+/*
+ * Split-KV paged flash decoding: one query per sequence against a paged KV cache.
+ *
+ *   q: [B, H, D]
+ *   k_cache, v_cache: [num_pages, page_size, H, D]; token t of sequence b is
+ *       at page page_table[b][t / page_size], slot t % page_size
+ *   page_table: [B, max_pages_per_seq] int32
+ *   seq_lens: [B] int32
+ *   o: [B, H, D] output, dtype as q
+ *   page_size: 16 (else ATTN_E_UNSUPPORTED); D: 64 or 128
+ *   workspace: device scratch of at least
+ *       attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size)
+ *       bytes, owned by the caller; its contents need no initialisation.
+ *
+ * Preconditions (device data; not checked): 0 <= seq_lens[b] <=
+ * max_pages_per_seq * page_size (a longer length is clamped to that bound;
+ * a sequence of length 0 gets O = 0); the first ceil(seq_lens[b] / page_size)
+ * entries of page_table[b] lie in [0, num_pages).  Other page-table entries
+ * and cache slots past seq_lens[b] are never read.
+ *
+ * The KV range of each sequence is cut into splits; each split produces a
+ * partial output and its log-sum-exp, and a combine kernel merges them
+ * (flash decoding; "Wave February 2025 Release", FlashDecoding list; KV split
+ * sized to fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950",
+ * Changes / Host side).  Splits past a sequence's end do no work.
+ */
+int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, void* o,
+                      int B, int H, int D, int page_size, int num_pages,
+                      int max_pages_per_seq, int dtype, float scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Split plan of attn_paged_decode: returns the number of KV splits per
+ * sequence (0 on invalid sizes) and, if tokens_per_split is not NULL, stores
+ * the tokens per split there.  The plan depends only on these host-side
+ * sizes (the host never reads seq_lens), so it is the same for every call
+ * with the same sizes. */
+int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
+                                 int* tokens_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

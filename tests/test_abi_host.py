@@ -1,0 +1,130 @@
+"""C-ABI host logic, without a GPU: the library loads, exports every symbol
+include/attn.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import attention_flash_attn_prefill_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["attn_status_string", "attn_prefill", "attn_paged_decode",
+                            "attn_paged_decode_workspace_size", "attn_paged_decode_num_splits"])
+    assert set(names) == set(attn.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert attn.attn_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert attn.attn_status_string(s) not in ("ok", "unknown status")
+    assert attn.attn_status_string(99) == "unknown status"
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=1, Sq=16, Skv=16, D=128, layout=0, dtype=0,
+             causal=0, scale=0.1, stream=0)
+    a.update(kw)
+    return attn.attn_prefill(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), attn.ATTN_E_INVALID),
+    (dict(Sq=-3), attn.ATTN_E_INVALID),
+    (dict(layout=2), attn.ATTN_E_INVALID),
+    (dict(dtype=7), attn.ATTN_E_INVALID),
+    (dict(scale=float("nan")), attn.ATTN_E_INVALID),
+    (dict(scale=float("inf")), attn.ATTN_E_INVALID),
+    (dict(scale=-0.5), attn.ATTN_E_INVALID),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(D=256), attn.ATTN_E_UNSUPPORTED),
+    (dict(D=0), attn.ATTN_E_INVALID),
+    (dict(q=None), attn.ATTN_E_INVALID),
+    (dict(o=None), attn.ATTN_E_INVALID),
+    (dict(k=None), attn.ATTN_E_INVALID),
+    (dict(q=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(v=FAKE + 2), attn.ATTN_E_INVALID),
+    (dict(layout=1, H=1 << 20, Sq=4096, Skv=4096), attn.ATTN_E_UNSUPPORTED),  # 32-bit offsets
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Sq=0),
+                                dict(B=0, q=None, k=None, v=None, o=None),
+                                dict(Sq=0, q=None, o=None)])
+def test_prefill_empty_is_a_noop(kw):
+    assert _prefill(**kw) == attn.ATTN_OK
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, seq_lens=FAKE, o=FAKE, B=4,
+             H=8, D=128, page_size=16, num_pages=64, max_pages_per_seq=8, dtype=0, scale=0.1,
+             workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return attn.attn_paged_decode(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), attn.ATTN_E_INVALID),
+    (dict(page_size=8), attn.ATTN_E_UNSUPPORTED),
+    (dict(page_size=0), attn.ATTN_E_INVALID),
+    (dict(D=80), attn.ATTN_E_UNSUPPORTED),
+    (dict(dtype=3), attn.ATTN_E_INVALID),
+    (dict(scale=float("nan")), attn.ATTN_E_INVALID),
+    (dict(num_pages=0), attn.ATTN_E_INVALID),
+    (dict(max_pages_per_seq=0), attn.ATTN_E_INVALID),
+    (dict(page_table=None), attn.ATTN_E_INVALID),
+    (dict(seq_lens=FAKE + 2), attn.ATTN_E_INVALID),
+    (dict(k_cache=FAKE + 4), attn.ATTN_E_INVALID),
+    (dict(workspace=None), attn.ATTN_E_WORKSPACE),
+    (dict(workspace_bytes=16), attn.ATTN_E_WORKSPACE),
+    (dict(B=70000), attn.ATTN_E_UNSUPPORTED),
+])
+def test_decode_validation(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_decode_empty_is_a_noop():
+    assert _decode(B=0, q=None, o=None) == attn.ATTN_OK
+    assert _decode(H=0) == attn.ATTN_OK
+
+
+def test_split_plan_and_workspace():
+    n, tps = attn.attn_paged_decode_num_splits(64, 32, 512, 16)
+    assert tps % 32 == 0 and tps >= 32
+    assert n == math.ceil(512 * 16 / tps)
+    ws = attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
+    rows = 64 * 32 * n
+    assert ws >= rows * 129 * 4
+    # a small batch splits finer so the grid still fills the GPU
+    n1, tps1 = attn.attn_paged_decode_num_splits(1, 32, 512, 16)
+    assert tps1 <= tps and n1 >= n
+    assert attn.attn_paged_decode_num_splits(4, 8, 8, 7) == (0, 0)
+    assert attn.attn_paged_decode_workspace_size(4, 8, 96, 8, 16) == 0
+
+
+def test_no_cpu_fallback(tmp_path):
+    with pytest.raises(ImportError):
+        attn.load_library(str(tmp_path / "missing.so"))

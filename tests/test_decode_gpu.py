@@ -1,0 +1,105 @@
+"""GPU parity of attn_paged_decode (through the C ABI) against the fp64 oracle.
+
+The oracle gathers each sequence's K/V through the page table explicitly.
+Full-size workload: every (sequence, head) output is compared.  Edge cases:
+sequence lengths around page and split boundaries, NaN-poisoned unused cache
+slots, bitwise invariance under a page-pool permutation, and split-plan
+invariance within fp32 noise.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_gpu(batch):
+    return {k: getattr(batch, k).cuda() for k in ("q", "k_cache", "v_cache", "page_table",
+                                                 "seq_lens")}
+
+
+def _run(attn, batch, scale=None, page_table=None):
+    print(f"[case] decode B{batch.q.shape[0]} H{batch.q.shape[1]} D{batch.q.shape[2]} "
+          f"{batch.q.dtype} pages{batch.num_pages} lens={batch.seq_lens.tolist()[:8]}...",
+          flush=True)
+    g = _to_gpu(batch)
+    if page_table is not None:
+        g["page_table"] = page_table.cuda()
+    o = attn.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"],
+                          scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _ref(batch, scale=None):
+    return oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                               batch.seq_lens, scale=scale)
+
+
+EDGE_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 1000, 4096, 8191, 8192]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_edge_lengths_nan_poisoned(gpu_lib, D, dtype):
+    H = 6
+    batch = workloads.paged_decode_inputs(B=len(EDGE_LENS), H=H, D=D, dtype=dtype, page_size=16,
+                                          num_pages=2048, max_seq=8192, seed=D + len(dtype),
+                                          seq_lens=EDGE_LENS, fill=float("nan"))
+    o = _run(gpu_lib, batch)
+    assert torch.isfinite(o.float()).all(), "NaN from an unused cache slot leaked into O"
+    assert_parity(o.double().numpy(), _ref(batch), f"edge lengths D{D} {dtype}")
+
+
+def test_decode_one_long_among_short(gpu_lib):
+    lens = [1] * 20 + [8192] + [3] * 11
+    batch = workloads.paged_decode_inputs(B=len(lens), H=8, D=128, page_size=16, num_pages=1024,
+                                          seed=12, seq_lens=lens)
+    assert_parity(_run(gpu_lib, batch).double().numpy(), _ref(batch), "one long among short")
+
+
+def test_decode_pool_permutation_bitwise(gpu_lib):
+    batch = workloads.paged_decode_inputs(B=16, H=8, D=128, page_size=16, num_pages=4096,
+                                          max_seq=3000, seed=21)
+    moved = workloads.permute_pool(batch, seed=99)
+    a = _run(gpu_lib, batch)
+    b = _run(gpu_lib, moved)
+    assert torch.equal(a, b)
+    assert_parity(a.double().numpy(), _ref(batch), "pool permutation")
+
+
+def test_decode_split_plan_invariance(gpu_lib):
+    """Widening the page table (unused columns) changes the split plan, not O."""
+    attn = gpu_lib
+    batch = workloads.paged_decode_inputs(B=2, H=8, D=128, page_size=16, num_pages=2048,
+                                          max_seq=4096, seed=31, seq_lens=[4096, 2500])
+    plan_a = attn.attn_paged_decode_num_splits(2, 8, batch.max_pages_per_seq, 16)
+    wide = torch.full((2, 8192), batch.meta["unused_page"], dtype=torch.int32)
+    wide[:, :batch.max_pages_per_seq] = batch.page_table
+    plan_b = attn.attn_paged_decode_num_splits(2, 8, 8192, 16)
+    assert plan_a[1] != plan_b[1], (plan_a, plan_b)
+    a = _run(attn, batch)
+    b = _run(attn, batch, page_table=wide)
+    assert float((a.double() - b.double()).abs().max()) <= 2e-3
+    assert_parity(b.double().numpy(), _ref(batch), "wide page table")
+
+
+def test_decode_scale(gpu_lib):
+    batch = workloads.paged_decode_inputs(B=4, H=4, D=64, page_size=16, num_pages=256,
+                                          max_seq=700, seed=41)
+    for scale in (0.0, 0.05, 0.4):
+        assert_parity(_run(gpu_lib, batch, scale=scale).double().numpy(),
+                      _ref(batch, scale=scale), f"scale {scale}")
+
+
+def test_decode_full_config4(gpu_lib):
+    batch = workloads.decode_config(4)
+    o = _run(gpu_lib, batch, scale=batch.meta["scale"])
+    ref = _ref(batch, scale=batch.meta["scale"])
+    assert_parity(o.double().numpy(), ref, "config 4 (all sequences and heads)")

@@ -1,0 +1,152 @@
+"""GPU parity of attn_prefill (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs error <= 1e-2 and relative Frobenius error <= 2e-3, over the
+whole output for shapes the oracle finishes in seconds, and over sampled rows
+(computed one by one by the oracle) at the full workload sizes, in the same
+launch configuration the bench times.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(attn, q, k, v, causal, scale, layout):
+    print(f"[case] prefill q{tuple(q.shape)} k{tuple(k.shape)} {q.dtype} {layout} "
+          f"causal={causal}", flush=True)
+    o = attn.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, layout=layout)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+# --------------------------------------------------------------- small shapes
+
+ODD = [
+    # (B, H, Sq, Skv)
+    (2, 3, 300, 300),     # ragged query and key tiles
+    (1, 2, 67, 1500),     # small odd query block, long ragged KV
+    (1, 2, 257, 513),     # causal bottom-right with Sq < Skv
+    (1, 2, 513, 257),     # Sq > Skv: causal rows that see no key give 0
+]
+
+
+@pytest.mark.parametrize("shape", ODD, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_odd_shapes(gpu_lib, shape, D, dtype, layout, causal):
+    B, H, Sq, Skv = shape
+    seed = zlib.crc32(repr((shape, D, dtype, layout, causal)).encode()) % 10000
+    q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, dtype, layout, seed=seed)
+    scale = 1 / math.sqrt(D)
+    o = _run(gpu_lib, q, k, v, causal, scale, layout)
+    ref = oracle.sdpa(q, k, v, causal=causal, scale=scale, layout=layout)
+    assert_parity(_f64(o), ref, f"{shape} D{D} {dtype} {layout} causal={causal}")
+
+
+def test_prefill_config1_full(gpu_lib):
+    q, k, v, m = workloads.prefill_config(1)
+    o = _run(gpu_lib, q, k, v, m["causal"], m["scale"], m["layout"])
+    ref = oracle.sdpa(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"])
+    assert_parity(_f64(o), ref, "config 1 (full tensor)")
+
+
+@pytest.mark.parametrize("Sq,Skv,causal", [(1, 1, False), (1, 1000, True), (1000, 1, True),
+                                          (1, 64, False), (64, 1, False), (128, 128, True)])
+def test_prefill_degenerate_lengths(gpu_lib, Sq, Skv, causal):
+    q, k, v = workloads.prefill_inputs(1, 2, Sq, Skv, 128, "f16", "BHSD", seed=Sq * 7 + Skv)
+    o = _run(gpu_lib, q, k, v, causal, 1 / math.sqrt(128), "BHSD")
+    ref = oracle.sdpa(q, k, v, causal=causal, layout="BHSD")
+    assert_parity(_f64(o), ref, f"Sq{Sq} Skv{Skv} causal={causal}")
+
+
+def test_prefill_empty_and_no_keys(gpu_lib):
+    attn = gpu_lib
+    dev = torch.device("cuda")
+    # B*H*Sq = 0: nothing to do, no launch
+    z = torch.empty((0, 2, 16, 64), dtype=torch.float16, device=dev)
+    assert attn.prefill(z, z, z).shape == z.shape
+    # Skv = 0: every row sees no key, O = 0
+    q = torch.randn((1, 2, 40, 64), device=dev).half()
+    kv = torch.empty((1, 2, 0, 64), dtype=torch.float16, device=dev)
+    o = attn.prefill(q, kv, kv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o) == 0
+
+
+def test_prefill_scale_zero_is_uniform(gpu_lib):
+    q, k, v = workloads.prefill_inputs(1, 2, 100, 300, 64, "f16", "BHSD", seed=5)
+    o = _run(gpu_lib, q, k, v, False, 0.0, "BHSD")
+    ref = oracle.sdpa(q, k, v, causal=False, scale=0.0)
+    assert_parity(_f64(o), ref, "scale 0")
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_ones_v_gives_ones(gpu_lib, dtype):
+    q, k, _ = workloads.prefill_inputs(1, 2, 200, 333, 128, dtype, "BHSD", seed=3)
+    v = torch.ones_like(k)
+    o = _run(gpu_lib, q, k, v, True, 1 / math.sqrt(128), "BHSD")
+    assert float((o.double() - 1).abs().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_causal_row0_is_v0_exactly(gpu_lib, dtype):
+    q, k, v = workloads.prefill_inputs(2, 3, 150, 150, 128, dtype, "BSHD", seed=4)
+    o = _run(gpu_lib, q, k, v, True, 1 / math.sqrt(128), "BSHD")
+    assert torch.equal(o[:, 0], v[:, 0])
+
+
+def test_prefill_layouts_bitwise_equal(gpu_lib):
+    q, k, v = workloads.prefill_inputs(2, 3, 190, 270, 128, "bf16", "BHSD", seed=6)
+    a = _run(gpu_lib, q, k, v, True, 0.1, "BHSD")
+    b = _run(gpu_lib, *(t.transpose(1, 2).contiguous() for t in (q, k, v)), True, 0.1, "BSHD")
+    assert torch.equal(a, b.transpose(1, 2))
+
+
+def test_prefill_deterministic(gpu_lib):
+    q, k, v = workloads.prefill_inputs(1, 4, 256, 512, 128, "f16", "BHSD", seed=8)
+    a = _run(gpu_lib, q, k, v, False, 0.09, "BHSD")
+    b = _run(gpu_lib, q, k, v, False, 0.09, "BHSD")
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------ full workload sizes
+
+def _sample_rows(B, H, Sq, n_random, seed):
+    g = np.random.default_rng(seed)
+    rows = set()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        for i in (0, 1, 127, 128, Sq // 2, Sq - 129, Sq - 128, Sq - 1):
+            rows.add((b, h, i))
+    for _ in range(n_random):
+        rows.add((int(g.integers(B)), int(g.integers(H)), int(g.integers(Sq))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("cfg,n_random", [(2, 384), (3, 384), (5, 256)])
+def test_prefill_full_config_sampled(gpu_lib, cfg, n_random):
+    q, k, v, m = workloads.prefill_config(cfg)
+    o = _run(gpu_lib, q, k, v, m["causal"], m["scale"], m["layout"])
+    rows = _sample_rows(m["B"], m["H"], m["Sq"], n_random, seed=cfg)
+    ref = oracle.sdpa_rows(q, k, v, rows, causal=m["causal"], scale=m["scale"], layout=m["layout"])
+    if m["layout"] == "BHSD":
+        got = torch.stack([o[b, h, i] for b, h, i in rows])
+    else:
+        got = torch.stack([o[b, i, h] for b, h, i in rows])
+    assert torch.isfinite(o.float()).all()
+    assert_parity(_f64(got), ref, f"config {cfg} ({len(rows)} sampled rows)")
