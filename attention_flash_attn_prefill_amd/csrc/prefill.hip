@@ -312,13 +312,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -base));
+        // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
+        // ext-vector *element* (pf[s][j]) as a read of element 0.
+        f16x2 h[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pf[s][j] = pack_f16(e[2 * j], e[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) h[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
+        pf[s] = (u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                        __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
         // row sum of the rounded P (the values P.V actually uses)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pf[s][j]),
-                                         (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run, false);
+          l_run = __builtin_amdgcn_fdot2(h[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
+                                         false);
       }
 
       // O^T += V^T P^T
