@@ -47,9 +47,10 @@ def source_hash(path):
 
 
 def load_traffic(name, src):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<kernel>__<workload>__traffic.json), if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}__traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -95,7 +96,7 @@ def bench_prefill(attn, cfg, steps, warmup):
     tflops = flops / (t["mean_ms"] * 1e-3) / 1e12
     cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "Sq": m["Sq"], "Skv": m["Skv"],
                "D": m["D"], "layout": m["layout"], "causal": m["causal"], "dtype": m["dtype"]}
-    traffic = load_traffic(f"prefill_cfg{cfg}", PREFILL_SRC)
+    traffic = load_traffic(f"prefill_fwd__{m['name']}", PREFILL_SRC)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": traffic}
     del q, k, v, o
@@ -132,11 +133,27 @@ def bench_decode(attn, cfg, steps, warmup):
                "page_size": batch.page_size, "num_pages": batch.num_pages,
                "live_tokens": n_tok, "n_splits": n_splits, "tokens_per_split": tps}
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM, 4), "traffic": load_traffic(f"decode_cfg{cfg}",
-                                                                      DECODE_SRC)}
+            "frac": round(gbs / PEAK_HBM, 4),
+            "traffic": load_traffic(f"decode_split__{batch.meta['name']}", DECODE_SRC)}
     del g, ws, o
     torch.cuda.empty_cache()
     return dict(config=cfg_out, timing=t, bytes_per_step=nbytes, gbs=gbs, roofline=roof)
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy of known size (reads and writes mib MiB each),
+    run so HBM byte counters can be scaled against it."""
+    import torch
+    n = mib * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 3 x neg over {mib} MiB (read {mib} MiB, write {mib} MiB)",
+          file=sys.stderr, flush=True)
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline_prefill(cfg, budget_s=15.0):
@@ -185,6 +202,8 @@ def main():
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -201,6 +220,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
 
     cfgs = [int(c) for c in args.configs.split(",") if c.strip()]
     head_cfg = next((c for c in cfgs if c != 4), 2)
