@@ -21,19 +21,22 @@
 //   * exp(S^T) rounded to fp16 is already laid out as the B operand of
 //     O^T (D x 32) = V^T (D x 64) . P^T (64 x 32): P never round-trips
 //     through LDS.
-// The MFMA sums over k in whatever order the lanes present it, so P^T's
-// k-order (dictated by the accumulator layout) only has to match V^T's.  The
-// V tile is therefore written to LDS transposed ([d][key]) with keys permuted
-// inside each 16-key group so each lane's eight keys are contiguous
-// (one 128-bit LDS read per operand).
+// The A operand V^T needs, per lane, eight keys of one d column of the
+// row-major V tile: two ds_read_b64_tr_b16 per operand (CDNA4's transposing
+// LDS read: within each 16-lane group, lane (r, c) names 4 halves of row r and
+// lane j receives column j of the 4 x 16 block).
 //
-// Memory path: K and V tiles (64 keys) are fetched with 128-bit coalesced
-// global loads into registers while the previous tile computes, then written
-// to a double-buffered LDS pair (one barrier per tile; register staging and
-// double buffering per "Wave February 2025 Release", Multi-Buffering and
-// EvoFormer lists; vectorised/coarsened global reads per the WAVE summary,
-// lowering pipeline).  LDS rows are padded by 16 bytes so the 128-bit operand
-// reads of a wave fall in distinct banks.
+// Memory path: K and V tiles (64 keys x D) go from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (no staging VGPRs, no ds_write, hardware range
+// checking returns zeros past the sequence end), double-buffered so tile t+1
+// streams in while tile t computes, with one barrier per tile (multi-buffering:
+// "Wave February 2025 Release", Multi-Buffering list; 128-bit coalesced global
+// reads: WAVE summary, lowering pipeline, global read coarsening; async
+// global->LDS copies: "[FlyDSL] FP8 MQA logits improvements for gfx950",
+// Changes / Kernel).  The 16-byte chunks of each LDS row are XOR-swizzled by a
+// function of the row; the same XOR is applied to the DMA source address and
+// to the read address, so it must be (and is) its own inverse.  For bf16
+// inputs V is converted to fp16 on the way, so it is staged through VGPRs.
 //
 // Softmax numerics: scores stay fp32; the scale is folded in fp32 as
 // c = scale*log2(e) into one FMA feeding v_exp_f32 (never into fp16/bf16 Q).
@@ -67,12 +70,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 constexpr int NT = kPrefillThreads;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kBufferConfig = 0x00020000;  // raw buffer, 32-bit data format
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
@@ -131,21 +137,34 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x * q + min(x, r) + k;
 }
 
+// XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
+// D = 128 (16 chunks) it is a bijection of the row's low four bits, so 16
+// consecutive rows read at one logical chunk hit 16 distinct chunk positions,
+// and the four rows of a transposing read spread over eight positions.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return row & 7;
+}
+
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
-  constexpr int KSTR = D + 8;          // K tile: [BN][KSTR] halves
-  constexpr int VSTR = BN + 8;         // V^T tile: [D][VSTR] halves
-  constexpr int KTILE = BN * KSTR;
-  constexpr int VTILE = D * VSTR;
-  constexpr int KCH = BN * D / 8 / NT; // 16-byte K chunks per thread
-  constexpr int VBLK = (BN / 4) * (D / 8);  // 4-key x 8-d V blocks per tile
-  static_assert(KCH * NT * 8 == BN * D, "K tile must split evenly over the threads");
-  static_assert(VBLK <= NT, "one V block per thread at most");
-  static_assert(2 * (KTILE + VTILE) * 2 <= 80 * 1024, "two workgroups per CU must fit in LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KTILE + VTILE)];
+  // The body uses amdgcn-only types (buffer resources, LDS address space); the
+  // host pass only needs the kernel's signature for its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int LOADS = BN * CPR / NT;    // chunk loads per thread per K (or V) tile
+  static_assert(LOADS * NT == BN * CPR, "tile must split evenly over the threads");
+  // Two stages of K and V, as separate objects so the compiler can tell the
+  // stage being filled from the stage being read.
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[BN * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 31, hi = lane >> 5;
 
   const int L = xcd_remap(blockIdx.x, a.total_tiles);
@@ -179,166 +198,196 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
   const bool wave_active = q0 < a.Sq;
   const int wave_kv_end = CAUSAL ? min(a.Skv, min(q0 + 32, a.Sq) + a.causal_off) : a.Skv;
 
+  // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
+  // LDS chunk P = (wave * LOADS + i) * 64 + lane of the tile: row P / CPR,
+  // position P % CPR, holding logical chunk position ^ swz(row).
+  int g_off[LOADS];  // byte offset of the chunk within the tile's rows
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (wave * LOADS + i) * 64 + lane;
+    const int row = P / CPR, pos = P % CPR;
+    g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
+  }
+  const uint32_t row_bytes = (uint32_t)a.k_ss * 2u;
+
+  auto tile_rsrc = [&](const uint16_t* base, int kv0) {
+    const uint32_t rows = (uint32_t)max(0, a.Skv - kv0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss), (short)0,
+                                             (int)(rows * row_bytes), kBufferConfig);
+  };
+
+  // Issue the DMA loads of one tile into (k_dst, v_dst).  V goes through
+  // registers (vreg) when it needs the bf16 -> fp16 conversion.
+  u32x4 vreg[LOADS];
+  auto issue_tile = [&](int kv0, LDS_AS uint16_t* k_dst, LDS_AS uint16_t* v_dst) {
+    const auto rk = tile_rsrc(kp, kv0);
+    const auto rv = tile_rsrc(vp, kv0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int base = (wave * LOADS + i) * 64 * 8;  // halves
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + base), 16, g_off[i], 0,
+                                               0, 0);
+      if constexpr (BF16) {
+        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, g_off[i], 0, 0));
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(v_dst + base), 16, g_off[i],
+                                                 0, 0, 0);
+      }
+    }
+  };
+  // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
+  auto store_v = [&](LDS_AS uint16_t* v_dst) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int base = (wave * LOADS + i) * 64 * 8 + lane * 8;
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(vreg[i][j]);
+        *reinterpret_cast<LDS_AS u32x4*>(v_dst + base) = w;
+      }
+    }
+  };
+
+  // ---- LDS read offsets (halves, loop invariant).
+  // K (A operand of S^T): lane reads row 32jb + li, logical chunk 2s + hi.
+  int k_rd[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
+  // V (transposing reads): lane (group g = lane/16, r, c) names 4 halves of
+  // key 16s + 8half + 4hi + r at d = 32db + 16(g & 1) + 4c.
+  const int g16 = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
+  int v_rd[2][D / 32];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int key = 8 * half + 4 * hi + tr_r;  // key within its 16-key step (key & 15)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = 4 * db + 2 * (g16 & 1) + (tr_c >> 1);
+      v_rd[half][db] = key * D + ((chunk ^ swz<D>(key)) * 8) + (tr_c & 1) * 4;
+    }
+  }
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   float m_run = kNegInf;  // reference max (log2 units) used in the exponent
   float l_run = 0.f;      // this lane's share of the row sum
 
-  // ---- staging: global -> registers -> LDS
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  const int vkg = tid / (D / 8), vdg = tid % (D / 8);  // V block of this thread
-
-  auto load_tile = [&](int kv0) {
+  auto compute_tile = [&](int kv0, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) {
+    // S^T = K Q^T : two 32-key blocks.
+    f32x16 sacc[2];
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + NT * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      kreg[r] = (kv0 + row < a.Skv)
-                    ? *reinterpret_cast<const u32x4*>(kp + (kv0 + row) * a.k_ss + col * 8)
-                    : (u32x4){0u, 0u, 0u, 0u};
-    }
-    if (tid < VBLK) {
+    for (int jb = 0; jb < 2; ++jb) {
+      sacc[jb] = (f32x16){};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = kv0 + 4 * vkg + r;
-        vreg[r] = (row < a.Skv)
-                      ? *reinterpret_cast<const u32x4*>(vp + row * a.k_ss + vdg * 8)
-                      : (u32x4){0u, 0u, 0u, 0u};
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
+        sacc[jb] = mfma_qk<BF16>(kf, qf[s], sacc[jb]);
       }
     }
-  };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = lds + buf * (KTILE + VTILE);
-    uint16_t* vs = ks + KTILE;
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + NT * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * KSTR + col * 8) = kreg[r];
-    }
-    if (tid < VBLK) {
-      uint32_t w[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[r][j] = BF16 ? bf16x2_to_f16x2(vreg[r][j]) : vreg[r][j];
-      // keys 4*vkg .. +3 go to positions pos .. pos+3 of their 16-key group:
-      // key 16s + 8a + 4h + e sits at 16s + 8h + 4a + e.
-      const int pos = 16 * (vkg >> 2) + 8 * (vkg & 1) + 4 * ((vkg >> 1) & 1);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int j = d >> 1;
-        u32x2 out;
-        if (d & 1) {
-          out[0] = (w[0][j] >> 16) | (w[1][j] & 0xffff0000u);
-          out[1] = (w[2][j] >> 16) | (w[3][j] & 0xffff0000u);
-        } else {
-          out[0] = (w[0][j] & 0xffffu) | (w[1][j] << 16);
-          out[1] = (w[2][j] & 0xffffu) | (w[3][j] << 16);
-        }
-        *reinterpret_cast<u32x2*>(vs + (8 * vdg + d) * VSTR + pos) = out;
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * BN;
-    if (t + 1 < n_tiles) load_tile(kv0 + BN);
-
-    if (wave_active && kv0 < wave_kv_end) {
-      const uint16_t* ks = lds + (t & 1) * (KTILE + VTILE);
-      const uint16_t* vs = ks + KTILE;
-
-      // S^T = K Q^T : two 32-key blocks.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        sacc[jb] = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const u32x4 kf =
-              *reinterpret_cast<const u32x4*>(ks + (32 * jb + li) * KSTR + 16 * s + 8 * hi);
-          sacc[jb] = mfma_qk<BF16>(kf, qf[s], sacc[jb]);
-        }
-      }
-
-      // Mask keys past the sequence end and (causal) above the diagonal.
-      const bool need_mask =
-          (kv0 + BN > a.Skv) || (CAUSAL && kv0 + BN - 1 > q0 + a.causal_off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * jb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key > lim) sacc[jb][r] = kNegInf;
-          }
-      }
-
-      // Row max over the 64 keys (own 32 values + the partner lane's 32).
-      float mx = kNegInf;
+    // Mask keys past the sequence end and (causal) above the diagonal.
+    const bool need_mask = (kv0 + BN > a.Skv) || (CAUSAL && kv0 + BN - 1 > q0 + a.causal_off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jb][r]);
-      mx = pair_max(mx) * a.c;
-
-      // Lazy rescale: move the reference max only when a row's max grew by > 8.
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float base = (m_run == kNegInf) ? 0.f : m_run;
-
-      // P^T = exp2(S^T * c - base) in fp16: B operand fragments for P.V.
-      u32x4 pf[BN / 16];
-#pragma unroll
-      for (int s = 0; s < BN / 16; ++s) {
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -base));
-        // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
-        // ext-vector *element* (pf[s][j]) as a read of element 0.
-        f16x2 h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
-        pf[s] = (u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                        __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
-        // row sum of the rounded P (the values P.V actually uses)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          l_run = __builtin_amdgcn_fdot2(h[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
-                                         false);
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int s = 0; s < BN / 16; ++s) {
-          const u32x4 vf =
-              *reinterpret_cast<const u32x4*>(vs + (32 * db + li) * VSTR + 16 * s + 8 * hi);
-          acc[db] = mfma_pv(vf, pf[s], acc[db]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * jb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key > lim) sacc[jb][r] = kNegInf;
         }
     }
 
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-    __syncthreads();
+    // Row max over the 64 keys (own 32 values + the partner lane's 32).
+    float mx = kNegInf;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jb][r]);
+    mx = pair_max(mx) * a.c;
+
+    // Lazy rescale: move the reference max only when a row's max grew by > 8.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float base = (m_run == kNegInf) ? 0.f : m_run;
+
+    // P^T = exp2(S^T * c - base) in fp16: B operand fragments for P.V.
+    u32x4 pf[BN / 16];
+#pragma unroll
+    for (int s = 0; s < BN / 16; ++s) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -base));
+      // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
+      // ext-vector *element* (pf[s][j]) as a read of element 0.
+      f16x2 hp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hp[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
+      pf[s] = (u32x4){__builtin_bit_cast(uint32_t, hp[0]), __builtin_bit_cast(uint32_t, hp[1]),
+                      __builtin_bit_cast(uint32_t, hp[2]), __builtin_bit_cast(uint32_t, hp[3])};
+      // row sum of the rounded P (the values P.V actually uses)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        l_run = __builtin_amdgcn_fdot2(hp[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
+                                       false);
+    }
+
+    // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
+    // of the lane half's 16-key step).
+#pragma unroll
+    for (int s = 0; s < BN / 16; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[0][db]));
+        const fp16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[1][db]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
+        const u32x4 vf = (u32x4){l2[0], l2[1], h2[0], h2[1]};
+        acc[db] = mfma_pv(vf, pf[s], acc[db]);
+      }
+  };
+
+  // ---- main loop: two LDS stages, one barrier per tile.
+  LDS_AS uint16_t* const K0 = (LDS_AS uint16_t*)k_lds0;
+  LDS_AS uint16_t* const K1 = (LDS_AS uint16_t*)k_lds1;
+  LDS_AS uint16_t* const V0 = (LDS_AS uint16_t*)v_lds0;
+  LDS_AS uint16_t* const V1 = (LDS_AS uint16_t*)v_lds1;
+
+  if (n_tiles > 0) {
+    issue_tile(0, K0, V0);
+    store_v(V0);
+  }
+  for (int t = 0; t < n_tiles; t += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tt = t + u;
+      if (tt < n_tiles) {
+        LDS_AS uint16_t* const kc = u ? K1 : K0;
+        LDS_AS uint16_t* const vc = u ? V1 : V0;
+        LDS_AS uint16_t* const kn = u ? K0 : K1;
+        LDS_AS uint16_t* const vn = u ? V0 : V1;
+        // Tile tt has landed (this wave's DMA) and every wave is past tile
+        // tt-1, whose stage the next DMA overwrites.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const bool more = tt + 1 < n_tiles;
+        if (more) issue_tile((tt + 1) * BN, kn, vn);
+        if (wave_active && tt * BN < wave_kv_end) compute_tile(tt * BN, kc, vc);
+        if (more) store_v(vn);
+      }
+    }
   }
 
   // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
@@ -363,6 +412,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
         *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = out;
       }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <int D, bool BF16, bool CAUSAL>
