@@ -84,9 +84,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   const int64_t row_stride = layout == ATTN_BHSD ? D : (int64_t)H * D;
   const int64_t smax = Sq > Skv ? Sq : Skv;
   if (smax * row_stride >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
-  const int64_t n_mtiles = (Sq + kPrefillBM - 1) / kPrefillBM;
-  const int64_t total = (int64_t)B * H * n_mtiles;
-  if (total >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -96,8 +94,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   a.H = H;
   a.Sq = Sq;
   a.Skv = Skv;
-  a.n_mtiles = (int)n_mtiles;
-  a.total_tiles = (int)total;
+  a.n_mtiles = 0;     // set by launch_prefill for the chosen tile shape
+  a.total_tiles = 0;
   if (layout == ATTN_BHSD) {
     a.q_sb = (int64_t)H * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
     a.k_sb = (int64_t)H * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
@@ -107,7 +105,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   }
   a.c = exp2_multiplier(scale);
   a.causal_off = Skv - Sq;
-  hipError_t e = launch_prefill(D, dtype == ATTN_BF16, causal != 0, a, stream);
+  hipError_t e = launch_prefill(D, dtype == ATTN_BF16, causal != 0, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -7,19 +7,14 @@
 
 namespace mi355_attn {
 
-// Query rows per prefill workgroup, keys per KV tile, threads per workgroup.
-constexpr int kPrefillBM = 128;
-constexpr int kPrefillBN = 64;
-constexpr int kPrefillThreads = 256;
-
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
   int H, Sq, Skv;
-  int n_mtiles;        // ceil(Sq / kPrefillBM)
-  int total_tiles;     // B * H * n_mtiles  (= grid size)
+  int n_mtiles;        // ceil(Sq / BM), set by launch_prefill
+  int total_tiles;     // B * H * n_mtiles  (= grid size), set by launch_prefill
   int64_t q_sb, q_sh;  // element strides of q and o between batches / heads
   int q_ss;            // element stride between query rows
   int64_t k_sb, k_sh;  // element strides of k and v
@@ -28,7 +23,8 @@ struct PrefillArgs {
   int causal_off;      // Skv - Sq (bottom-right causal alignment)
 };
 
-hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, int B,
+                          hipStream_t s);
 
 // Paged decode: one wave per (sequence, head, split); four heads per workgroup.
 constexpr int kDecodeHeadsPerWG = 4;

@@ -9,9 +9,10 @@
 //
 // Mapping onto the CDNA4 matrix cores
 // -----------------------------------
-// A workgroup owns 128 query rows of one (batch, head); each of its four waves
-// owns 32 of them.  The wave computes the *transposed* score tile
+// A workgroup owns 256 query rows of one (batch, head) (128 for D = 64); each
+// of its eight (four) waves owns 32 of them, and all share each K/V tile.  The wave computes the *transposed* score tile
 //     S^T (64 keys x 32 queries) = K (64 x D) . Q^T (D x 32)
+// for each 64-key tile
 // with v_mfma_f32_32x32x16_{f16,bf16}: K is the A operand (read from LDS), Q^T
 // is the B operand (held in VGPRs for the whole KV loop).  In the 32x32 fp32
 // accumulator a lane owns one query column (lane % 32) and 16 key rows, so
@@ -58,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mi355_attn {
@@ -73,12 +76,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = kPrefillBM;
-constexpr int BN = kPrefillBN;
-constexpr int NT = kPrefillThreads;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLazyRescale = 8.0f;  // log2 units
 constexpr int kBufferConfig = 0x00020000;  // raw buffer, 32-bit data format
+
+
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
@@ -138,25 +140,38 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 }
 
 // XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
-// D = 128 (16 chunks) it is a bijection of the row's low four bits, so 16
-// consecutive rows read at one logical chunk hit 16 distinct chunk positions,
-// and the four rows of a transposing read spread over eight positions.
+// D = 128 (16 chunks) it swaps the two 2-bit halves of the row's low nibble:
+// 16 consecutive rows read at one logical chunk (the K operand reads) land on
+// 16 distinct chunk positions, and the four consecutive rows named by one
+// transposing read land on distinct chunk quartets, so neither read pattern
+// has bank conflicts.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return row & 7;
 }
 
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
+// s_waitcnt that waits until at most N vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
+template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NT = 64 * NW;
+  constexpr int BM = 32 * NW;
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   constexpr int LOADS = BN * CPR / NT;    // chunk loads per thread per K (or V) tile
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly over the threads");
-  // Two stages of K and V, as separate objects so the compiler can tell the
-  // stage being filled from the stage being read.
+  static_assert(BN % 32 == 0 && 2 * 2 * BN * D * 2 <= 160 * 1024, "tile shape");
+  // Two LDS stages each of K and V, as separate objects so the compiler can
+  // tell the stage being filled from the stage being read.
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[BN * D];
@@ -216,23 +231,25 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
                                              (int)(rows * row_bytes), kBufferConfig);
   };
 
-  // Issue the DMA loads of one tile into (k_dst, v_dst).  V goes through
-  // registers (vreg) when it needs the bf16 -> fp16 conversion.
+  // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
+  // first for the fp16 conversion; store_v writes it to LDS).
   u32x4 vreg[LOADS];
-  auto issue_tile = [&](int kv0, LDS_AS uint16_t* k_dst, LDS_AS uint16_t* v_dst) {
+  auto issue_k = [&](int kv0, LDS_AS uint16_t* k_dst) {
     const auto rk = tile_rsrc(kp, kv0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
+                                               16, g_off[i], 0, 0, 0);
+  };
+  auto issue_v = [&](int kv0, LDS_AS uint16_t* v_dst) {
     const auto rv = tile_rsrc(vp, kv0);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int base = (wave * LOADS + i) * 64 * 8;  // halves
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + base), 16, g_off[i], 0,
-                                               0, 0);
-      if constexpr (BF16) {
+      if constexpr (BF16)
         vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, g_off[i], 0, 0));
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(v_dst + base), 16, g_off[i],
-                                                 0, 0, 0);
-      }
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
+                                                 16, g_off[i], 0, 0, 0);
     }
   };
   // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
@@ -274,41 +291,47 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
   float m_run = kNegInf;  // reference max (log2 units) used in the exponent
   float l_run = 0.f;      // this lane's share of the row sum
 
-  auto compute_tile = [&](int kv0, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) {
-    // S^T = K Q^T : two 32-key blocks.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      sacc[jb] = (f32x16){};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
-        sacc[jb] = mfma_qk<BF16>(kf, qf[s], sacc[jb]);
-      }
-    }
+  // ---- per-tile pieces.
 
-    // Mask keys past the sequence end and (causal) above the diagonal.
+  // S^T = K Q^T for one tile: one 32-key accumulator chain per 32 keys,
+  // interleaved.
+  auto qk = [&](const LDS_AS uint16_t* ks, f32x16 (&sc)[BN / 32]) {
+#pragma unroll
+    for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int jb = 0; jb < BN / 32; ++jb) {
+        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
+        sc[jb] = mfma_qk<BF16>(kf, qf[s], sc[jb]);
+      }
+  };
+
+  // Mask keys past the sequence end and (causal) above the diagonal.
+  auto mask_tile = [&](int kv0, f32x16 (&sc)[BN / 32]) {
     const bool need_mask = (kv0 + BN > a.Skv) || (CAUSAL && kv0 + BN - 1 > q0 + a.causal_off);
     if (need_mask) {
       const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int jb = 0; jb < BN / 32; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * jb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key > lim) sacc[jb][r] = kNegInf;
+          if (key > lim) sc[jb][r] = kNegInf;
         }
     }
+  };
 
-    // Row max over the 64 keys (own 32 values + the partner lane's 32).
+  // Row max over the tile's keys and the lazy rescale; returns the
+  // reference max used in this tile's exponent.
+  auto max_rescale = [&](const f32x16 (&sc)[BN / 32]) {
     float mx = kNegInf;
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < BN / 32; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
     mx = pair_max(mx) * a.c;
-
-    // Lazy rescale: move the reference max only when a row's max grew by > 8.
+    // Move the reference max only when some row's max grew by more than 8.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -317,16 +340,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       m_run = m_new;
     }
-    const float base = (m_run == kNegInf) ? 0.f : m_run;
+    return (m_run == kNegInf) ? 0.f : m_run;
+  };
 
-    // P^T = exp2(S^T * c - base) in fp16: B operand fragments for P.V.
-    u32x4 pf[BN / 16];
+  // P^T = exp2(S^T * c - base) rounded to fp16 (the B operand of P.V), and
+  // the row sum of exactly those rounded values.
+  auto exp_tile = [&](const f32x16 (&sc)[BN / 32], float base, u32x4 (&pf)[BN / 16]) {
 #pragma unroll
     for (int s = 0; s < BN / 16; ++s) {
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -base));
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s >> 1][8 * (s & 1) + j], a.c, -base));
       // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
       // ext-vector *element* (pf[s][j]) as a read of element 0.
       f16x2 hp[4];
@@ -335,15 +360,16 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
         hp[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
       pf[s] = (u32x4){__builtin_bit_cast(uint32_t, hp[0]), __builtin_bit_cast(uint32_t, hp[1]),
                       __builtin_bit_cast(uint32_t, hp[2]), __builtin_bit_cast(uint32_t, hp[3])};
-      // row sum of the rounded P (the values P.V actually uses)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         l_run = __builtin_amdgcn_fdot2(hp[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
                                        false);
     }
+  };
 
-    // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
-    // of the lane half's 16-key step).
+  // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
+  // of the lane half's 16-key step).
+  auto pv = [&](const u32x4 (&pf)[BN / 16], const LDS_AS uint16_t* vs) {
 #pragma unroll
     for (int s = 0; s < BN / 16; ++s)
 #pragma unroll
@@ -359,35 +385,41 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
       }
   };
 
-  // ---- main loop: two LDS stages, one barrier per tile.
-  LDS_AS uint16_t* const K0 = (LDS_AS uint16_t*)k_lds0;
-  LDS_AS uint16_t* const K1 = (LDS_AS uint16_t*)k_lds1;
-  LDS_AS uint16_t* const V0 = (LDS_AS uint16_t*)v_lds0;
-  LDS_AS uint16_t* const V1 = (LDS_AS uint16_t*)v_lds1;
+  // ---- main loop: two LDS stages; tile t+1 streams in while tile t
+  // computes; one barrier per tile.
+  LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
+  LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
 
   if (n_tiles > 0) {
-    issue_tile(0, K0, V0);
-    store_v(V0);
+    issue_v(0, Vs[0]);
+    issue_k(0, Ks[0]);
+    store_v(Vs[0]);
   }
-  for (int t = 0; t < n_tiles; t += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tt = t + u;
-      if (tt < n_tiles) {
-        LDS_AS uint16_t* const kc = u ? K1 : K0;
-        LDS_AS uint16_t* const vc = u ? V1 : V0;
-        LDS_AS uint16_t* const kn = u ? K0 : K1;
-        LDS_AS uint16_t* const vn = u ? V0 : V1;
-        // Tile tt has landed (this wave's DMA) and every wave is past tile
-        // tt-1, whose stage the next DMA overwrites.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const bool more = tt + 1 < n_tiles;
-        if (more) issue_tile((tt + 1) * BN, kn, vn);
-        if (wave_active && tt * BN < wave_kv_end) compute_tile(tt * BN, kc, vc);
-        if (more) store_v(vn);
-      }
+  auto iteration = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;  // t % 2
+    // Tile t has landed for this wave; after the barrier for every wave, and
+    // every wave is done with tile t-1, whose stages are refilled next.
+    wait_vmcnt<0>();
+    __syncthreads();
+    const bool more = t + 1 < n_tiles;
+    if (more) {
+      issue_v((t + 1) * BN, Vs[P ^ 1]);
+      issue_k((t + 1) * BN, Ks[P ^ 1]);
     }
+    if (wave_active && t * BN < wave_kv_end) {
+      f32x16 sc[BN / 32];
+      qk(Ks[P], sc);
+      mask_tile(t * BN, sc);
+      const float base = max_rescale(sc);
+      u32x4 pf[BN / 16];
+      exp_tile(sc, base, pf);
+      pv(pf, Vs[P]);
+    }
+    if (more) store_v(Vs[P ^ 1]);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
@@ -415,27 +447,39 @@ __global__ __launch_bounds__(NT, 2) void prefill_fwd_kernel(PrefillArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool BF16, bool CAUSAL>
-hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(a.total_tiles), dim3(NT), 0, s, a);
+template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
+  const int64_t n_mtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
+  const int64_t total = (int64_t)B * a.H * n_mtiles;
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  a.n_mtiles = (int)n_mtiles;
+  a.total_tiles = (int)total;
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, NW, BN>), dim3(a.total_tiles),
+                     dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
+// D = 128: eight waves (256 query rows) share each 64-key K/V tile, one
+// workgroup per CU (two waves per SIMD); D = 64: four waves (128 rows).
 template <int D, bool BF16>
-hipError_t launch_c(bool causal, const PrefillArgs& a, hipStream_t s) {
-  return causal ? launch_t<D, BF16, true>(a, s) : launch_t<D, BF16, false>(a, s);
+hipError_t launch_c(bool causal, const PrefillArgs& a, int B, hipStream_t s) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int BN = 64;
+  return causal ? launch_t<D, BF16, true, NW, BN>(a, B, s)
+                : launch_t<D, BF16, false, NW, BN>(a, B, s);
 }
 
 template <int D>
-hipError_t launch_d(bool bf16, bool causal, const PrefillArgs& a, hipStream_t s) {
-  return bf16 ? launch_c<D, true>(causal, a, s) : launch_c<D, false>(causal, a, s);
+hipError_t launch_d(bool bf16, bool causal, const PrefillArgs& a, int B, hipStream_t s) {
+  return bf16 ? launch_c<D, true>(causal, a, B, s) : launch_c<D, false>(causal, a, B, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, hipStream_t s) {
-  if (D == 128) return launch_d<128>(bf16, causal, a, s);
-  if (D == 64) return launch_d<64>(bf16, causal, a, s);
+hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, int B,
+                          hipStream_t s) {
+  if (D == 128) return launch_d<128>(bf16, causal, a, B, s);
+  if (D == 64) return launch_d<64>(bf16, causal, a, B, s);
   return hipErrorInvalidValue;
 }
 
