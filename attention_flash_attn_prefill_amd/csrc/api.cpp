@@ -33,18 +33,19 @@ struct SplitPlan {
   int tokens_per_split;
 };
 
-// Tokens per split: a multiple of two pages (the kernel's batch), chosen so
-// the grid holds enough work items to fill 256 CUs even when sequences are
-// short, while keeping the partial-result traffic (one D+1 fp32 row per
-// split) below about 2% of the KV bytes at the default of 256 tokens.
+// Tokens per split: a multiple of four pages (the kernel's batch), 512 by
+// default, halved while the grid holds fewer than 8192 (sequence, head group,
+// split) work items, so short batches still fill 256 CUs.  Partial results
+// cost one D+1 fp32 row per split: about 0.5% of the KV bytes at 512 tokens.
+// The plan depends only on host-side sizes (never on seq_lens).
 SplitPlan plan_splits(int B, int H, int max_pages, int page_size) {
   SplitPlan p{0, 0};
   if (B <= 0 || H <= 0 || max_pages <= 0 || page_size != kDecodePageSize) return p;
   const int64_t max_tokens = (int64_t)max_pages * page_size;
   const int64_t head_groups = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
-  int tps = 256;
+  int tps = 512;
   auto splits = [&](int t) { return (max_tokens + t - 1) / t; };
-  while (tps > 2 * kDecodePageSize && (int64_t)B * head_groups * splits(tps) < 8192) tps /= 2;
+  while (tps > 4 * kDecodePageSize && (int64_t)B * head_groups * splits(tps) < 8192) tps /= 2;
   while (splits(tps) > 4096) tps *= 2;
   p.tokens_per_split = tps;
   p.n_splits = (int)splits(tps);

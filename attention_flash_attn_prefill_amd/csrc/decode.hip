@@ -12,10 +12,12 @@
 //   * A wave owns one (sequence, head, split).  Its lanes form groups of D/8
 //     lanes; each group reads one token's K (and V) row with 128-bit loads, so
 //     a wave-wide load instruction covers 4 (D = 128) or 8 (D = 64) tokens.
-//   * The wave walks its split two pages (32 tokens) at a time and issues all
-//     K and V loads of the batch before any arithmetic: 16 128-bit loads in
-//     flight per lane.  Page ids are wave-uniform (scalar loads) and page bases
-//     use 64-bit offsets (an 8 GiB pool exceeds 2^32 elements).
+//   * The wave walks its split four pages (64 tokens) at a time and issues all
+//     K and V loads of the batch before any arithmetic: 32 128-bit loads in
+//     flight per lane (D = 128).  The loads are non-temporal: every cache byte
+//     is read once per call, so it should not displace anything in L2/MALL.
+//     Page ids are wave-uniform (scalar loads) and page bases use 64-bit
+//     offsets (an 8 GiB pool exceeds 2^32 elements).
 //   * Scores are fp32 dot products (v_dot2_f32_f16 / bf16 widening) reduced
 //     across the D/8 lanes of a group with DPP; each group keeps its own online
 //     softmax state (max, sum, D/8-lane slice of the output) and the groups are
@@ -100,7 +102,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(DecodeArgs a) {
   constexpr int G = D / 8;          // lanes per token row
   constexpr int RPW = 64 / G;       // token rows per wave-wide load
-  constexpr int BATCH = 2 * PS;     // tokens per batch (two pages)
+  constexpr int PAGES = 4;          // pages per batch
+  constexpr int BATCH = PAGES * PS; // tokens per batch
   constexpr int UNR = BATCH / RPW;  // tokens per lane per batch
   static_assert(UNR * RPW == BATCH, "batch must tile the wave");
 
@@ -130,21 +133,23 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
   for (int tb = t_begin; tb < t_end; tb += BATCH) {
-    // Page ids of the (up to) two pages of this batch; only pages holding a
-    // live token are looked up.
-    const int pg0 = ptab[tb / PS];
-    const int pg1 = (tb + PS < t_end) ? ptab[tb / PS + 1] : pg0;
+    // Page ids of the pages of this batch; only pages holding a live token
+    // are looked up.
+    int pgs[PAGES];
+    pgs[0] = ptab[tb / PS];
+#pragma unroll
+    for (int j = 1; j < PAGES; ++j) pgs[j] = (tb + j * PS < t_end) ? ptab[tb / PS + j] : pgs[0];
 
     u32x4 kr[UNR], vr[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int off = grp + RPW * u;  // token offset within the batch
       const int t = tb + off;
-      const int pg = (off < PS) ? pg0 : pg1;
+      const int pg = pgs[off / PS];
       const int64_t idx = ((int64_t)pg * PS + (off % PS)) * row_stride + head_off;
       if (t < t_end) {
-        kr[u] = *reinterpret_cast<const u32x4*>(a.k_cache + idx);
-        vr[u] = *reinterpret_cast<const u32x4*>(a.v_cache + idx);
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_cache + idx));
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_cache + idx));
       } else {
         kr[u] = (u32x4){0u, 0u, 0u, 0u};
         vr[u] = (u32x4){0u, 0u, 0u, 0u};

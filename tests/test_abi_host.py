@@ -113,7 +113,7 @@ def test_decode_empty_is_a_noop():
 
 def test_split_plan_and_workspace():
     n, tps = attn.attn_paged_decode_num_splits(64, 32, 512, 16)
-    assert tps % 32 == 0 and tps >= 32
+    assert tps % 64 == 0 and tps >= 64
     assert n == math.ceil(512 * 16 / tps)
     ws = attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
     rows = 64 * 32 * n

@@ -77,12 +77,12 @@ def test_decode_pool_permutation_bitwise(gpu_lib):
 def test_decode_split_plan_invariance(gpu_lib):
     """Widening the page table (unused columns) changes the split plan, not O."""
     attn = gpu_lib
-    batch = workloads.paged_decode_inputs(B=2, H=8, D=128, page_size=16, num_pages=2048,
-                                          max_seq=4096, seed=31, seq_lens=[4096, 2500])
-    plan_a = attn.attn_paged_decode_num_splits(2, 8, batch.max_pages_per_seq, 16)
-    wide = torch.full((2, 8192), batch.meta["unused_page"], dtype=torch.int32)
+    batch = workloads.paged_decode_inputs(B=32, H=8, D=128, page_size=16, num_pages=8192,
+                                          max_seq=4096, seed=31)
+    plan_a = attn.attn_paged_decode_num_splits(32, 8, batch.max_pages_per_seq, 16)
+    wide = torch.full((32, 4096), batch.meta["unused_page"], dtype=torch.int32)
     wide[:, :batch.max_pages_per_seq] = batch.page_table
-    plan_b = attn.attn_paged_decode_num_splits(2, 8, 8192, 16)
+    plan_b = attn.attn_paged_decode_num_splits(32, 8, 4096, 16)
     assert plan_a[1] != plan_b[1], (plan_a, plan_b)
     a = _run(attn, batch)
     b = _run(attn, batch, page_table=wide)
