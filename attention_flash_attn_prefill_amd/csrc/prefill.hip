@@ -296,15 +296,22 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // S^T = K Q^T for one tile: one 32-key accumulator chain per 32 keys,
   // interleaved.
   auto qk = [&](const LDS_AS uint16_t* ks, f32x16 (&sc)[BN / 32]) {
+    // All K fragments are read before the first MFMA (the fence keeps the
+    // scheduler from recycling two registers and exposing an LDS round trip
+    // per MFMA pair).
+    u32x4 kf[D / 16][BN / 32];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int jb = 0; jb < BN / 32; ++jb)
+        kf[s][jb] = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-      for (int jb = 0; jb < BN / 32; ++jb) {
-        const u32x4 kf = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
-        sc[jb] = mfma_qk<BF16>(kf, qf[s], sc[jb]);
-      }
+      for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk<BF16>(kf[s][jb], qf[s], sc[jb]);
   };
 
   // Mask keys past the sequence end and (causal) above the diagonal.
@@ -370,6 +377,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
   // of the lane half's 16-key step).
   auto pv = [&](const u32x4 (&pf)[BN / 16], const LDS_AS uint16_t* vs) {
+    // All V^T fragments are read before the first MFMA (see qk).
+    u32x4 vf[BN / 16][D / 32];
 #pragma unroll
     for (int s = 0; s < BN / 16; ++s)
 #pragma unroll
@@ -380,9 +389,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
             (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[1][db]));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
-        const u32x4 vf = (u32x4){l2[0], l2[1], h2[0], h2[1]};
-        acc[db] = mfma_pv(vf, pf[s], acc[db]);
+        vf[s][db] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
       }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < BN / 16; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_pv(vf[s][db], pf[s], acc[db]);
   };
 
   // ---- main loop: two LDS stages; tile t+1 streams in while tile t

@@ -156,6 +156,30 @@ def copy_calibration(mib):
     torch.cuda.empty_cache()
 
 
+def vendor_gemm_reference(n=16384, dtype_name="f16"):
+    """Throughput of the vendor's tuned dense GEMM (torch.matmul -> hipBLASLt)
+    on this GPU, as context for the MFMA roofline: sustained matrix-core load
+    runs the chip below its 2.4 GHz peak clock."""
+    import torch
+    dt = torch.float16 if dtype_name == "f16" else torch.bfloat16
+    a = torch.randn(n, n, device="cuda", dtype=dt)
+    b = torch.randn(n, n, device="cuda", dtype=dt)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b
+    torch.cuda.empty_cache()
+    return {"what": f"torch.matmul {dtype_name} {n}x{n}x{n} (hipBLASLt)",
+            "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3)}
+
+
 def cpu_baseline_prefill(cfg, budget_s=15.0):
     """The fp64 oracle as it stands, on whole heads of the same workload,
     until about budget_s seconds of CPU work; scaled to TFLOP/s."""
@@ -202,6 +226,8 @@ def main():
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip timing the vendor GEMM reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -242,6 +268,12 @@ def main():
               f"({100 * r['roofline']['frac']:.1f}% of peak)", file=sys.stderr, flush=True)
 
     head = results[head_cfg]
+    gemm_ref = None
+    if not args.no_gemm_reference:
+        print("[bench] vendor GEMM reference ...", file=sys.stderr, flush=True)
+        gemm_ref = vendor_gemm_reference()
+        print(f"[bench] vendor GEMM reference: {gemm_ref['tflops']} TFLOP/s", file=sys.stderr,
+              flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle) ...", file=sys.stderr, flush=True)
@@ -274,6 +306,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "extra": extra,
+        "mfma_context": gemm_ref,
     }
     print(json.dumps(line), flush=True)
 
