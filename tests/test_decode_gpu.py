@@ -103,3 +103,26 @@ def test_decode_full_config4(gpu_lib):
     o = _run(gpu_lib, batch, scale=batch.meta["scale"])
     ref = _ref(batch, scale=batch.meta["scale"])
     assert_parity(o.double().numpy(), ref, "config 4 (all sequences and heads)")
+
+
+@pytest.mark.parametrize("dtype,amp", [("f16", 6.0), ("bf16", 8.0)])
+def test_decode_large_logits(gpu_lib, dtype, amp):
+    """Large q and k make the running max jump between batches and splits."""
+    batch = workloads.paged_decode_inputs(B=12, H=8, D=128, dtype=dtype, page_size=16,
+                                          num_pages=4096, min_seq=1, max_seq=4000, seed=41,
+                                          amp=amp)
+    # V at std 1/3 keeps |O| < 2, where rounding O to bf16 costs < 4e-3.
+    batch.v_cache = (batch.v_cache.float() / (3 * amp)).to(batch.v_cache.dtype)
+    o = _run(gpu_lib, batch)
+    assert_parity(o.double().numpy(), _ref(batch), f"decode amp {amp} {dtype}")
+
+
+def test_decode_small_batch_fine_splits(gpu_lib):
+    """One sequence: the plan picks its smallest split, so most splits hold
+    one 64-token batch and some hold none."""
+    batch = workloads.paged_decode_inputs(B=1, H=4, D=64, page_size=16, num_pages=700,
+                                          seq_lens=[3000], max_pages_per_seq=640, seed=42)
+    n, tps = gpu_lib.attn_paged_decode_num_splits(1, 4, 640, 16)
+    assert tps == 64 and n == 160
+    o = _run(gpu_lib, batch)
+    assert_parity(o.double().numpy(), _ref(batch), "B1 fine splits")

@@ -150,3 +150,57 @@ def test_prefill_full_config_sampled(gpu_lib, cfg, n_random):
         got = torch.stack([o[b, i, h] for b, h, i in rows])
     assert torch.isfinite(o.float()).all()
     assert_parity(_f64(got), ref, f"config {cfg} ({len(rows)} sampled rows)")
+
+
+# ------------------------------------------------------------ stress cases
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
+def test_prefill_mostly_idle_waves(gpu_lib, causal, layout):
+    """Sq far below one 256-row workgroup: most waves have no query rows."""
+    q, k, v = workloads.prefill_inputs(3, 5, 33, 2000, 128, "bf16", layout, seed=21)
+    o = _run(gpu_lib, q, k, v, causal, 1 / math.sqrt(128), layout)
+    ref = oracle.sdpa(q, k, v, causal=causal, layout=layout)
+    assert_parity(_f64(o), ref, f"Sq33 Skv2000 {layout} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_long_kv_tiny_q_causal(gpu_lib, dtype):
+    """Bottom-right causal with Sq << Skv: every row sees almost all keys."""
+    q, k, v = workloads.prefill_inputs(2, 3, 7, 5000, 128, dtype, "BHSD", seed=22)
+    o = _run(gpu_lib, q, k, v, True, 1 / math.sqrt(128), "BHSD")
+    assert_parity(_f64(o), oracle.sdpa(q, k, v, causal=True), f"Sq7 Skv5000 {dtype}")
+
+
+@pytest.mark.parametrize("dtype,amp", [("f16", 6.0), ("bf16", 8.0)])
+def test_prefill_large_logits_force_rescales(gpu_lib, dtype, amp):
+    """Large inputs make the running max jump often (the lazy rescale path)."""
+    q, k, v = workloads.prefill_inputs(1, 4, 700, 1900, 128, dtype, "BHSD", amp=amp, seed=23)
+    # Only the logits grow: V is brought to std 1/3, so |O| < 2.  Near one-hot
+    # rows copy single V values, and rounding O to bf16 alone costs up to
+    # 2^-9 |O|, which must stay well inside the 1e-2 bar.
+    v = (v.float() / (3 * amp)).to(v.dtype)
+    for causal in (False, True):
+        o = _run(gpu_lib, q, k, v, causal, 1 / math.sqrt(128), "BHSD")
+        assert_parity(_f64(o), oracle.sdpa(q, k, v, causal=causal),
+                      f"amp {amp} {dtype} causal={causal}")
+
+
+def test_prefill_near_argmax_scale(gpu_lib):
+    """A large scale concentrates each row on its top keys."""
+    q, k, v = workloads.prefill_inputs(1, 2, 300, 800, 64, "f16", "BSHD", seed=24)
+    o = _run(gpu_lib, q, k, v, False, 2.0, "BSHD")
+    assert_parity(_f64(o), oracle.sdpa(q, k, v, causal=False, scale=2.0, layout="BSHD"),
+                  "scale 2.0")
+
+
+def test_prefill_rejects_bad_tensors(gpu_lib):
+    attn = gpu_lib
+    q = torch.randn((1, 2, 64, 128), device="cuda").half()
+    with pytest.raises(ValueError):
+        attn.prefill(q, q.transpose(2, 3).contiguous().transpose(2, 3), q)   # non-contiguous k
+    with pytest.raises(TypeError):
+        attn.prefill(q, q.float(), q)
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill(q[..., :96].contiguous(), q[..., :96].contiguous(), q[..., :96].contiguous())
+    assert e.value.status == attn.ATTN_E_UNSUPPORTED
