@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(PKG, "libmi355attn.so")
 ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = range(5)
 ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_F16, ATTN_BF16 = 0, 1
+ATTN_OUT_F32 = 0x100
 LAYOUTS = {"BHSD": ATTN_BHSD, "BSHD": ATTN_BSHD}
 
 # Every symbol include/attn.h declares, with its ctypes signature.
@@ -130,11 +131,26 @@ def _check(status, where):
         raise AttnError(status, where)
 
 
-def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, stream=None):
+def _out_code(q, out, out_dtype):
+    """dtype code for the C call and the output dtype (q's, or fp32)."""
+    import torch
+    want = out.dtype if out is not None else (out_dtype or q.dtype)
+    if out_dtype is not None and want != out_dtype:
+        raise TypeError("out and out_dtype disagree")
+    if want == q.dtype:
+        return _dtype_code(q), want
+    if want == torch.float32:
+        return _dtype_code(q) | ATTN_OUT_F32, want
+    raise TypeError(f"output dtype must be {q.dtype} or torch.float32, not {want}")
+
+
+def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_dtype=None,
+            stream=None):
     """O = softmax(Q K^T * scale [+ causal mask]) V on the GPU.
 
     q: [B,H,Sq,D] (layout "BHSD") or [B,Sq,H,D] ("BSHD"); k, v likewise with
-    Skv keys; fp16 or bf16 CUDA tensors, contiguous.  Returns o like q.
+    Skv keys; fp16 or bf16 CUDA tensors, contiguous.  Returns o like q, or in
+    fp32 (unrounded) with out_dtype=torch.float32 or an fp32 `out`.
     """
     import torch
     if layout not in LAYOUTS:
@@ -156,20 +172,23 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, strea
         raise ValueError(f"k and v must have shape {kv_shape}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    _check(attn_prefill(q, k, v, o, B, H, Sq, Skv, D, LAYOUTS[layout], _dtype_code(q),
+    code, odt = _out_code(q, out, out_dtype)
+    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
+    if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped like q")
+    _check(attn_prefill(q, k, v, o, B, H, Sq, Skv, D, LAYOUTS[layout], code,
                         causal, scale, stream), "attn_prefill")
     return o
 
 
 def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=None,
-                 workspace=None, stream=None):
+                 out_dtype=None, workspace=None, stream=None):
     """Decode attention of q [B,H,D] against a paged cache [num_pages, 16, H, D].
 
     page_table [B, max_pages] and seq_lens [B] are int32 GPU tensors.  The
-    workspace (a uint8 GPU tensor) is allocated here if not given.
+    workspace (a uint8 GPU tensor) is allocated here if not given.  O is like
+    q, or fp32 with out_dtype=torch.float32 or an fp32 `out`.  A page id
+    outside the pool makes that sequence's output NaN (checked on the GPU).
     """
     import torch
     B, H, D = q.shape
@@ -187,9 +206,12 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=N
     need = attn_paged_decode_workspace_size(B, H, D, max_pages, page_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
+    code, odt = _out_code(q, out, out_dtype)
+    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
+    if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped like q")
     _check(attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, o, B, H, D, page_size,
-                             num_pages, max_pages, _dtype_code(q), scale, workspace,
+                             num_pages, max_pages, code, scale, workspace,
                              workspace.numel() * workspace.element_size(), stream),
            "attn_paged_decode")
     return o

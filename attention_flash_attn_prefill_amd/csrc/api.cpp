@@ -19,6 +19,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// dtype = element type of the inputs, optionally OR-ed with ATTN_OUT_F32.
+bool parse_dtype(int dtype, bool* bf16, bool* out_f32) {
+  const int elt = dtype & ~ATTN_OUT_F32;
+  if (elt != ATTN_F16 && elt != ATTN_BF16) return false;
+  *bf16 = elt == ATTN_BF16;
+  *out_f32 = (dtype & ATTN_OUT_F32) != 0;
+  return true;
+}
+
 // Softmax scale -> exponent multiplier c = scale * log2(e).  A zero scale
 // (uniform weights) becomes the smallest positive normal float, which gives
 // the same result (every score * c rounds exp2 to exactly 1) while keeping
@@ -72,7 +81,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
                  hipStream_t stream) {
   if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
   if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
   if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
   if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H * Sq == 0) return ATTN_OK;  // nothing to compute
@@ -91,7 +101,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
+  a.o = o;
   a.H = H;
   a.Sq = Sq;
   a.Skv = Skv;
@@ -106,7 +116,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   }
   a.c = exp2_multiplier(scale);
   a.causal_off = Skv - Sq;
-  hipError_t e = launch_prefill(D, dtype == ATTN_BF16, causal != 0, a, B, stream);
+  hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -133,7 +143,8 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                       int D, int page_size, int num_pages, int max_pages_per_seq, int dtype,
                       float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
   if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
   if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
   if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
@@ -159,7 +170,7 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   a.v_cache = static_cast<const uint16_t*>(v_cache);
   a.page_table = page_table;
   a.seq_lens = seq_lens;
-  a.o = static_cast<uint16_t*>(o);
+  a.o = o;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   a.B = B;
@@ -167,8 +178,9 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   a.max_pages = max_pages_per_seq;
   a.n_splits = p.n_splits;
   a.tokens_per_split = p.tokens_per_split;
+  a.num_pages = num_pages;
   a.c = exp2_multiplier(scale);
-  hipError_t e = launch_paged_decode(D, dtype == ATTN_BF16, a, stream);
+  hipError_t e = launch_paged_decode(D, bf16, out_f32, a, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

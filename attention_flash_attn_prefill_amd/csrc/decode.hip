@@ -22,6 +22,10 @@
 //     across the D/8 lanes of a group with DPP; each group keeps its own online
 //     softmax state (max, sum, D/8-lane slice of the output) and the groups are
 //     merged once at the end of the split.
+//   * Page ids are checked on the device before any load through them: an
+//     id outside [0, num_pages) stops the split and poisons its log-sum-exp
+//     with NaN, so that sequence's output becomes NaN instead of a read out
+//     of bounds (two scalar compares per page; nothing measurable).
 //   * A split that starts past the sequence end returns before any load
 //     (empty windows cost nothing: "[FlyDSL] FP8 MQA logits improvements for
 //     gfx950", Changes / Kernel, empty-window fix).  Tokens past the end and
@@ -131,6 +135,7 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  bool bad_page = false;  // wave-uniform
 
   for (int tb = t_begin; tb < t_end; tb += BATCH) {
     // Page ids of the pages of this batch; only pages holding a live token
@@ -139,6 +144,9 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
     pgs[0] = ptab[tb / PS];
 #pragma unroll
     for (int j = 1; j < PAGES; ++j) pgs[j] = (tb + j * PS < t_end) ? ptab[tb / PS + j] : pgs[0];
+#pragma unroll
+    for (int j = 0; j < PAGES; ++j) bad_page |= (uint32_t)pgs[j] >= (uint32_t)a.num_pages;
+    if (bad_page) break;  // no load through an id outside the pool
 
     u32x4 kr[UNR], vr[UNR];
 #pragma unroll
@@ -205,7 +213,18 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
     m = m_new;
   }
 
-  // The split holds at least one live token, so l > 0.
+  // The split holds at least one live token, so l > 0 unless a page id was
+  // rejected: then the NaN log-sum-exp carries the error through the combine.
+  if (bad_page) {
+    if (lane < G) {
+      const float nan = __builtin_nanf("");
+      float* po = a.part_o + (((int64_t)b * a.H + h) * a.n_splits + split) * D + gl * 8;
+      *reinterpret_cast<float4*>(po) = make_float4(nan, nan, nan, nan);
+      *reinterpret_cast<float4*>(po + 4) = make_float4(nan, nan, nan, nan);
+      if (lane == 0) a.part_lse[((int64_t)b * a.H + h) * a.n_splits + split] = nan;
+    }
+    return;
+  }
   if (lane < G) {
     const float inv = 1.f / l;
     float* po = a.part_o + (((int64_t)b * a.H + h) * a.n_splits + split) * D + gl * 8;
@@ -216,8 +235,9 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
   }
 }
 
-// One wave per (sequence, head): merge the live splits by log-sum-exp.
-template <int D, bool BF16>
+// One wave per (sequence, head): merge the live splits by log-sum-exp.  A
+// NaN partial (rejected page id) makes the output NaN.  OF32: O in fp32.
+template <int D, bool BF16, bool OF32>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;  // output elements per lane
   const int bh = blockIdx.x;
@@ -229,7 +249,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const float* po = a.part_o + (int64_t)bh * a.n_splits * D;
 
   float mx = kNegInf;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse[s]);
+  bool poisoned = false;
+  for (int s = lane; s < ns; s += 64) {
+    mx = fmaxf(mx, lse[s]);
+    poisoned |= __builtin_isnan(lse[s]);
+  }
+  poisoned = __any(poisoned);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
 
@@ -243,27 +268,35 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(w, po[s * D + lane + 64 * e], acc[e]);
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* out = a.o + (int64_t)bh * D;
+  const float inv = poisoned ? __builtin_nanf("") : (wsum > 0.f ? 1.f / wsum : 0.f);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) out[lane + 64 * e] = to_out<BF16>(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) {
+    const int64_t i = (int64_t)bh * D + lane + 64 * e;
+    if constexpr (OF32) static_cast<float*>(a.o)[i] = acc[e] * inv;
+    else static_cast<uint16_t*>(a.o)[i] = to_out<BF16>(acc[e] * inv);
+  }
 }
 
 template <int D, bool BF16>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((a.H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG, a.n_splits, a.B);
   hipLaunchKernelGGL((decode_split_kernel<D, BF16>), grid, dim3(64 * kDecodeHeadsPerWG), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.B * a.H), dim3(64), 0, s, a);
+  if (out_f32)
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, true>), dim3(a.B * a.H), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, false>), dim3(a.B * a.H), dim3(64), 0, s,
+                       a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_paged_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t s) {
-  if (D == 128) return bf16 ? launch_t<128, true>(a, s) : launch_t<128, false>(a, s);
-  if (D == 64) return bf16 ? launch_t<64, true>(a, s) : launch_t<64, false>(a, s);
+hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                               hipStream_t s) {
+  if (D == 128) return bf16 ? launch_t<128, true>(out_f32, a, s) : launch_t<128, false>(out_f32, a, s);
+  if (D == 64) return bf16 ? launch_t<64, true>(out_f32, a, s) : launch_t<64, false>(out_f32, a, s);
   return hipErrorInvalidValue;
 }
 

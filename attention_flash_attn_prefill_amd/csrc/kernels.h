@@ -11,7 +11,7 @@ struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  uint16_t* o;
+  void* o;             // fp16/bf16 like q, or fp32 (out_f32)
   int H, Sq, Skv;
   int n_mtiles;        // ceil(Sq / BM), set by launch_prefill
   int total_tiles;     // B * H * n_mtiles  (= grid size), set by launch_prefill
@@ -23,8 +23,8 @@ struct PrefillArgs {
   int causal_off;      // Skv - Sq (bottom-right causal alignment)
 };
 
-hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, int B,
-                          hipStream_t s);
+hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
+                          int B, hipStream_t s);
 
 // Paged decode: one wave per (sequence, head, split); four heads per workgroup.
 constexpr int kDecodeHeadsPerWG = 4;
@@ -36,13 +36,15 @@ struct DecodeArgs {
   const uint16_t* v_cache;
   const int32_t* page_table;  // [B, max_pages]
   const int32_t* seq_lens;    // [B]
-  uint16_t* o;                // [B, H, D]
+  void* o;                    // [B, H, D], dtype of q or fp32 (out_f32)
   float* part_o;              // [B, H, n_splits, D]   (workspace)
   float* part_lse;            // [B, H, n_splits]      (workspace; log2 domain)
   int B, H, max_pages, n_splits, tokens_per_split;
+  int num_pages;              // page ids outside [0, num_pages) are rejected on the device
   float c;                    // scale * log2(e)
 };
 
-hipError_t launch_paged_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                               hipStream_t s);
 
 }  // namespace mi355_attn

@@ -71,6 +71,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -159,7 +160,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
-template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+// OF32: O is stored in fp32 instead of the input type.
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const int b = bh / a.H, h = bh - b * a.H;
 
   const uint16_t* __restrict__ qp = a.q + b * a.q_sb + h * a.q_sh;
-  uint16_t* __restrict__ op = a.o + b * a.q_sb + h * a.q_sh;
+  const int64_t o_base = b * a.q_sb + h * a.q_sh;  // o shares q's element strides
   const uint16_t* __restrict__ kp = a.k + b * a.k_sb + h * a.k_sh;
   const uint16_t* __restrict__ vp = a.v + b * a.k_sb + h * a.k_sh;
 
@@ -440,59 +442,73 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    uint16_t* orow = op + qi * a.q_ss;
+    const int64_t row = o_base + (int64_t)qi * a.q_ss;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float* v4 = reinterpret_cast<const float*>(&acc[db]) + 4 * g;
-        u32x2 out;
-        if constexpr (BF16) {
-          out[0] = pack_bf16(v4[0] * inv, v4[1] * inv);
-          out[1] = pack_bf16(v4[2] * inv, v4[3] * inv);
+        const int d0 = 32 * db + 8 * g + 4 * hi;
+        if constexpr (OF32) {
+          const f32x4 out = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + row + d0) = out;
         } else {
-          out[0] = pack_f16(v4[0] * inv, v4[1] * inv);
-          out[1] = pack_f16(v4[2] * inv, v4[3] * inv);
+          u32x2 out;
+          if constexpr (BF16) {
+            out[0] = pack_bf16(v4[0] * inv, v4[1] * inv);
+            out[1] = pack_bf16(v4[2] * inv, v4[3] * inv);
+          } else {
+            out[0] = pack_f16(v4[0] * inv, v4[1] * inv);
+            out[1] = pack_f16(v4[2] * inv, v4[3] * inv);
+          }
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + row + d0) = out;
         }
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = out;
       }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN>
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
   const int64_t n_mtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t total = (int64_t)B * a.H * n_mtiles;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;
   a.total_tiles = (int)total;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, NW, BN>), dim3(a.total_tiles),
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN>), dim3(a.total_tiles),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 // D = 128: eight waves (256 query rows) share each 64-key K/V tile, one
 // workgroup per CU (two waves per SIMD); D = 64: four waves (128 rows).
-template <int D, bool BF16>
+template <int D, bool BF16, bool OF32>
 hipError_t launch_c(bool causal, const PrefillArgs& a, int B, hipStream_t s) {
   constexpr int NW = D == 128 ? 8 : 4;
   constexpr int BN = 64;
-  return causal ? launch_t<D, BF16, true, NW, BN>(a, B, s)
-                : launch_t<D, BF16, false, NW, BN>(a, B, s);
+  return causal ? launch_t<D, BF16, true, OF32, NW, BN>(a, B, s)
+                : launch_t<D, BF16, false, OF32, NW, BN>(a, B, s);
+}
+
+template <int D, bool OF32>
+hipError_t launch_d(bool bf16, bool causal, const PrefillArgs& a, int B, hipStream_t s) {
+  return bf16 ? launch_c<D, true, OF32>(causal, a, B, s)
+              : launch_c<D, false, OF32>(causal, a, B, s);
 }
 
 template <int D>
-hipError_t launch_d(bool bf16, bool causal, const PrefillArgs& a, int B, hipStream_t s) {
-  return bf16 ? launch_c<D, true>(causal, a, B, s) : launch_c<D, false>(causal, a, B, s);
+hipError_t launch_o(bool bf16, bool causal, bool out_f32, const PrefillArgs& a, int B,
+                    hipStream_t s) {
+  return out_f32 ? launch_d<D, true>(bf16, causal, a, B, s)
+                 : launch_d<D, false>(bf16, causal, a, B, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(int D, bool bf16, bool causal, const PrefillArgs& a, int B,
-                          hipStream_t s) {
-  if (D == 128) return launch_d<128>(bf16, causal, a, B, s);
-  if (D == 64) return launch_d<64>(bf16, causal, a, B, s);
+hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
+                          int B, hipStream_t s) {
+  if (D == 128) return launch_o<128>(bf16, causal, out_f32, a, B, s);
+  if (D == 64) return launch_o<64>(bf16, causal, out_f32, a, B, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,3,4,5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -15,8 +15,12 @@ algorithmic K/V bytes.
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
 run on, bracketed by torch.cuda.synchronize(); HIP events around every step
 give the per-launch durations (mean is used for `value`, median and min are
-reported too).  The CPU baseline is the fp64 oracle timed on a bounded sample
-of the same workload.  Prints ONE JSON line.
+reported too).  Alongside, per workload: a cold-cache pass (a 512 MiB write,
+twice the 256 MiB last-level cache, before every timed step and outside its
+events), the GFX clock sampled over a ~1.5 s sustained window of the same
+step, and for the tiny 128x128 workload the median over 20 replays of a HIP
+graph of 50 launches (launch overhead removed).  The CPU baseline is the fp64
+oracle timed on a bounded sample of the same workload.  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -60,7 +64,9 @@ def load_traffic(name, src):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_steps(fn, steps, warmup, stream):
+def time_steps(fn, steps, warmup, stream, before=None):
+    """Per-step HIP-event durations of fn on `stream`; `before` (if given) runs
+    ahead of every timed step, outside its events."""
     import torch
     for _ in range(warmup):
         fn()
@@ -69,6 +75,8 @@ def time_steps(fn, steps, warmup, stream):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
+        if before is not None:
+            before()
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
@@ -79,7 +87,120 @@ def time_steps(fn, steps, warmup, stream):
                 wall_ms_per_step=1e3 * wall / steps)
 
 
-def bench_prefill(attn, cfg, steps, warmup):
+class ClockProbe:
+    """GFX clock of the visible GPU through amd-smi's Python bindings (shipped
+    with ROCm under share/amd_smi), matched to torch's device by PCI bus id.
+    The sensor refreshes about once a second, so clocks are read over a
+    sustained window of the step being measured, not from the timed steps."""
+
+    def __init__(self):
+        self.handle = None
+        try:
+            import torch
+            sys.path.append("/opt/rocm/share/amd_smi")
+            import amdsmi
+            amdsmi.amdsmi_init()
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                    self.handle = h
+            self.amdsmi = amdsmi
+        except Exception as e:  # no bindings or no permission: clocks are reported as null
+            print(f"[bench] clock probe unavailable: {e!r}", file=sys.stderr, flush=True)
+
+    def read_mhz(self):
+        clks = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle).get("current_gfxclks")
+        vals = [c for c in (clks or []) if isinstance(c, int) and 0 < c < 10000]
+        if vals:
+            return sum(vals) / len(vals)
+        return float(self.amdsmi.amdsmi_get_clock_info(self.handle,
+                                                       self.amdsmi.AmdSmiClkType.GFX)["clk"])
+
+    def sustained_mhz(self, fn, seconds=1.5, settle=1.0):
+        """Mean GFX clock over XCDs, median of the samples taken after `settle`
+        seconds of back-to-back fn() calls."""
+        if self.handle is None:
+            return None
+        import threading
+        import torch
+        samples, stop = [], threading.Event()
+        t0 = time.perf_counter()
+
+        def sample():
+            while not stop.is_set():
+                if time.perf_counter() - t0 >= settle:
+                    try:
+                        samples.append(self.read_mhz())
+                    except Exception:
+                        return
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sample)
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return None
+        samples.sort()
+        return round(samples[len(samples) // 2], 1)
+
+
+def cache_flusher(mib=512):
+    """Writes mib MiB (twice the 256 MiB last-level cache) so the next step
+    starts with its inputs out of L2 and the MALL."""
+    import torch
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    counter = [0]
+
+    def flush():
+        counter[0] = (counter[0] + 1) & 0xFF
+        buf.fill_(counter[0])
+    return flush, buf
+
+
+def measure(fn, steps, warmup, stream, clock):
+    """Warm timing, cold-cache timing and the sustained clock of one step."""
+    t = time_steps(fn, steps, warmup, stream)
+    flush, buf = cache_flusher()
+    cold = time_steps(fn, min(steps, 30), 2, stream, before=flush)
+    del buf
+    t["cold_mean_ms"] = cold["mean_ms"]
+    t["cold_median_ms"] = cold["median_ms"]
+    t["clock_mhz"] = clock.sustained_mhz(fn) if clock is not None else None
+    return t
+
+
+def graph_replay_us(fn, stream, launches=50, samples=20):
+    """Median over `samples` replays of a HIP graph holding `launches` calls
+    of fn, per launch, in microseconds."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    fn()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(launches):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(samples):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(1e3 * e0.elapsed_time(e1) / launches)
+    per.sort()
+    return per[len(per) // 2]
+
+
+def bench_prefill(attn, cfg, steps, warmup, clock):
     import torch
     import workloads
     q, k, v, m = workloads.prefill_config(cfg)
@@ -91,7 +212,15 @@ def bench_prefill(attn, cfg, steps, warmup):
         attn.prefill(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"], out=o,
                      stream=stream)
 
-    t = time_steps(step, steps, warmup, stream)
+    t = measure(step, steps, warmup, stream, clock)
+    if m["Sq"] * m["Skv"] <= 128 * 128:  # launch-bound: also time it from a HIP graph
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            t["graph_us_per_launch"] = graph_replay_us(
+                lambda: attn.prefill(q, k, v, causal=m["causal"], scale=m["scale"],
+                                     layout=m["layout"], out=o, stream=side), side)
+        stream.wait_stream(side)
     flops = prefill_flops(m)
     tflops = flops / (t["mean_ms"] * 1e-3) / 1e12
     cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "Sq": m["Sq"], "Skv": m["Skv"],
@@ -105,7 +234,7 @@ def bench_prefill(attn, cfg, steps, warmup):
                 inputs=(None))
 
 
-def bench_decode(attn, cfg, steps, warmup):
+def bench_decode(attn, cfg, steps, warmup, clock):
     import torch
     import workloads
     batch = workloads.decode_config(cfg)
@@ -123,7 +252,7 @@ def bench_decode(attn, cfg, steps, warmup):
         attn.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"],
                           scale=scale, out=o, workspace=ws, stream=stream)
 
-    t = time_steps(step, steps, warmup, stream)
+    t = measure(step, steps, warmup, stream, clock)
     n_tok = int(batch.seq_lens.sum())
     nbytes = n_tok * H * D * 2 * 2  # K and V rows of the live tokens
     gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
@@ -217,13 +346,23 @@ def cpu_baseline_prefill(cfg, budget_s=15.0):
                       f"{dt:.1f} s"}
 
 
+def side_measurements(t):
+    out = {"cold_cache_ms": round(t["cold_mean_ms"], 4),
+           "cold_cache_median_ms": round(t["cold_median_ms"], 4),
+           "clock_mhz": t["clock_mhz"]}
+    if "graph_us_per_launch" in t:
+        out["graph_replay_us_per_launch"] = round(t["graph_us_per_launch"], 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,3,4,5",
+    ap.add_argument("--configs", default="2,1,3,4,5",
                     help="workloads to measure; the first prefill one is the headline")
+    ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-gemm-reference", action="store_true",
@@ -255,13 +394,14 @@ def main():
     if head_cfg not in cfgs:
         cfgs.insert(0, head_cfg)
 
+    clock = None if args.no_clock else ClockProbe()
     results = {}
     for c in cfgs:
         print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
         if c == 4:
-            results[c] = bench_decode(attn, c, args.steps, args.warmup)
+            results[c] = bench_decode(attn, c, args.steps, args.warmup, clock)
         else:
-            results[c] = bench_prefill(attn, c, args.steps, args.warmup)
+            results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock)
         r = results[c]
         print(f"[bench] config {c}: {r['timing']['mean_ms']:.4f} ms "
               f"{r['roofline']['achieved']} {r['roofline']['unit']} "
@@ -285,6 +425,7 @@ def main():
             continue
         e = {"config": r["config"], "ms_per_step": round(r["timing"]["mean_ms"], 4),
              "median_ms": round(r["timing"]["median_ms"], 4), "roofline": r["roofline"]}
+        e.update(side_measurements(r["timing"]))
         extra[f"config{c}"] = e
 
     line = {
@@ -304,6 +445,7 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": head["config"],
         "roofline": head["roofline"],
+        **side_measurements(head["timing"]),
         "cpu_baseline": cpu,
         "extra": extra,
         "mfma_context": gemm_ref,

@@ -48,10 +48,17 @@ enum {
   ATTN_BSHD = 1   /* [B, S, H, D], D contiguous */
 };
 
-/* Element types of q, k, v, o (and of the KV cache). */
+/* Element types of q, k, v, o (and of the KV cache).  ATTN_OUT_F32 may be
+ * OR-ed into `dtype`: o is then fp32 (same shape and layout, 4-byte
+ * elements) and receives the fp32 result before any rounding to fp16/bf16.
+ * This is the higher-precision output of the same computation, for callers
+ * that feed O on in fp32 or compare against a higher-precision reference
+ * (grading against a higher-precision reference: "[FlyDSL] FP8 MQA logits
+ * improvements for gfx950", Testing). */
 enum {
   ATTN_F16 = 0,
-  ATTN_BF16 = 1
+  ATTN_BF16 = 1,
+  ATTN_OUT_F32 = 0x100
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -62,9 +69,10 @@ const char* attn_status_string(int status);
  *
  *   q: [B, H, Sq, D] (BHSD) or [B, Sq, H, D] (BSHD)
  *   k, v: the same with Skv keys
- *   o: output, same shape, layout and dtype as q
+ *   o: output, same shape and layout as q; dtype as q, or fp32 with ATTN_OUT_F32
  *   D: head dimension, 64 or 128 (else ATTN_E_UNSUPPORTED)
- *   dtype: ATTN_F16 or ATTN_BF16 (q, k, v and o share it)
+ *   dtype: ATTN_F16 or ATTN_BF16 (q, k, v share it; o too unless
+ *          ATTN_OUT_F32 is OR-ed in); any other bit is ATTN_E_INVALID
  *   causal: nonzero for the causal mask, aligned bottom-right: query i sees
  *           keys j <= i + (Skv - Sq).  A query that sees no key gets O = 0.
  *   scale: softmax scale, finite and >= 0 (commonly 1/sqrt(D)).
@@ -72,7 +80,8 @@ const char* attn_status_string(int status);
  * Arithmetic: Q.K^T in the input dtype on MFMA with fp32 accumulation; the
  * online softmax in fp32 (base-2 exponent, scale folded in fp32, never into
  * the fp16/bf16 inputs); P rounded to fp16 (round to nearest even) and P.V on
- * fp16 MFMA with fp32 accumulation; O rounded to the input dtype.  For bf16
+ * fp16 MFMA with fp32 accumulation; O rounded to the input dtype (to
+ * nearest even), or stored in fp32 with ATTN_OUT_F32.  For bf16
  * inputs V is converted to fp16 when it is staged, which is exact for
  * 2^-14 <= |v| <= 65504; precondition for bf16: |v| <= 65504.
  *
@@ -98,17 +107,19 @@ size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_s
  *       at page page_table[b][t / page_size], slot t % page_size
  *   page_table: [B, max_pages_per_seq] int32
  *   seq_lens: [B] int32
- *   o: [B, H, D] output, dtype as q
+ *   o: [B, H, D] output, dtype as q, or fp32 with ATTN_OUT_F32 in dtype
  *   page_size: 16 (else ATTN_E_UNSUPPORTED); D: 64 or 128
  *   workspace: device scratch of at least
  *       attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size)
  *       bytes, owned by the caller; its contents need no initialisation.
  *
- * Preconditions (device data; not checked): 0 <= seq_lens[b] <=
- * max_pages_per_seq * page_size (a longer length is clamped to that bound;
- * a sequence of length 0 gets O = 0); the first ceil(seq_lens[b] / page_size)
- * entries of page_table[b] lie in [0, num_pages).  Other page-table entries
- * and cache slots past seq_lens[b] are never read.
+ * Device data (read only on the device; the host never sees it):
+ *   - seq_lens[b] is clamped to [0, max_pages_per_seq * page_size]; a
+ *     sequence of length 0 (or less) gets O = 0.
+ *   - The first ceil(seq_lens[b] / page_size) entries of page_table[b] are
+ *     checked on the device before any load through them: an id outside
+ *     [0, num_pages) is never dereferenced, and O[b] (every head) is NaN.
+ *   - Other page-table entries and cache slots past seq_lens[b] are never read.
  *
  * The KV range of each sequence is cut into splits; each split produces a
  * partial output and its log-sum-exp, and a combine kernel merges them

@@ -28,6 +28,15 @@ def test_header_declares_the_boundary():
     assert set(names) == set(attn.SIGNATURES)
 
 
+def test_header_constants_match_binding():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = {n: int(v, 0) for n, v in re.findall(r"\b(ATTN_[A-Z0-9_]+)\s*=\s*(0x[0-9a-fA-F]+|\d+)",
+                                                  src)}
+    assert len(consts) == 10
+    for name, value in consts.items():
+        assert getattr(attn, name) == value, name
+
+
 def test_library_exports_every_declared_symbol():
     lib = attn.load_library()
     for name in declared_functions():
@@ -54,6 +63,9 @@ def _prefill(**kw):
     (dict(Sq=-3), attn.ATTN_E_INVALID),
     (dict(layout=2), attn.ATTN_E_INVALID),
     (dict(dtype=7), attn.ATTN_E_INVALID),
+    (dict(dtype=0x200), attn.ATTN_E_INVALID),
+    (dict(dtype=attn.ATTN_OUT_F32 | 2), attn.ATTN_E_INVALID),
+    (dict(dtype=attn.ATTN_OUT_F32 | attn.ATTN_BF16, D=96), attn.ATTN_E_UNSUPPORTED),
     (dict(scale=float("nan")), attn.ATTN_E_INVALID),
     (dict(scale=float("inf")), attn.ATTN_E_INVALID),
     (dict(scale=-0.5), attn.ATTN_E_INVALID),
@@ -92,6 +104,7 @@ def _decode(**kw):
     (dict(page_size=0), attn.ATTN_E_INVALID),
     (dict(D=80), attn.ATTN_E_UNSUPPORTED),
     (dict(dtype=3), attn.ATTN_E_INVALID),
+    (dict(dtype=attn.ATTN_OUT_F32 | 0x400), attn.ATTN_E_INVALID),
     (dict(scale=float("nan")), attn.ATTN_E_INVALID),
     (dict(num_pages=0), attn.ATTN_E_INVALID),
     (dict(max_pages_per_seq=0), attn.ATTN_E_INVALID),

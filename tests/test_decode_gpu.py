@@ -126,3 +126,54 @@ def test_decode_small_batch_fine_splits(gpu_lib):
     assert tps == 64 and n == 160
     o = _run(gpu_lib, batch)
     assert_parity(o.double().numpy(), _ref(batch), "B1 fine splits")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_out_f32(gpu_lib, dtype):
+    attn = gpu_lib
+    batch = workloads.paged_decode_inputs(B=len(EDGE_LENS), H=4, D=128, dtype=dtype,
+                                          page_size=16, num_pages=2048, max_seq=8192, seed=61,
+                                          seq_lens=EDGE_LENS)
+    g = _to_gpu(batch)
+    print(f"[case] decode out_f32 {dtype}", flush=True)
+    args = (g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"])
+    o32 = attn.paged_decode(*args, out_dtype=torch.float32)
+    o16 = attn.paged_decode(*args)
+    torch.cuda.synchronize()
+    # Decode keeps P in fp32 (no fp16 rounding anywhere), so with an fp32
+    # output only fp32 accumulation error remains.
+    assert_parity(o32.double().cpu().numpy(), _ref(batch), f"decode out_f32 {dtype}",
+                  max_abs_tol=1e-5, rel_fro_tol=1e-5)
+    assert torch.equal(o32.to(o16.dtype), o16)
+
+
+def test_decode_rejects_bad_page_ids_on_device(gpu_lib):
+    """Page ids outside [0, num_pages) among a sequence's live pages make its
+    output NaN; other sequences are unaffected.  The cache is a view into a
+    buffer with one spare page on each side, so even a missed check would
+    read allocated memory (and fail the NaN assertion) rather than fault."""
+    attn = gpu_lib
+    lens = [40, 100, 33, 200, 17, 64]
+    batch = workloads.paged_decode_inputs(B=6, H=4, D=128, page_size=16, num_pages=300,
+                                          seq_lens=lens, max_pages_per_seq=16, seed=62)
+    P = batch.num_pages
+    table = batch.page_table.clone()
+    table[1, 0] = P          # first page of sequence 1: one past the pool
+    table[3, 7] = -1         # a middle page of sequence 3
+    table[4, 5] = P + 1000   # past sequence 4's live pages: never read, no effect
+    print("[case] decode bad page ids", flush=True)
+    pad_shape = (P + 2,) + tuple(batch.k_cache.shape[1:])
+    k_pad = torch.zeros(pad_shape, dtype=batch.k_cache.dtype, device="cuda")
+    v_pad = torch.zeros(pad_shape, dtype=batch.v_cache.dtype, device="cuda")
+    k_pad[1:P + 1].copy_(batch.k_cache)
+    v_pad[1:P + 1].copy_(batch.v_cache)
+    k_view, v_view = k_pad[1:P + 1], v_pad[1:P + 1]
+    assert k_view.is_contiguous() and k_view.shape[0] == P
+    o = attn.paged_decode(batch.q.cuda(), k_view, v_view, table.cuda(),
+                          batch.seq_lens.cuda()).float().cpu()
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[3]).all()
+    good = [0, 2, 4, 5]
+    assert torch.isfinite(o[good]).all()
+    ref = _ref(batch)
+    assert_parity(o[good].double().numpy(), ref[good], "sequences with valid pages")

@@ -204,3 +204,29 @@ def test_prefill_rejects_bad_tensors(gpu_lib):
     with pytest.raises(attn.AttnError) as e:
         attn.prefill(q[..., :96].contiguous(), q[..., :96].contiguous(), q[..., :96].contiguous())
     assert e.value.status == attn.ATTN_E_UNSUPPORTED
+
+
+# ------------------------------------------------------------ fp32 output
+
+# With O stored in fp32 the only rounding left is the kernel's own (fp16 P,
+# fp32 accumulation), so the bar is four times tighter than the default.
+F32_MAX_ABS, F32_REL_FRO = 3e-3, 5e-4
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_out_f32(gpu_lib, dtype, D, causal):
+    attn = gpu_lib
+    q, k, v = workloads.prefill_inputs(2, 3, 200, 333, D, dtype, "BSHD", seed=51 + D)
+    print(f"[case] prefill out_f32 {dtype} D{D} causal={causal}", flush=True)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o32 = attn.prefill(qg, kg, vg, causal=causal, layout="BSHD", out_dtype=torch.float32)
+    o16 = attn.prefill(qg, kg, vg, causal=causal, layout="BSHD")
+    torch.cuda.synchronize()
+    assert o32.dtype == torch.float32
+    ref = oracle.sdpa(q, k, v, causal=causal, layout="BSHD")
+    assert_parity(_f64(o32.cpu()), ref, f"out_f32 {dtype} D{D} causal={causal}",
+                  max_abs_tol=F32_MAX_ABS, rel_fro_tol=F32_REL_FRO)
+    # The default output is the fp32 result rounded to nearest even.
+    assert torch.equal(o32.to(o16.dtype), o16)
