@@ -162,14 +162,19 @@ def cache_flusher(mib=512):
     return flush, buf
 
 
+COLD = True  # cleared by --no-cold (profiling runs that should see warm steps only)
+
+
 def measure(fn, steps, warmup, stream, clock):
     """Warm timing, cold-cache timing and the sustained clock of one step."""
     t = time_steps(fn, steps, warmup, stream)
-    flush, buf = cache_flusher()
-    cold = time_steps(fn, min(steps, 30), 2, stream, before=flush)
-    del buf
-    t["cold_mean_ms"] = cold["mean_ms"]
-    t["cold_median_ms"] = cold["median_ms"]
+    t["cold_mean_ms"] = t["cold_median_ms"] = None
+    if COLD:
+        flush, buf = cache_flusher()
+        cold = time_steps(fn, min(steps, 30), 2, stream, before=flush)
+        del buf
+        t["cold_mean_ms"] = cold["mean_ms"]
+        t["cold_median_ms"] = cold["median_ms"]
     t["clock_mhz"] = clock.sustained_mhz(fn) if clock is not None else None
     return t
 
@@ -347,8 +352,8 @@ def cpu_baseline_prefill(cfg, budget_s=15.0):
 
 
 def side_measurements(t):
-    out = {"cold_cache_ms": round(t["cold_mean_ms"], 4),
-           "cold_cache_median_ms": round(t["cold_median_ms"], 4),
+    r4 = lambda x: None if x is None else round(x, 4)
+    out = {"cold_cache_ms": r4(t["cold_mean_ms"]), "cold_cache_median_ms": r4(t["cold_median_ms"]),
            "clock_mhz": t["clock_mhz"]}
     if "graph_us_per_launch" in t:
         out["graph_replay_us_per_launch"] = round(t["graph_us_per_launch"], 2)
@@ -363,6 +368,7 @@ def main():
     ap.add_argument("--configs", default="2,1,3,4,5",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-gemm-reference", action="store_true",
@@ -394,6 +400,8 @@ def main():
     if head_cfg not in cfgs:
         cfgs.insert(0, head_cfg)
 
+    global COLD
+    COLD = not args.no_cold
     clock = None if args.no_clock else ClockProbe()
     results = {}
     for c in cfgs:
