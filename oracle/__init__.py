@@ -16,7 +16,9 @@ list):
 
 in float64 from the exact upcast of the fp16/bf16 inputs.  Paged decode is the
 same function at Sq = 1 applied to each sequence's keys and values, gathered
-explicitly through the page table.
+explicitly through the page table.  With fewer KV heads than query heads
+(grouped-query / multi-query attention, which the pages do not define), query
+head h reads KV head h // (H / H_kv).
 
 Pinned by ``tests/test_oracle.py`` (brute force at 50 digits, the torch
 library routine, closed forms, invariants) and
@@ -26,6 +28,7 @@ from .attention import (  # noqa: F401
     attend_rows,
     attention_probs,
     gather_sequence,
+    kv_head,
     n_visible,
     paged_decode,
     sdpa,

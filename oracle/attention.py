@@ -59,6 +59,18 @@ def attend_rows(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray, scale:
     return p @ values
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """KV head read by query head h when H query heads share H_kv KV heads.
+
+    The pages do not define grouped-query attention; this is its plain
+    reading: consecutive query heads form groups of H / H_kv that share one KV
+    head (H_kv = H is ordinary multi-head attention, H_kv = 1 multi-query).
+    """
+    if H_kv <= 0 or H % H_kv:
+        raise ValueError(f"{H} query heads cannot share {H_kv} KV heads evenly")
+    return h // (H // H_kv)
+
+
 def _bhsd(x: np.ndarray, layout: str) -> np.ndarray:
     if layout == "BHSD":
         return x
@@ -71,11 +83,12 @@ def sdpa(q, k, v, *, causal: bool, scale: float | None = None, layout: str = "BH
          chunk: int = 2048) -> np.ndarray:
     """Full attention output in float64, in the inputs' layout.
 
-    q: [B,H,Sq,D] (BHSD) or [B,Sq,H,D] (BSHD); k, v likewise with Skv.
+    q: [B,H,Sq,D] (BHSD) or [B,Sq,H,D] (BSHD); k, v likewise with Skv keys
+    and H_kv heads (H_kv divides H; see ``kv_head``).
     """
     qf, kf, vf = (_bhsd(to_f64(t), layout) for t in (q, k, v))
     B, H, Sq, D = qf.shape
-    Skv = kf.shape[2]
+    H_kv, Skv = kf.shape[1], kf.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     vis = n_visible(Sq, Skv, causal)
@@ -84,7 +97,8 @@ def sdpa(q, k, v, *, causal: bool, scale: float | None = None, layout: str = "BH
         for h in range(H):
             for r0 in range(0, Sq, chunk):
                 r1 = min(Sq, r0 + chunk)
-                out[b, h, r0:r1] = attend_rows(qf[b, h, r0:r1], kf[b, h], vf[b, h], scale, vis[r0:r1])
+                g = kv_head(h, H, H_kv)
+                out[b, h, r0:r1] = attend_rows(qf[b, h, r0:r1], kf[b, g], vf[b, g], scale, vis[r0:r1])
     return _bhsd(out, layout)
 
 
@@ -98,13 +112,13 @@ def sdpa_rows(q, k, v, rows, *, causal: bool, scale: float | None = None,
     rows = [tuple(int(x) for x in r) for r in rows]
     if layout == "BHSD":
         B, H, Sq, D = q.shape
-        Skv = k.shape[2]
+        H_kv, Skv = k.shape[1], k.shape[2]
 
         def head(t, b, h):
             return t[b, h]
     elif layout == "BSHD":
         B, Sq, H, D = q.shape
-        Skv = k.shape[1]
+        Skv, H_kv = k.shape[1], k.shape[2]
 
         def head(t, b, h):
             return t[b, :, h]
@@ -118,8 +132,8 @@ def sdpa_rows(q, k, v, rows, *, causal: bool, scale: float | None = None,
     for n, (b, h, i) in enumerate(rows):
         groups.setdefault((b, h), []).append((n, i))
     for (b, h), items in groups.items():
-        kf = to_f64(head(k, b, h))
-        vf = to_f64(head(v, b, h))
+        kf = to_f64(head(k, b, kv_head(h, H, H_kv)))
+        vf = to_f64(head(v, b, kv_head(h, H, H_kv)))
         qh = head(q, b, h)
         idx = np.array([i for _, i in items])
         qf = to_f64(qh[torch.as_tensor(idx)] if isinstance(qh, torch.Tensor) else qh[idx])
@@ -145,12 +159,12 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: float | No
                  batch_indices=None) -> np.ndarray:
     """Decode attention (one query per sequence) through a page table, float64.
 
-    q: [B, H, D]; k_cache, v_cache: [num_pages, page_size, H, D];
-    page_table: [B, max_pages] int; seq_lens: [B] int.  Returns [B, H, D]
-    (or [len(batch_indices), H, D]).
+    q: [B, H, D]; k_cache, v_cache: [num_pages, page_size, H_kv, D] (H_kv
+    divides H; see ``kv_head``); page_table: [B, max_pages] int; seq_lens: [B]
+    int.  Returns [B, H, D] (or [len(batch_indices), H, D]).
     """
     B, H, D = q.shape
-    page_size = int(k_cache.shape[1])
+    page_size, H_kv = int(k_cache.shape[1]), int(k_cache.shape[2])
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     table = np.asarray(page_table.cpu() if isinstance(page_table, torch.Tensor) else page_table)
@@ -163,6 +177,7 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: float | No
         vf = to_f64(gather_sequence(v_cache, table[b], n, page_size))
         qf = to_f64(q[b])                                                # [H, D]
         for h in range(H):
-            out[n_out, h] = attend_rows(qf[h:h + 1], kf[:, h], vf[:, h], scale,
+            g = kv_head(h, H, H_kv)
+            out[n_out, h] = attend_rows(qf[h:h + 1], kf[:, g], vf[:, g], scale,
                                         np.array([n]))[0]
     return out

@@ -19,7 +19,10 @@ import workloads   # noqa: E402
 CASES = [
     dict(B=1, H=2, Sq=5, Skv=7, D=4, dtype="f16", layout="BHSD", causal=True, seed=1001),
     dict(B=1, H=1, Sq=6, Skv=6, D=8, dtype="bf16", layout="BSHD", causal=False, seed=1002),
+    dict(B=1, H=4, h_kv=2, Sq=4, Skv=6, D=4, dtype="f16", layout="BSHD", causal=True, seed=1004),
 ]
+DECODE_GQA = dict(B=2, H=4, h_kv=1, D=4, dtype="bf16", page_size=16, num_pages=8, seed=1005,
+                  seq_lens=[3, 18])
 DECODE = dict(B=3, H=2, D=4, dtype="f16", page_size=16, num_pages=8, seed=1003,
               seq_lens=[1, 16, 21])
 
@@ -28,12 +31,15 @@ def build():
     out = {"prefill": [], "decode": None}
     for c in CASES:
         q, k, v = workloads.prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
-                                           c["layout"], seed=c["seed"])
+                                           c["layout"], seed=c["seed"], h_kv=c.get("h_kv"))
         o = oracle.sdpa(q, k, v, causal=c["causal"], layout=c["layout"])
         out["prefill"].append(dict(case=c, out=o.round(15).tolist()))
     b = workloads.paged_decode_inputs(**DECODE)
     o = oracle.paged_decode(b.q, b.k_cache, b.v_cache, b.page_table, b.seq_lens)
     out["decode"] = dict(case=DECODE, out=o.round(15).tolist())
+    b = workloads.paged_decode_inputs(**DECODE_GQA)
+    o = oracle.paged_decode(b.q, b.k_cache, b.v_cache, b.page_table, b.seq_lens)
+    out["decode_gqa"] = dict(case=DECODE_GQA, out=o.round(15).tolist())
     return out
 
 

@@ -315,10 +315,73 @@ def check_decode_nan_poison():
     _close(a, b, 0.0, "NaN poison")
 
 
+# ------------------------------------------------- grouped-query attention
+
+GQA_CASES = [  # (B, H, H_kv, Sq, Skv, D, causal, layout)
+    (2, 8, 2, 9, 13, 16, False, "BHSD"),
+    (1, 8, 2, 12, 12, 8, True, "BSHD"),
+    (1, 6, 1, 7, 10, 8, True, "BHSD"),     # multi-query
+    (2, 4, 4, 5, 9, 8, False, "BSHD"),     # H_kv = H: ordinary multi-head
+]
+
+
+def check_gqa_library():
+    """torch's routine with enable_gqa (consecutive query heads share a KV head)."""
+    for n, (B, H, Hk, Sq, Skv, D, causal, layout) in enumerate(GQA_CASES):
+        q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "bf16", layout, seed=500 + n, h_kv=Hk)
+        got = oracle.sdpa(q, k, v, causal=causal, layout=layout)
+        qt, kt, vt = ((t.transpose(1, 2) if layout == "BSHD" else t).to(F64) for t in (q, k, v))
+        mask = torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq) if causal else None
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, enable_gqa=True).numpy()
+        if layout == "BSHD":
+            ref = ref.transpose(0, 2, 1, 3)
+        _close(got, ref, 1e-12, f"gqa library case {n}")
+
+
+def check_gqa_group_locality():
+    """Changing KV head g changes exactly the outputs of query heads in group g."""
+    B, H, Hk, S, D = 1, 8, 4, 6, 8
+    q, k, v = workloads.prefill_inputs(B, H, S, S, D, "f16", "BHSD", seed=510, h_kv=Hk)
+    base = oracle.sdpa(q, k, v, causal=False)
+    for g in range(Hk):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, g] = -k2[:, g]
+        v2[:, g] = v2[:, g] + 1
+        moved = oracle.sdpa(q, k2, v2, causal=False)
+        changed = [h for h in range(H) if not np.allclose(moved[0, h], base[0, h], atol=0)]
+        assert changed == list(range(g * H // Hk, (g + 1) * H // Hk)), (g, changed)
+
+
+def check_gqa_rows_and_decode():
+    """Sampled rows and paged decode follow the same head mapping as the full output."""
+    B, H, Hk, Sq, Skv, D = 2, 6, 3, 11, 20, 8
+    for layout in ("BHSD", "BSHD"):
+        q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "f16", layout, seed=520, h_kv=Hk)
+        full = oracle.sdpa(q, k, v, causal=True, layout=layout)
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in (0, 5, Sq - 1)]
+        got = oracle.sdpa_rows(q, k, v, rows, causal=True, layout=layout)
+        ref = [full[b, h, i] if layout == "BHSD" else full[b, i, h] for b, h, i in rows]
+        _close(got, np.array(ref), 1e-13, f"gqa rows {layout}")
+    batch = workloads.paged_decode_inputs(B=4, H=8, D=16, page_size=4, num_pages=64, seed=521,
+                                          seq_lens=[1, 4, 9, 30], h_kv=2)
+    got = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens)
+    for b in range(4):
+        n = int(batch.seq_lens[b])
+        tok = torch.arange(n)
+        pages = batch.page_table[b].long()[tok // 4]
+        kk = batch.k_cache[pages, tok % 4].to(F64).transpose(0, 1)[None]   # [1, H_kv, n, D]
+        vv = batch.v_cache[pages, tok % 4].to(F64).transpose(0, 1)[None]
+        qq = batch.q[b].to(F64)[None, :, None, :]                          # [1, H, 1, D]
+        ref = F.scaled_dot_product_attention(qq, kk, vv, enable_gqa=True)[0, :, 0].numpy()
+        _close(got[b], ref, 1e-12, f"gqa decode b{b}")
+
+
 ALL_CHECKS = [
     check_bruteforce, check_library_sdpa, check_rows_match_full, check_ones_v, check_causal_row0,
     check_zero_keys, check_two_keys, check_dominant_key, check_zero_scale,
     check_probs_rows_sum_to_one, check_logit_shift, check_permutations, check_layouts_agree,
     check_decode_library, check_decode_matches_prefill_row, check_decode_pool_permutation,
-    check_decode_nan_poison,
+    check_decode_nan_poison, check_gqa_library, check_gqa_group_locality,
+    check_gqa_rows_and_decode,
 ]

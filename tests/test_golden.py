@@ -13,5 +13,8 @@ def test_oracle_matches_stored_golden():
     for s, f in zip(stored["prefill"], fresh["prefill"]):
         assert s["case"] == f["case"]
         np.testing.assert_allclose(np.array(f["out"]), np.array(s["out"]), rtol=0, atol=1e-14)
-    np.testing.assert_allclose(np.array(fresh["decode"]["out"]), np.array(stored["decode"]["out"]),
-                               rtol=0, atol=1e-14)
+    assert len(stored["prefill"]) == len(fresh["prefill"])
+    for key in ("decode", "decode_gqa"):
+        assert stored[key]["case"] == fresh[key]["case"]
+        np.testing.assert_allclose(np.array(fresh[key]["out"]), np.array(stored[key]["out"]),
+                                   rtol=0, atol=1e-14)

@@ -64,6 +64,14 @@ def _gather_from_end(cache, page_row, n_tokens, page_size):
     return sel.reshape(n_pages * page_size, *sel.shape[2:])[:n_tokens]
 
 
+def _kv_head_strided(h, H, H_kv):
+    return h % H_kv
+
+
+def _kv_head_reversed(h, H, H_kv):
+    return H_kv - 1 - h // (H // H_kv)
+
+
 MUTATIONS = [
     ("n_visible", _top_left, [pins.check_library_sdpa, pins.check_bruteforce]),
     ("n_visible", _off_by_one, [pins.check_causal_row0, pins.check_library_sdpa]),
@@ -74,6 +82,8 @@ MUTATIONS = [
     ("gather_sequence", _gather_slot_major, [pins.check_decode_library]),
     ("gather_sequence", _gather_from_end, [pins.check_decode_library,
                                            pins.check_decode_matches_prefill_row]),
+    ("kv_head", _kv_head_strided, [pins.check_gqa_library, pins.check_gqa_group_locality]),
+    ("kv_head", _kv_head_reversed, [pins.check_gqa_library, pins.check_gqa_rows_and_decode]),
 ]
 
 

@@ -44,12 +44,22 @@ PREFILL_CONFIGS = {
             layout="BSHD", causal=True, amp=0.5, scale=None),
     5: dict(name="long-causal-32k", B=1, H=64, Sq=32768, Skv=32768, D=128, dtype="bf16",
             layout="BHSD", causal=True, amp=1.0, scale=None),
+    # Grouped-query attention (four query heads per KV head), otherwise shaped
+    # like the causal 8k workload.
+    6: dict(name="gqa-causal-bshd-8k", B=2, H=32, H_kv=8, Sq=8192, Skv=8192, D=128,
+            dtype="bf16", layout="BSHD", causal=True, amp=0.5, scale=None),
 }
 
 # Paged decode workload.
 DECODE_CONFIGS = {
     4: dict(name="paged-decode-b64", B=64, H=32, D=128, dtype="f16", page_size=16,
             num_pages=65536, min_seq=1, max_seq=8192),
+    # Grouped-query (8 KV heads for 32 query heads) and multi-query (1 KV head)
+    # decode over the same length mix.
+    7: dict(name="gqa-paged-decode-b64", B=64, H=32, H_kv=8, D=128, dtype="f16",
+            page_size=16, num_pages=65536, min_seq=1, max_seq=8192),
+    8: dict(name="mqa-paged-decode-b256", B=256, H=32, H_kv=1, D=128, dtype="f16",
+            page_size=16, num_pages=131072, min_seq=1, max_seq=8192),
 }
 
 
@@ -73,12 +83,14 @@ def _draw(shape, g, amp, dtype):
     return x.to(DTYPES[dtype])
 
 
-def prefill_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, seed=0):
-    """Seeded q, k, v (CPU tensors in ``layout``), drawn q then k then v."""
+def prefill_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, seed=0, h_kv=None):
+    """Seeded q, k, v (CPU tensors in ``layout``), drawn q then k then v.
+    k and v have ``h_kv`` heads (default H)."""
     g = torch.Generator().manual_seed(seed)
+    hk = H if h_kv is None else h_kv
     q = _draw(layout_shape(B, H, Sq, D, layout), g, amp, dtype)
-    k = _draw(layout_shape(B, H, Skv, D, layout), g, amp, dtype)
-    v = _draw(layout_shape(B, H, Skv, D, layout), g, amp, dtype)
+    k = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
+    v = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
     return q, k, v
 
 
@@ -86,7 +98,8 @@ def prefill_config(cfg: int):
     """(q, k, v, meta) for one of the numbered prefill workloads, seeded with its number."""
     c = dict(PREFILL_CONFIGS[cfg])
     q, k, v = prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
-                             c["layout"], c["amp"], seed=cfg)
+                             c["layout"], c["amp"], seed=cfg, h_kv=c.get("H_kv"))
+    c.setdefault("H_kv", c["H"])
     if c["scale"] is None:
         c["scale"] = default_scale(c["D"])
     c["seed"] = cfg
@@ -96,8 +109,8 @@ def prefill_config(cfg: int):
 @dataclass
 class PagedBatch:
     q: torch.Tensor            # [B, H, D]
-    k_cache: torch.Tensor      # [num_pages, page_size, H, D]
-    v_cache: torch.Tensor      # [num_pages, page_size, H, D]
+    k_cache: torch.Tensor      # [num_pages, page_size, H_kv, D]
+    v_cache: torch.Tensor      # [num_pages, page_size, H_kv, D]
     page_table: torch.Tensor   # [B, max_pages_per_seq] int32
     seq_lens: torch.Tensor     # [B] int32
     page_size: int
@@ -118,7 +131,7 @@ def _np_bits_dtype(dtype):
 
 def paged_decode_inputs(B, H, D, dtype="f16", page_size=16, num_pages=65536,
                         min_seq=1, max_seq=8192, seed=0, fill=0.0, seq_lens=None,
-                        amp=1.0, max_pages_per_seq=None):
+                        amp=1.0, max_pages_per_seq=None, h_kv=None):
     """Seeded paged-decode batch (CPU tensors).
 
     ``seq_lens`` may be given explicitly (a list of ints); otherwise it is drawn
@@ -147,12 +160,13 @@ def paged_decode_inputs(B, H, D, dtype="f16", page_size=16, num_pages=65536,
         page_table[b, :npg] = perm[cursor:cursor + npg].to(torch.int32)
         cursor += npg
 
+    hk = H if h_kv is None else h_kv
     q = _draw((B, H, D), g, amp, dtype)
     n_live = int(lens.sum())
-    k_live = _draw((n_live, H, D), g, amp, dtype)
-    v_live = _draw((n_live, H, D), g, amp, dtype)
+    k_live = _draw((n_live, hk, D), g, amp, dtype)
+    v_live = _draw((n_live, hk, D), g, amp, dtype)
 
-    shape = (num_pages, page_size, H, D)
+    shape = (num_pages, page_size, hk, D)
     tdt = DTYPES[dtype]
     if fill == 0.0 and not math.isnan(fill):
         k_np = np.zeros(shape, dtype=np.uint16)
@@ -178,7 +192,7 @@ def paged_decode_inputs(B, H, D, dtype="f16", page_size=16, num_pages=65536,
 
     k_cache = torch.from_numpy(k_np).view(torch.int16).view(tdt)
     v_cache = torch.from_numpy(v_np).view(torch.int16).view(tdt)
-    meta = dict(B=B, H=H, D=D, dtype=dtype, page_size=page_size, num_pages=num_pages,
+    meta = dict(B=B, H=H, H_kv=hk, D=D, dtype=dtype, page_size=page_size, num_pages=num_pages,
                 seed=seed, fill=fill, n_live_tokens=n_live, unused_page=unused_page)
     return PagedBatch(q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
                       seq_lens=lens.to(torch.int32), page_size=page_size, meta=meta)
@@ -188,7 +202,8 @@ def decode_config(cfg: int, fill=0.0):
     """PagedBatch for one of the numbered decode workloads, seeded with its number."""
     c = dict(DECODE_CONFIGS[cfg])
     batch = paged_decode_inputs(c["B"], c["H"], c["D"], c["dtype"], c["page_size"],
-                                c["num_pages"], c["min_seq"], c["max_seq"], seed=cfg, fill=fill)
+                                c["num_pages"], c["min_seq"], c["max_seq"], seed=cfg, fill=fill,
+                                h_kv=c.get("H_kv"))
     batch.meta.update(name=c["name"], scale=default_scale(c["D"]), config=cfg)
     return batch
 
