@@ -6,10 +6,11 @@ device memory and the current stream; nothing here computes attention, and
 there is no CPU fallback: if the shared library is missing the calls raise.
 
 Low-level functions carry the C names (``attn_prefill``,
-``attn_paged_decode``, ``attn_paged_decode_workspace_size``,
-``attn_paged_decode_num_splits``, ``attn_status_string``) and take tensors
-or raw integer pointers; ``prefill`` and ``paged_decode`` are conveniences
-that derive the sizes from tensor shapes and allocate the output.
+``attn_prefill_gqa``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
+workspace-size and split-plan queries, ``attn_status_string``) and take
+tensors or raw integer pointers; ``prefill`` and ``paged_decode`` are
+conveniences that derive the sizes (including the number of KV heads) from
+tensor shapes and allocate the output.
 """
 from __future__ import annotations
 
@@ -35,6 +36,11 @@ SIGNATURES = {
     "attn_paged_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _F,
                                _VP, _SZ, _VP]),
     "attn_paged_decode_num_splits": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "attn_prefill_gqa": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _VP]),
+    "attn_paged_decode_gqa": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I,
+                                   _F, _VP, _SZ, _VP]),
+    "attn_paged_decode_gqa_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "attn_paged_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
 }
 
 _lib = None
@@ -102,6 +108,37 @@ def attn_prefill(q, k, v, o, B, H, Sq, Skv, D, layout, dtype, causal, scale, str
                                        _stream(stream))
 
 
+def attn_prefill_gqa(q, k, v, o, B, H, H_kv, Sq, Skv, D, layout, dtype, causal, scale,
+                     stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, H_kv, Sq,
+                                           Skv, D, layout, dtype, int(bool(causal)),
+                                           float(scale), _stream(stream))
+
+
+def attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size) -> int:
+    return int(load_library().attn_paged_decode_gqa_workspace_size(B, H, H_kv, D,
+                                                                   max_pages_per_seq, page_size))
+
+
+def attn_paged_decode_gqa_num_splits(B, H, H_kv, max_pages_per_seq, page_size):
+    """(n_splits, tokens_per_split) of the grouped-query decode split plan."""
+    tps = ctypes.c_int(0)
+    n = load_library().attn_paged_decode_gqa_num_splits(B, H, H_kv, max_pages_per_seq,
+                                                        page_size, ctypes.byref(tps))
+    return int(n), int(tps.value)
+
+
+def attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_kv, D,
+                          page_size, num_pages, max_pages_per_seq, dtype, scale, workspace,
+                          workspace_bytes, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_paged_decode_gqa(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H,
+        H_kv, D, page_size, num_pages, max_pages_per_seq, dtype, float(scale), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+
+
 def attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size) -> int:
     return int(load_library().attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq,
                                                                page_size))
@@ -149,8 +186,10 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_d
     """O = softmax(Q K^T * scale [+ causal mask]) V on the GPU.
 
     q: [B,H,Sq,D] (layout "BHSD") or [B,Sq,H,D] ("BSHD"); k, v likewise with
-    Skv keys; fp16 or bf16 CUDA tensors, contiguous.  Returns o like q, or in
-    fp32 (unrounded) with out_dtype=torch.float32 or an fp32 `out`.
+    Skv keys and H_kv heads (H_kv divides H: grouped-query attention, query
+    head h reads KV head h // (H // H_kv)); fp16 or bf16 GPU tensors,
+    contiguous.  Returns o like q, or in fp32 (unrounded) with
+    out_dtype=torch.float32 or an fp32 `out`.
     """
     import torch
     if layout not in LAYOUTS:
@@ -162,12 +201,12 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_d
         raise TypeError("q, k, v must share a dtype")
     if layout == "BHSD":
         B, H, Sq, D = q.shape
-        Skv = k.shape[2]
-        kv_shape = (B, H, Skv, D)
+        H_kv, Skv = k.shape[1], k.shape[2]
+        kv_shape = (B, H_kv, Skv, D)
     else:
         B, Sq, H, D = q.shape
-        Skv = k.shape[1]
-        kv_shape = (B, Skv, H, D)
+        Skv, H_kv = k.shape[1], k.shape[2]
+        kv_shape = (B, Skv, H_kv, D)
     if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
         raise ValueError(f"k and v must have shape {kv_shape}")
     if scale is None:
@@ -176,14 +215,15 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_d
     o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
     if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
         raise ValueError("out must be a contiguous GPU tensor shaped like q")
-    _check(attn_prefill(q, k, v, o, B, H, Sq, Skv, D, LAYOUTS[layout], code,
-                        causal, scale, stream), "attn_prefill")
+    _check(attn_prefill_gqa(q, k, v, o, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], code,
+                            causal, scale, stream), "attn_prefill_gqa")
     return o
 
 
 def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=None,
                  out_dtype=None, workspace=None, stream=None):
-    """Decode attention of q [B,H,D] against a paged cache [num_pages, 16, H, D].
+    """Decode attention of q [B,H,D] against a paged cache [num_pages, 16, H_kv, D]
+    (H_kv divides H; query head h reads KV head h // (H // H_kv)).
 
     page_table [B, max_pages] and seq_lens [B] are int32 GPU tensors.  The
     workspace (a uint8 GPU tensor) is allocated here if not given.  O is like
@@ -192,9 +232,9 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=N
     """
     import torch
     B, H, D = q.shape
-    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
-    if tuple(k_cache.shape) != (num_pages, page_size, H, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H, D]")
+    num_pages, page_size, H_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (num_pages, page_size, H_kv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H_kv, D]")
     if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("page_table and seq_lens must be int32")
     for t in (q, k_cache, v_cache, page_table, seq_lens):
@@ -203,15 +243,15 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=N
     max_pages = page_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = attn_paged_decode_workspace_size(B, H, D, max_pages, page_size)
+    need = attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages, page_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     code, odt = _out_code(q, out, out_dtype)
     o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
     if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
         raise ValueError("out must be a contiguous GPU tensor shaped like q")
-    _check(attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, o, B, H, D, page_size,
-                             num_pages, max_pages, code, scale, workspace,
-                             workspace.numel() * workspace.element_size(), stream),
-           "attn_paged_decode")
+    _check(attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_kv, D,
+                                 page_size, num_pages, max_pages, code, scale, workspace,
+                                 workspace.numel() * workspace.element_size(), stream),
+           "attn_paged_decode_gqa")
     return o

@@ -42,19 +42,28 @@ struct SplitPlan {
   int tokens_per_split;
 };
 
-// Tokens per split: a multiple of four pages (the kernel's batch), 512 by
-// default, halved while the grid holds fewer than 8192 (sequence, head group,
-// split) work items, so short batches still fill 256 CUs.  Partial results
-// cost one D+1 fp32 row per split: about 0.5% of the KV bytes at 512 tokens.
-// The plan depends only on host-side sizes (never on seq_lens).
-SplitPlan plan_splits(int B, int H, int max_pages, int page_size) {
+// Tokens per split: a multiple of four pages (64 tokens), 512 by default,
+// halved while the grid holds fewer than 8192 work items (workgroups), so
+// short batches still fill 256 CUs.  Partial results cost one D+1 fp32 row
+// per split and query head: about 0.5% of the KV bytes at 512 tokens.  The
+// plan depends only on host-side sizes (never on seq_lens).
+//
+// Work items per split: group = 1 (decode.hip): B x ceil(H / 4) workgroups of
+// four waves; group > 1 (decode_gqa.hip): B x H_kv x ceil(group / 32)
+// one-wave workgroups.
+SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
   SplitPlan p{0, 0};
-  if (B <= 0 || H <= 0 || max_pages <= 0 || page_size != kDecodePageSize) return p;
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || max_pages <= 0 ||
+      page_size != kDecodePageSize)
+    return p;
+  const int group = H / H_kv;
+  const int64_t items = group == 1
+      ? (int64_t)B * ((H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG)
+      : (int64_t)B * H_kv * ((group + 31) / 32);
   const int64_t max_tokens = (int64_t)max_pages * page_size;
-  const int64_t head_groups = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
   int tps = 512;
   auto splits = [&](int t) { return (max_tokens + t - 1) / t; };
-  while (tps > 4 * kDecodePageSize && (int64_t)B * head_groups * splits(tps) < 8192) tps /= 2;
+  while (tps > 4 * kDecodePageSize && items * splits(tps) < 8192) tps /= 2;
   while (splits(tps) > 4096) tps *= 2;
   p.tokens_per_split = tps;
   p.n_splits = (int)splits(tps);
@@ -79,7 +88,14 @@ const char* attn_status_string(int status) {
 int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
                  int Skv, int D, int layout, int dtype, int causal, float scale,
                  hipStream_t stream) {
-  if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
+  return attn_prefill_gqa(q, k, v, o, B, H, H, Sq, Skv, D, layout, dtype, causal, scale, stream);
+}
+
+int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B, int H,
+                     int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
+                     float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
   if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
   bool bf16, out_f32;
   if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
@@ -92,9 +108,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
     return ATTN_E_INVALID;
 
   // In-head offsets (row * row_stride) are 32-bit in the kernel.
-  const int64_t row_stride = layout == ATTN_BHSD ? D : (int64_t)H * D;
-  const int64_t smax = Sq > Skv ? Sq : Skv;
-  if (smax * row_stride >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  const int64_t q_row = layout == ATTN_BHSD ? D : (int64_t)H * D;
+  const int64_t kv_row = layout == ATTN_BHSD ? D : (int64_t)H_kv * D;
+  if ((int64_t)Sq * q_row >= ((int64_t)1 << 31) || (int64_t)Skv * kv_row >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
   PrefillArgs a;
@@ -103,16 +120,18 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   a.v = static_cast<const uint16_t*>(v);
   a.o = o;
   a.H = H;
+  a.H_kv = H_kv;
+  a.group = H / H_kv;
   a.Sq = Sq;
   a.Skv = Skv;
   a.n_mtiles = 0;     // set by launch_prefill for the chosen tile shape
   a.total_tiles = 0;
   if (layout == ATTN_BHSD) {
     a.q_sb = (int64_t)H * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
-    a.k_sb = (int64_t)H * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
+    a.k_sb = (int64_t)H_kv * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
   } else {
     a.q_sb = (int64_t)Sq * H * D; a.q_sh = D; a.q_ss = H * D;
-    a.k_sb = (int64_t)Skv * H * D; a.k_sh = D; a.k_ss = H * D;
+    a.k_sb = (int64_t)Skv * H_kv * D; a.k_sh = D; a.k_ss = H_kv * D;
   }
   a.c = exp2_multiplier(scale);
   a.causal_off = Skv - Sq;
@@ -120,17 +139,23 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
-int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
-                                 int* tokens_per_split) {
-  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
+                                     int page_size, int* tokens_per_split) {
+  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
   if (tokens_per_split) *tokens_per_split = p.tokens_per_split;
   return p.n_splits;
 }
 
-size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
-                                        int page_size) {
+int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
+                                 int* tokens_per_split) {
+  return attn_paged_decode_gqa_num_splits(B, H, H, max_pages_per_seq, page_size,
+                                          tokens_per_split);
+}
+
+size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D, int max_pages_per_seq,
+                                            int page_size) {
   if (D != 64 && D != 128) return 0;
-  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
   if (p.n_splits == 0) return 0;
   const size_t rows = (size_t)B * H * p.n_splits;
   // partial outputs [B,H,S,D] fp32, then log-sum-exps [B,H,S] fp32, 256-B aligned
@@ -138,11 +163,18 @@ size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_s
   return o_bytes + rows * sizeof(float);
 }
 
-int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* page_table, const int32_t* seq_lens, void* o, int B, int H,
-                      int D, int page_size, int num_pages, int max_pages_per_seq, int dtype,
-                      float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
+size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
+                                        int page_size) {
+  return attn_paged_decode_gqa_workspace_size(B, H, H, D, max_pages_per_seq, page_size);
+}
+
+int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* page_table, const int32_t* seq_lens, void* o, int B,
+                          int H, int H_kv, int D, int page_size, int num_pages,
+                          int max_pages_per_seq, int dtype, float scale, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
   bool bf16, out_f32;
   if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
   if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
@@ -150,15 +182,19 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H == 0) return ATTN_OK;
   if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
-  if (B > 65535) return ATTN_E_UNSUPPORTED;
+  const int group = H / H_kv;
+  const int qchunks = (group + 31) / 32;
+  if (group == 1 ? B > 65535 : (int64_t)B * H_kv * qchunks >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;  // grid limits
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return ATTN_E_INVALID;
   if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
 
-  const SplitPlan p = plan_splits(B, H, max_pages_per_seq, page_size);
+  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
   if (p.n_splits == 0 || p.n_splits > 65535) return ATTN_E_UNSUPPORTED;
-  const size_t need = attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size);
+  const size_t need =
+      attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size);
   if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_E_INVALID;
 
@@ -175,13 +211,26 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   a.B = B;
   a.H = H;
+  a.H_kv = H_kv;
+  a.group = group;
+  a.qchunks = qchunks;
   a.max_pages = max_pages_per_seq;
   a.n_splits = p.n_splits;
   a.tokens_per_split = p.tokens_per_split;
   a.num_pages = num_pages;
   a.c = exp2_multiplier(scale);
-  hipError_t e = launch_paged_decode(D, bf16, out_f32, a, stream);
+  hipError_t e = group == 1 ? launch_paged_decode(D, bf16, out_f32, a, stream)
+                            : launch_paged_decode_gqa(D, bf16, out_f32, a, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, void* o, int B, int H,
+                      int D, int page_size, int num_pages, int max_pages_per_seq, int dtype,
+                      float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H, D,
+                               page_size, num_pages, max_pages_per_seq, dtype, scale, workspace,
+                               workspace_bytes, stream);
 }
 
 }  // extern "C"

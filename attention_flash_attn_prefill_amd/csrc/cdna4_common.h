@@ -1,0 +1,87 @@
+// Device helpers shared by the MFMA kernels (prefill.hip, decode_gqa.hip):
+// vector types, the gfx950 32x32x16 MFMAs, lane-pair reductions, rounding
+// conversions, the LDS chunk swizzle and vmcnt waits.  Internal; included
+// inside namespace mi355_attn's anonymous namespace of each kernel file.
+#pragma once
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kBufferConfig = 0x00020000;  // raw buffer, 32-bit data format
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Max / sum of a value with the same value in lane ^ 32.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two fp32 -> packed fp16x2, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return bf16_bits(a) | (bf16_bits(b) << 16);
+}
+
+// Packed bf16x2 -> packed fp16x2 (exact inside the fp16 normal range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
+// D = 128 (16 chunks) it swaps the two 2-bit halves of the row's low nibble:
+// 16 consecutive rows read at one logical chunk (the K operand reads) land on
+// 16 distinct chunk positions, and the four consecutive rows named by one
+// transposing read land on distinct chunk quartets, so neither read pattern
+// has bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return row & 7;
+}
+
+// s_waitcnt that waits until at most N vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}

@@ -278,11 +278,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 }
 
 template <int D, bool BF16>
-hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((a.H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG, a.n_splits, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, BF16>), grid, dim3(64 * kDecodeHeadsPerWG), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_combine_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
   if (out_f32)
     hipLaunchKernelGGL((decode_combine_kernel<D, BF16, true>), dim3(a.B * a.H), dim3(64), 0, s, a);
   else
@@ -291,7 +287,25 @@ hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((a.H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG, a.n_splits, a.B);
+  hipLaunchKernelGGL((decode_split_kernel<D, BF16>), grid, dim3(64 * kDecodeHeadsPerWG), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine_t<D, BF16>(out_f32, a, s);
+}
+
 }  // namespace
+
+hipError_t launch_decode_combine(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                                 hipStream_t s) {
+  if (D == 128) return bf16 ? launch_combine_t<128, true>(out_f32, a, s)
+                            : launch_combine_t<128, false>(out_f32, a, s);
+  if (D == 64) return bf16 ? launch_combine_t<64, true>(out_f32, a, s)
+                           : launch_combine_t<64, false>(out_f32, a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                hipStream_t s) {

@@ -1,0 +1,304 @@
+// Grouped-query paged flash decoding for gfx950: the query heads that share a
+// KV head (grouped-query / multi-query attention, H_kv < H) are decoded
+// together, so each K/V row is read from HBM once for the whole group and the
+// group's queries become the N dimension of the matrix-core products.  The
+// flash-decoding structure is the MHA kernel's (split the KV range, one
+// partial output and log-sum-exp per split, merge by log-sum-exp: "Wave
+// February 2025 Release", FlashDecoding list; splits sized to fill the GPU:
+// "[FlyDSL] FP8 MQA logits improvements for gfx950", Changes / Host side).
+//
+// One wave per (sequence, KV head, split, 32-query chunk of the group):
+//   * Tiles of 32 tokens (two 16-token pages).  K and V rows of a tile are
+//     gathered through the page table straight into the wave's own LDS with
+//     16-byte buffer loads to LDS (two stages: tile t+1 streams in while tile
+//     t computes).  Each page gets its own buffer resource whose range ends
+//     at the split's last live token, so slots past it read as zero and a
+//     page past the end is never touched.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (K rows are the M dimension, the
+//     group's queries the N dimension, zero-padded to 32), the online softmax
+//     per query column in fp32 (base 2, lazy rescale), P rounded to fp16 and
+//     O^T += V^T P^T on fp16 MFMA with V read by transposing LDS reads -- the
+//     operand layouts and swizzle of the prefill kernel.
+//   * Page ids are checked before any load through them: an id outside
+//     [0, num_pages) poisons the split's partial result with NaN.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace mi355_attn {
+namespace {
+
+#include "cdna4_common.h"
+
+constexpr int PS = kDecodePageSize;  // tokens per page
+constexpr int T = 2 * PS;            // tokens per tile
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int CPR = D / 8;           // 16-byte chunks per token row
+  constexpr int LOADS = T * CPR / 64;  // 16-byte loads per lane per K (or V) tile
+  static_assert(LOADS * 64 == T * CPR && LOADS % 2 == 0, "tile must split over the wave");
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[T * D];
+
+  const int lane = threadIdx.x;
+  const int li = lane & 31, hi = lane >> 5;
+  const int item = blockIdx.x;  // ((b * H_kv) + kv_head) * qchunks + qchunk
+  const int split = blockIdx.y;
+  const int qc = item % a.qchunks;
+  const int bk = item / a.qchunks;
+  const int hk = bk % a.H_kv, b = bk / a.H_kv;
+
+  // Clamp to the page table's capacity so a bad length cannot index past it.
+  const int n = max(0, min(a.seq_lens[b], a.max_pages * PS));
+  const int t_begin = split * a.tokens_per_split;
+  if (t_begin >= n) return;  // empty split: no loads, no writes
+  const int t_end = min(n, t_begin + a.tokens_per_split);
+  const int n_tiles = (t_end - t_begin + T - 1) / T;
+
+  // Q^T fragments (B operand): lane holds query head qc*32 + li of the group,
+  // dims 16s + 8hi .. +7; columns past the group are zero.
+  const int qn = qc * 32 + li;
+  const bool q_ok = qn < a.group;
+  const int h = hk * a.group + qn;
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.H + h) * D + 16 * s + 8 * hi)
+                 : (u32x4){0u, 0u, 0u, 0u};
+
+  // ---- gather addresses.  Load i of a lane fills LDS chunk P = 64 i + lane of
+  // the tile: row r = P / CPR (token r of the tile: page r / 16, slot r % 16),
+  // position P % CPR, holding logical chunk position ^ swz(r).
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int64_t page_elems = (int64_t)PS * a.H_kv * D;
+  const uint32_t row_bytes = (uint32_t)a.H_kv * D * 2u;
+  int g_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = 64 * i + lane;
+    const int r = P / CPR, pos = P % CPR;
+    g_off[i] = (((r % PS) * a.H_kv + hk) * D + ((pos ^ swz<D>(r)) * 8)) * 2;
+  }
+  // A page's buffer covers its first `live` slots; live = 0 covers nothing.
+  auto page_rsrc = [&](const uint16_t* cache, int pg, int live) {
+    const uint16_t* base = live > 0 ? cache + (int64_t)pg * page_elems : cache;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(live * row_bytes),
+                                             kBufferConfig);
+  };
+
+  u32x4 vreg[LOADS];  // bf16 V staged in registers for the fp16 conversion
+  bool bad_page = false;  // wave-uniform
+  // Issue the loads of the tile starting at token tb into one stage; false
+  // (and nothing issued) if a page id lies outside the pool.
+  auto issue = [&](int tb, LDS_AS uint16_t* kd, LDS_AS uint16_t* vd) {
+    const int live0 = min(PS, t_end - tb);
+    const int live1 = max(0, min(PS, t_end - tb - PS));
+    const int pg0 = ptab[tb / PS];
+    const int pg1 = live1 > 0 ? ptab[tb / PS + 1] : pg0;
+    if ((uint32_t)pg0 >= (uint32_t)a.num_pages || (uint32_t)pg1 >= (uint32_t)a.num_pages)
+      return false;
+    const auto k0 = page_rsrc(a.k_cache, pg0, live0), k1 = page_rsrc(a.k_cache, pg1, live1);
+    const auto v0 = page_rsrc(a.v_cache, pg0, live0), v1 = page_rsrc(a.v_cache, pg1, live1);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < LOADS / 2 ? k0 : k1,
+                                               (LDS_AS void*)(kd + i * 512), 16, g_off[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if constexpr (BF16)
+        vreg[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < LOADS / 2 ? v0 : v1, g_off[i], 0, 0));
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < LOADS / 2 ? v0 : v1,
+                                                 (LDS_AS void*)(vd + i * 512), 16, g_off[i], 0, 0, 0);
+    }
+    return true;
+  };
+  // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
+  auto store_v = [&](LDS_AS uint16_t* vd) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(vreg[i][j]);
+        *reinterpret_cast<LDS_AS u32x4*>(vd + i * 512 + lane * 8) = w;
+      }
+    }
+  };
+
+  // ---- LDS read offsets (halves): K rows li (A operand), V by transposing
+  // reads (lane (g16, r, c) names 4 halves of key 8half + 4hi + r at
+  // d = 32db + 16(g16 & 1) + 4c), exactly as in the prefill kernel.
+  int k_rd[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
+  const int g16 = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
+  int v_rd[2][D / 32];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int key = 8 * half + 4 * hi + tr_r;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = 4 * db + 2 * (g16 & 1) + (tr_c >> 1);
+      v_rd[half][db] = key * D + ((chunk ^ swz<D>(key)) * 8) + (tr_c & 1) * 4;
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  float m_run = kNegInf;  // reference max (log2 units) of this lane's query column
+  float l_run = 0.f;      // this lane's share of the row sum
+
+  auto compute = [&](int tb, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) {
+    // S^T = K Q^T (32 tokens x 32 queries).
+    u32x4 kf[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const LDS_AS u32x4*>(ks + k_rd[s]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sc = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) sc = mfma_qk<BF16>(kf[s], qf[s], sc);
+    // Tokens past the split's end.
+    if (tb + T > t_end) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (tb + 8 * (r >> 2) + 4 * hi + (r & 3) >= t_end) sc[r] = kNegInf;
+    }
+    // Row max and lazy rescale (the reference max moves only when some
+    // column's max grew by more than 8 in log2 units).
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = pair_max(mx) * a.c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float base = (m_run == kNegInf) ? 0.f : m_run;
+    // P^T = exp2(S^T c - base) in fp16, and the row sum of those values.
+    u32x4 pf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * s + j], a.c, -base));
+      f16x2 hp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hp[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
+      pf[s] = (u32x4){__builtin_bit_cast(uint32_t, hp[0]), __builtin_bit_cast(uint32_t, hp[1]),
+                      __builtin_bit_cast(uint32_t, hp[2]), __builtin_bit_cast(uint32_t, hp[3])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        l_run = __builtin_amdgcn_fdot2(hp[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
+                                       false);
+    }
+    // O^T += V^T P^T.
+    u32x4 vf[2][D / 32];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[0][db]));
+        const fp16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[1][db]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
+        vf[s][db] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_pv(vf[s][db], pf[s], acc[db]);
+  };
+
+  LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
+  LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
+  if (!issue(t_begin, Ks[0], Vs[0])) bad_page = true;
+  else store_v(Vs[0]);
+  // One tile per step; the next tile's loads are in flight during compute.
+  auto step = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;  // t % 2
+    const int tb = t_begin + t * T;
+    if (t + 1 < n_tiles) {
+      if (!issue(tb + T, Ks[P ^ 1], Vs[P ^ 1])) {
+        bad_page = true;
+        return;
+      }
+      wait_vmcnt<2 * LOADS>();  // this tile's loads have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    compute(tb, Ks[P], Vs[P]);
+    if (t + 1 < n_tiles) store_v(Vs[P ^ 1]);
+  };
+  for (int t = 0; t < n_tiles && !bad_page; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles && !bad_page) step(t + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt<0>();  // no load may still target this wave's LDS when it ends
+
+  // ---- partial result of the split: O normalised by its row sum, and the
+  // log-sum-exp in base 2.  Lane (li, hi) holds d = 32db + 8(r/4) + 4hi + r%4.
+  if (!q_ok) return;
+  const int64_t row = ((int64_t)b * a.H + h) * a.n_splits + split;
+  float* po = a.part_o + row * D;
+  if (bad_page) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g + 4 * hi) = (f32x4){nan, nan, nan, nan};
+    if (hi == 0) a.part_lse[row] = nan;
+    return;
+  }
+  const float l_tot = pair_sum(l_run);  // > 0: the split holds a live token
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* v4 = reinterpret_cast<const float*>(&acc[db]) + 4 * g;
+      *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g + 4 * hi) =
+          (f32x4){v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
+    }
+  if (hi == 0) a.part_lse[row] = m_run + __log2f(l_tot);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int D, bool BF16>
+hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.B * a.H_kv * a.qchunks, a.n_splits);
+  hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16>), grid, dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(D, BF16, out_f32, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode_gqa(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                                   hipStream_t s) {
+  if (D == 128) return bf16 ? launch_t<128, true>(out_f32, a, s) : launch_t<128, false>(out_f32, a, s);
+  if (D == 64) return bf16 ? launch_t<64, true>(out_f32, a, s) : launch_t<64, false>(out_f32, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mi355_attn

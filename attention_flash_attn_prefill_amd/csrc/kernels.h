@@ -12,12 +12,13 @@ struct PrefillArgs {
   const uint16_t* k;
   const uint16_t* v;
   void* o;             // fp16/bf16 like q, or fp32 (out_f32)
-  int H, Sq, Skv;
+  int H, Sq, Skv;       // H query heads
+  int H_kv, group;     // KV heads and query heads per KV head (H = H_kv * group)
   int n_mtiles;        // ceil(Sq / BM), set by launch_prefill
   int total_tiles;     // B * H * n_mtiles  (= grid size), set by launch_prefill
   int64_t q_sb, q_sh;  // element strides of q and o between batches / heads
   int q_ss;            // element stride between query rows
-  int64_t k_sb, k_sh;  // element strides of k and v
+  int64_t k_sb, k_sh;  // element strides of k and v (per batch, per KV head)
   int k_ss;
   float c;             // scale * log2(e)
   int causal_off;      // Skv - Sq (bottom-right causal alignment)
@@ -26,13 +27,16 @@ struct PrefillArgs {
 hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
                           int B, hipStream_t s);
 
-// Paged decode: one wave per (sequence, head, split); four heads per workgroup.
+// Paged decode.  H query heads share H_kv KV heads (group = H / H_kv).
+// group = 1: decode.hip, one wave per (sequence, head, split), four heads per
+// workgroup.  group > 1: decode_gqa.hip, one wave per (sequence, KV head,
+// split, chunk of up to 32 query heads of the group).
 constexpr int kDecodeHeadsPerWG = 4;
 constexpr int kDecodePageSize = 16;
 
 struct DecodeArgs {
   const uint16_t* q;          // [B, H, D]
-  const uint16_t* k_cache;    // [num_pages, 16, H, D]
+  const uint16_t* k_cache;    // [num_pages, 16, H_kv, D]
   const uint16_t* v_cache;
   const int32_t* page_table;  // [B, max_pages]
   const int32_t* seq_lens;    // [B]
@@ -40,11 +44,17 @@ struct DecodeArgs {
   float* part_o;              // [B, H, n_splits, D]   (workspace)
   float* part_lse;            // [B, H, n_splits]      (workspace; log2 domain)
   int B, H, max_pages, n_splits, tokens_per_split;
+  int H_kv, group, qchunks;   // qchunks = ceil(group / 32)
   int num_pages;              // page ids outside [0, num_pages) are rejected on the device
   float c;                    // scale * log2(e)
 };
 
 hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                hipStream_t s);
+hipError_t launch_paged_decode_gqa(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                                   hipStream_t s);
+// The log-sum-exp merge of the per-split partials (one wave per (b, h)).
+hipError_t launch_decode_combine(int D, bool bf16, bool out_f32, const DecodeArgs& a,
+                                 hipStream_t s);
 
 }  // namespace mi355_attn

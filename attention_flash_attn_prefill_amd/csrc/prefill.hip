@@ -66,70 +66,7 @@
 namespace mi355_attn {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kLazyRescale = 8.0f;  // log2 units
-constexpr int kBufferConfig = 0x00020000;  // raw buffer, 32-bit data format
-
-
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Max / sum of a value with the same value in lane ^ 32.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two fp32 -> packed fp16x2, round to nearest even.
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return bf16_bits(a) | (bf16_bits(b) << 16);
-}
-
-// Packed bf16x2 -> packed fp16x2 (exact inside the fp16 normal range).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
+#include "cdna4_common.h"
 
 // Workgroup -> work item.  The dispatcher sends workgroup w to XCD w % 8; give
 // each XCD a contiguous range of work items so one head's query tiles share
@@ -138,25 +75,6 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int q = total >> 3, r = total & 7;
   const int x = w & 7, k = w >> 3;
   return x * q + min(x, r) + k;
-}
-
-// XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
-// D = 128 (16 chunks) it swaps the two 2-bit halves of the row's low nibble:
-// 16 consecutive rows read at one logical chunk (the K operand reads) land on
-// 16 distinct chunk positions, and the four consecutive rows named by one
-// transposing read land on distinct chunk quartets, so neither read pattern
-// has bank conflicts.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return row & 7;
-}
-
-// s_waitcnt that waits until at most N vector-memory operations are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
@@ -184,16 +102,23 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 31, hi = lane >> 5;
 
-  const int L = xcd_remap(blockIdx.x, a.total_tiles);
-  const int bh = L / a.n_mtiles;
-  int mt = L - bh * a.n_mtiles;
+  // Work item L = ((b * H_kv + kv_head) * n_mtiles + mt) * group + g: the
+  // query heads that share a KV head are adjacent, so they run the same query
+  // tile at the same time on one XCD and read the same K/V tiles through its
+  // L2 (group = 1 is plain (b, h, mt) order).
+  int L = xcd_remap(blockIdx.x, a.total_tiles);
+  const int g = L % a.group;
+  L /= a.group;
+  int mt = L % a.n_mtiles;
+  L /= a.n_mtiles;
   if (CAUSAL) mt = a.n_mtiles - 1 - mt;  // heaviest query tiles first
-  const int b = bh / a.H, h = bh - b * a.H;
+  const int hk = L % a.H_kv, b = L / a.H_kv;
+  const int h = hk * a.group + g;
 
   const uint16_t* __restrict__ qp = a.q + b * a.q_sb + h * a.q_sh;
   const int64_t o_base = b * a.q_sb + h * a.q_sh;  // o shares q's element strides
-  const uint16_t* __restrict__ kp = a.k + b * a.k_sb + h * a.k_sh;
-  const uint16_t* __restrict__ vp = a.v + b * a.k_sb + h * a.k_sh;
+  const uint16_t* __restrict__ kp = a.k + b * a.k_sb + hk * a.k_sh;
+  const uint16_t* __restrict__ vp = a.v + b * a.k_sb + hk * a.k_sh;
 
   const int m0 = mt * BM;
   const int q0 = m0 + wave * 32;

@@ -93,6 +93,19 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  int causal, float scale, hipStream_t stream);
 
 /*
+ * Grouped-query (and multi-query) prefill: as attn_prefill, with k and v
+ * holding H_kv heads ([B, H_kv, Skv, D] or [B, Skv, H_kv, D]) shared by the H
+ * query heads: query head h reads KV head h / (H / H_kv).  H_kv must divide H
+ * (else ATTN_E_INVALID); H_kv = H is attn_prefill, H_kv = 1 multi-query
+ * attention.  The pages do not define grouped heads; this is the mapping
+ * that consecutive query heads share a KV head.  attn_prefill(...) is
+ * attn_prefill_gqa(..., H, H, ...).
+ */
+int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
+                     int causal, float scale, hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_paged_decode needs for these sizes: the
  * per-split partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
  */
@@ -132,6 +145,33 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                       int B, int H, int D, int page_size, int num_pages,
                       int max_pages_per_seq, int dtype, float scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Grouped-query (and multi-query) paged decode: as attn_paged_decode, with a
+ * cache of H_kv heads ([num_pages, page_size, H_kv, D]) shared by the H query
+ * heads of q: query head h reads KV head h / (H / H_kv).  H_kv must divide H
+ * (else ATTN_E_INVALID).  With H_kv < H the query heads of a group are
+ * decoded together, so each cache row is read from memory once per group;
+ * with H_kv = H this is attn_paged_decode.  The workspace comes from
+ * attn_paged_decode_gqa_workspace_size; page ids and lengths are treated as
+ * in attn_paged_decode (a bad page id makes O[b] NaN for every head).
+ * Arithmetic for H_kv < H: Q.K^T on MFMA in the input dtype with fp32
+ * accumulation, softmax in fp32, P rounded to fp16 and P.V on fp16 MFMA
+ * (bf16 V converted to fp16 on staging, as in attn_prefill).
+ */
+int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* page_table, const int32_t* seq_lens, void* o,
+                          int B, int H, int H_kv, int D, int page_size, int num_pages,
+                          int max_pages_per_seq, int dtype, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of attn_paged_decode_gqa (0 for invalid sizes). */
+size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D,
+                                            int max_pages_per_seq, int page_size);
+
+/* Split plan of attn_paged_decode_gqa (see attn_paged_decode_num_splits). */
+int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
+                                     int page_size, int* tokens_per_split);
 
 /* Split plan of attn_paged_decode: returns the number of KV splits per
  * sequence (0 on invalid sizes) and, if tokens_per_split is not NULL, stores

@@ -24,7 +24,10 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["attn_status_string", "attn_prefill", "attn_paged_decode",
-                            "attn_paged_decode_workspace_size", "attn_paged_decode_num_splits"])
+                            "attn_paged_decode_workspace_size", "attn_paged_decode_num_splits",
+                            "attn_prefill_gqa", "attn_paged_decode_gqa",
+                            "attn_paged_decode_gqa_workspace_size",
+                            "attn_paged_decode_gqa_num_splits"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -88,6 +91,67 @@ def test_prefill_validation(kw, status):
                                 dict(Sq=0, q=None, o=None)])
 def test_prefill_empty_is_a_noop(kw):
     assert _prefill(**kw) == attn.ATTN_OK
+
+
+def _prefill_gqa(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=8, H_kv=2, Sq=16, Skv=16, D=128, layout=0,
+             dtype=0, causal=0, scale=0.1, stream=0)
+    a.update(kw)
+    return attn.attn_prefill_gqa(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=3), attn.ATTN_E_INVALID),       # 3 does not divide 8
+    (dict(H_kv=0), attn.ATTN_E_INVALID),
+    (dict(H_kv=-1), attn.ATTN_E_INVALID),
+    (dict(H_kv=16), attn.ATTN_E_INVALID),      # more KV heads than query heads
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(k=None), attn.ATTN_E_INVALID),
+    (dict(layout=1, H=1 << 16, H_kv=1 << 16, Sq=4096, Skv=4096), attn.ATTN_E_UNSUPPORTED),
+])
+def test_prefill_gqa_validation(kw, status):
+    assert _prefill_gqa(**kw) == status
+
+
+def test_prefill_gqa_empty_is_a_noop():
+    assert _prefill_gqa(H=0, H_kv=0, q=None, k=None, v=None, o=None) == attn.ATTN_OK
+    assert _prefill_gqa(Sq=0) == attn.ATTN_OK
+
+
+def _decode_gqa(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, seq_lens=FAKE, o=FAKE, B=4,
+             H=32, H_kv=8, D=128, page_size=16, num_pages=64, max_pages_per_seq=8, dtype=0,
+             scale=0.1, workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return attn.attn_paged_decode_gqa(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=5), attn.ATTN_E_INVALID),
+    (dict(H_kv=0), attn.ATTN_E_INVALID),
+    (dict(H_kv=64), attn.ATTN_E_INVALID),
+    (dict(page_size=32), attn.ATTN_E_UNSUPPORTED),
+    (dict(workspace_bytes=64), attn.ATTN_E_WORKSPACE),
+    (dict(dtype=attn.ATTN_OUT_F32 | 5), attn.ATTN_E_INVALID),
+])
+def test_decode_gqa_validation(kw, status):
+    assert _decode_gqa(**kw) == status
+
+
+def test_gqa_split_plan_and_workspace():
+    # H_kv = H is the multi-head plan
+    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 32, 512, 16) == \
+        attn.attn_paged_decode_num_splits(64, 32, 512, 16)
+    assert attn.attn_paged_decode_gqa_workspace_size(64, 32, 32, 128, 512, 16) == \
+        attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
+    n, tps = attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16)
+    assert tps % 64 == 0 and tps >= 64 and n == math.ceil(512 * 16 / tps)
+    # one wave per (sequence, KV head, split): at least 8192 of them, or 64-token splits
+    assert 64 * 8 * n >= 8192 or tps == 64
+    ws = attn.attn_paged_decode_gqa_workspace_size(64, 32, 8, 128, 512, 16)
+    assert ws >= 64 * 32 * n * 129 * 4            # partials per query head
+    assert attn.attn_paged_decode_gqa_num_splits(4, 6, 4, 8, 16) == (0, 0)
+    assert attn.attn_paged_decode_gqa_workspace_size(4, 8, 2, 96, 8, 16) == 0
 
 
 def _decode(**kw):

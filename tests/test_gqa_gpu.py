@@ -1,0 +1,149 @@
+"""GPU parity of grouped-query / multi-query attention (H_kv < H) through the
+C ABI against the fp64 oracle, for prefill (attn_prefill_gqa) and paged
+decode (attn_paged_decode_gqa).  Same bar as the multi-head tests: max-abs
+<= 1e-2 and relative Frobenius <= 2e-3; with an fp32 output, 3e-3 and 5e-4.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _f64(t):
+    return t.double().cpu().numpy()
+
+
+# ------------------------------------------------------------------ prefill
+
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (12, 3), (8, 1), (64, 8)])
+@pytest.mark.parametrize("dtype,layout,causal", [("f16", "BHSD", False), ("bf16", "BSHD", True),
+                                                 ("bf16", "BHSD", True), ("f16", "BSHD", False)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_gqa(gpu_lib, H, H_kv, dtype, layout, causal, D):
+    Sq, Skv = (150, 333) if H <= 12 else (70, 90)
+    q, k, v = workloads.prefill_inputs(2, H, Sq, Skv, D, dtype, layout, seed=H + H_kv + D,
+                                       h_kv=H_kv)
+    print(f"[case] prefill_gqa H{H}/{H_kv} D{D} {dtype} {layout} causal={causal}", flush=True)
+    o = gpu_lib.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, causal=causal, layout=layout)
+    assert_parity(_f64(o), ref, f"prefill gqa H{H}/{H_kv} D{D} {dtype} {layout} causal={causal}")
+
+
+def test_prefill_gqa_equals_repeated_kv_bitwise(gpu_lib):
+    """Grouped K/V give bitwise the result of the same K/V repeated per query head."""
+    q, k, v = workloads.prefill_inputs(2, 8, 300, 300, 128, "bf16", "BHSD", seed=71, h_kv=2)
+    print("[case] prefill_gqa vs repeated kv", flush=True)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o_g = gpu_lib.prefill(qg, kg, vg, causal=True)
+    o_r = gpu_lib.prefill(qg, kg.repeat_interleave(4, dim=1).contiguous(),
+                          vg.repeat_interleave(4, dim=1).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+
+
+def test_prefill_gqa_full_config6_sampled(gpu_lib):
+    q, k, v, m = workloads.prefill_config(6)
+    print(f"[case] prefill config 6 {m['name']}", flush=True)
+    o = gpu_lib.prefill(q.cuda(), k.cuda(), v.cuda(), causal=m["causal"], scale=m["scale"],
+                        layout=m["layout"]).cpu()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = [(b, h, i) for b in range(m["B"]) for h in (0, 3, 4, 31)
+            for i in (0, 1, 255, 256, m["Sq"] - 1)]
+    rows += [(int(rng.integers(m["B"])), int(rng.integers(m["H"])), int(rng.integers(m["Sq"])))
+             for _ in range(64)]
+    ref = oracle.sdpa_rows(q, k, v, rows, causal=m["causal"], scale=m["scale"], layout=m["layout"])
+    got = np.stack([o[b, i, h].double().numpy() for b, h, i in rows])
+    assert_parity(got, ref, f"config 6 ({len(rows)} sampled rows)")
+
+
+# ------------------------------------------------------------------- decode
+
+EDGE_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 1000, 4096, 8191, 8192]
+
+
+def _decode(attn, batch, **kw):
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k_cache", "v_cache", "page_table",
+                                              "seq_lens")}
+    o = attn.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"], **kw)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _ref(batch):
+    return oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                               batch.seq_lens)
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 4), (8, 2), (32, 8), (32, 1), (64, 1), (40, 5)])
+@pytest.mark.parametrize("D,dtype", [(128, "f16"), (128, "bf16"), (64, "f16"), (64, "bf16")])
+def test_decode_gqa_edge_lengths_nan_poisoned(gpu_lib, H, H_kv, D, dtype):
+    batch = workloads.paged_decode_inputs(B=len(EDGE_LENS), H=H, D=D, dtype=dtype, page_size=16,
+                                          num_pages=2048, max_seq=8192, seed=H + H_kv + D,
+                                          seq_lens=EDGE_LENS, fill=float("nan"), h_kv=H_kv)
+    print(f"[case] decode_gqa H{H}/{H_kv} D{D} {dtype} edge lengths", flush=True)
+    o = _decode(gpu_lib, batch)
+    assert torch.isfinite(o.float()).all(), "NaN from an unused cache slot leaked into O"
+    assert_parity(_f64(o), _ref(batch), f"decode gqa H{H}/{H_kv} D{D} {dtype}")
+
+
+def test_decode_gqa_out_f32_and_rounding(gpu_lib):
+    batch = workloads.paged_decode_inputs(B=len(EDGE_LENS), H=16, D=128, dtype="bf16",
+                                          page_size=16, num_pages=2048, max_seq=8192, seed=72,
+                                          seq_lens=EDGE_LENS, h_kv=4)
+    print("[case] decode_gqa out_f32", flush=True)
+    o32 = _decode(gpu_lib, batch, out_dtype=torch.float32)
+    o16 = _decode(gpu_lib, batch)
+    assert_parity(_f64(o32), _ref(batch), "decode gqa out_f32", max_abs_tol=3e-3,
+                  rel_fro_tol=5e-4)
+    assert torch.equal(o32.to(o16.dtype), o16)
+
+
+def test_decode_gqa_pool_permutation_bitwise(gpu_lib):
+    batch = workloads.paged_decode_inputs(B=16, H=16, D=128, page_size=16, num_pages=4096,
+                                          max_seq=4000, seed=73, h_kv=2)
+    moved = workloads.permute_pool(batch, seed=9)
+    print("[case] decode_gqa pool permutation", flush=True)
+    assert torch.equal(_decode(gpu_lib, batch), _decode(gpu_lib, moved))
+
+
+def test_decode_gqa_bad_page_ids(gpu_lib):
+    lens = [40, 100, 33, 200]
+    batch = workloads.paged_decode_inputs(B=4, H=8, D=128, page_size=16, num_pages=300,
+                                          seq_lens=lens, max_pages_per_seq=16, seed=74, h_kv=2)
+    P = batch.num_pages
+    table = batch.page_table.clone()
+    table[1, 3] = P          # a middle page of sequence 1
+    table[3, 0] = -1         # first page of sequence 3
+    table[2, 6] = P + 99     # past sequence 2's live pages: never read
+    print("[case] decode_gqa bad page ids", flush=True)
+    pad = (P + 2,) + tuple(batch.k_cache.shape[1:])
+    k_pad = torch.zeros(pad, dtype=batch.k_cache.dtype, device="cuda")
+    v_pad = torch.zeros(pad, dtype=batch.v_cache.dtype, device="cuda")
+    k_pad[1:P + 1].copy_(batch.k_cache)
+    v_pad[1:P + 1].copy_(batch.v_cache)
+    o = gpu_lib.paged_decode(batch.q.cuda(), k_pad[1:P + 1], v_pad[1:P + 1], table.cuda(),
+                             batch.seq_lens.cuda()).float().cpu()
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[3]).all()
+    assert_parity(_f64(o[[0, 2]]), _ref(batch)[[0, 2]], "gqa sequences with valid pages")
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_decode_gqa_full_config(gpu_lib, cfg):
+    batch = workloads.decode_config(cfg)
+    print(f"[case] decode config {cfg} {batch.meta['name']}", flush=True)
+    o = _decode(gpu_lib, batch, scale=batch.meta["scale"])
+    B = batch.q.shape[0]
+    sel = list(range(0, B, max(1, B // 32)))  # every sequence's heads for a spread of sequences
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, scale=batch.meta["scale"], batch_indices=sel)
+    assert_parity(_f64(o[sel]), ref, f"config {cfg} ({len(sel)} sequences, all heads)")
