@@ -63,7 +63,11 @@ SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
   const int64_t max_tokens = (int64_t)max_pages * page_size;
   int tps = 512;
   auto splits = [&](int t) { return (max_tokens + t - 1) / t; };
-  while (tps > 4 * kDecodePageSize && items * splits(tps) < 8192) tps /= 2;
+  // Grouped heads write one partial row per query head and split: keep the
+  // split at least 16 tokens per query head of the group (partials <= ~6%).
+  int floor_tps = 4 * kDecodePageSize;
+  while (group > 1 && floor_tps < 512 && floor_tps < 16 * group) floor_tps *= 2;
+  while (tps > floor_tps && items * splits(tps) < 8192) tps /= 2;
   while (splits(tps) > 4096) tps *= 2;
   p.tokens_per_split = tps;
   p.n_splits = (int)splits(tps);

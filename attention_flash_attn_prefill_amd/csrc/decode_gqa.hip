@@ -9,11 +9,16 @@
 //
 // One wave per (sequence, KV head, split, 32-query chunk of the group):
 //   * Tiles of 32 tokens (two 16-token pages).  K and V rows of a tile are
-//     gathered through the page table straight into the wave's own LDS with
-//     16-byte buffer loads to LDS (two stages: tile t+1 streams in while tile
-//     t computes).  Each page gets its own buffer resource whose range ends
-//     at the split's last live token, so slots past it read as zero and a
-//     page past the end is never touched.
+//     gathered through the page table into registers with 16-byte
+//     non-temporal buffer loads (16 lanes per 256-byte row); tile t+1's loads
+//     are in flight while tile t computes.  The registers then go to the
+//     wave's own LDS (one stage, 16 KB: room for eight waves per CU), from
+//     which the MFMA operands are read.  The bytes in flight per CU, not the
+//     arithmetic, bound this kernel: staging through registers instead of
+//     LDS-only double buffering lets more waves (and bytes) be resident.
+//   * Each page gets its own buffer resource whose range ends at the split's
+//     last live token, so slots past it read as zero and a page past the end
+//     is never touched.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (K rows are the M dimension, the
 //     group's queries the N dimension, zero-padded to 32), the online softmax
 //     per query column in fp32 (base 2, lazy rescale), P rounded to fp16 and
@@ -42,10 +47,9 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
   constexpr int CPR = D / 8;           // 16-byte chunks per token row
   constexpr int LOADS = T * CPR / 64;  // 16-byte loads per lane per K (or V) tile
   static_assert(LOADS * 64 == T * CPR && LOADS % 2 == 0, "tile must split over the wave");
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[T * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[T * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[T * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[T * D];
+  constexpr int kNonTemporal = 2;      // buffer-load cache policy: streamed, read once
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[T * D];
 
   const int lane = threadIdx.x;
   const int li = lane & 31, hi = lane >> 5;
@@ -73,9 +77,10 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
     qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.H + h) * D + 16 * s + 8 * hi)
                  : (u32x4){0u, 0u, 0u, 0u};
 
-  // ---- gather addresses.  Load i of a lane fills LDS chunk P = 64 i + lane of
-  // the tile: row r = P / CPR (token r of the tile: page r / 16, slot r % 16),
-  // position P % CPR, holding logical chunk position ^ swz(r).
+  // ---- gather addresses.  Load i of a lane fetches tile chunk P = 64 i + lane,
+  // which goes to LDS chunk P: row r = P / CPR (token r of the tile: page
+  // r / 16, slot r % 16), position P % CPR, holding logical chunk
+  // position ^ swz(r).
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int64_t page_elems = (int64_t)PS * a.H_kv * D;
   const uint32_t row_bytes = (uint32_t)a.H_kv * D * 2u;
@@ -93,11 +98,11 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
                                              kBufferConfig);
   };
 
-  u32x4 vreg[LOADS];  // bf16 V staged in registers for the fp16 conversion
+  u32x4 vreg[LOADS], kreg[LOADS];  // the next tile, in flight
   bool bad_page = false;  // wave-uniform
-  // Issue the loads of the tile starting at token tb into one stage; false
-  // (and nothing issued) if a page id lies outside the pool.
-  auto issue = [&](int tb, LDS_AS uint16_t* kd, LDS_AS uint16_t* vd) {
+  // Issue the loads of the tile starting at token tb; false (and nothing
+  // issued) if a page id lies outside the pool.
+  auto issue = [&](int tb) {
     const int live0 = min(PS, t_end - tb);
     const int live1 = max(0, min(PS, t_end - tb - PS));
     const int pg0 = ptab[tb / PS];
@@ -108,29 +113,25 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
     const auto v0 = page_rsrc(a.v_cache, pg0, live0), v1 = page_rsrc(a.v_cache, pg1, live1);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < LOADS / 2 ? k0 : k1,
-                                               (LDS_AS void*)(kd + i * 512), 16, g_off[i], 0, 0, 0);
+      kreg[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < LOADS / 2 ? k0 : k1, g_off[i], 0, kNonTemporal));
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      if constexpr (BF16)
-        vreg[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < LOADS / 2 ? v0 : v1, g_off[i], 0, 0));
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < LOADS / 2 ? v0 : v1,
-                                                 (LDS_AS void*)(vd + i * 512), 16, g_off[i], 0, 0, 0);
-    }
+    for (int i = 0; i < LOADS; ++i)
+      vreg[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < LOADS / 2 ? v0 : v1, g_off[i], 0, kNonTemporal));
     return true;
   };
-  // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
-  auto store_v = [&](LDS_AS uint16_t* vd) {
-    if constexpr (BF16) {
+  // Write the loaded tile to LDS (bf16 V converted to fp16 on the way).
+  auto store_kv = [&](LDS_AS uint16_t* kd, LDS_AS uint16_t* vd) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        u32x4 w;
+    for (int i = 0; i < LOADS; ++i) {
+      *reinterpret_cast<LDS_AS u32x4*>(kd + i * 512 + lane * 8) = kreg[i];
+      u32x4 w = vreg[i];
+      if constexpr (BF16) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(vreg[i][j]);
-        *reinterpret_cast<LDS_AS u32x4*>(vd + i * 512 + lane * 8) = w;
       }
+      *reinterpret_cast<LDS_AS u32x4*>(vd + i * 512 + lane * 8) = w;
     }
   };
 
@@ -228,31 +229,22 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma_pv(vf[s][db], pf[s], acc[db]);
   };
 
-  LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
-  LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
-  if (!issue(t_begin, Ks[0], Vs[0])) bad_page = true;
-  else store_v(Vs[0]);
-  // One tile per step; the next tile's loads are in flight during compute.
-  auto step = [&](int t, auto par) {
-    constexpr int P = decltype(par)::value;  // t % 2
+  // One tile per step: tile t goes registers -> LDS (the LDS writes follow
+  // the previous tile's LDS reads in the wave's own order), tile t+1's loads
+  // are issued, tile t is computed from LDS.
+  LDS_AS uint16_t* const Ks = (LDS_AS uint16_t*)k_lds;
+  LDS_AS uint16_t* const Vs = (LDS_AS uint16_t*)v_lds;
+  if (!issue(t_begin)) bad_page = true;
+  for (int t = 0; t < n_tiles && !bad_page; ++t) {
     const int tb = t_begin + t * T;
-    if (t + 1 < n_tiles) {
-      if (!issue(tb + T, Ks[P ^ 1], Vs[P ^ 1])) {
-        bad_page = true;
-        return;
-      }
-      wait_vmcnt<2 * LOADS>();  // this tile's loads have landed
-    } else {
-      wait_vmcnt<0>();
+    store_kv(Ks, Vs);
+    if (t + 1 < n_tiles && !issue(tb + T)) {
+      bad_page = true;
+      break;
     }
-    compute(tb, Ks[P], Vs[P]);
-    if (t + 1 < n_tiles) store_v(Vs[P ^ 1]);
-  };
-  for (int t = 0; t < n_tiles && !bad_page; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles && !bad_page) step(t + 1, std::integral_constant<int, 1>{});
+    compute(tb, Ks, Vs);
   }
-  wait_vmcnt<0>();  // no load may still target this wave's LDS when it ends
+  wait_vmcnt<0>();  // no load is outstanding when the wave ends
 
   // ---- partial result of the split: O normalised by its row sum, and the
   // log-sum-exp in base 2.  Lane (li, hi) holds d = 32db + 8(r/4) + 4hi + r%4.

@@ -1,16 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
 attn_prefill launch) over the Llama-2-13B-shaped workload B=4 H=40
 Sq=Skv=4096 D=128 fp16 BHSD non-causal, with inputs resident in HBM.  The
 headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
-step).  The other workloads (causal BSHD bf16 8k, paged decode, long causal
-32k) are measured the same way and reported under "extra", decode in GB/s of
-algorithmic K/V bytes.
+step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
+decode, long causal 32k, grouped-query causal 8k, grouped-query and
+multi-query paged decode) are measured the same way and reported under
+"extra", decode in GB/s of algorithmic K/V bytes.
 
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
 run on, bracketed by torch.cuda.synchronize(); HIP events around every step
@@ -228,7 +229,8 @@ def bench_prefill(attn, cfg, steps, warmup, clock):
         stream.wait_stream(side)
     flops = prefill_flops(m)
     tflops = flops / (t["mean_ms"] * 1e-3) / 1e12
-    cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "Sq": m["Sq"], "Skv": m["Skv"],
+    cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "H_kv": m["H_kv"],
+               "Sq": m["Sq"], "Skv": m["Skv"],
                "D": m["D"], "layout": m["layout"], "causal": m["causal"], "dtype": m["dtype"]}
     traffic = load_traffic(f"prefill_fwd__{m['name']}", PREFILL_SRC)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
@@ -246,8 +248,9 @@ def bench_decode(attn, cfg, steps, warmup, clock):
     g = {k: getattr(batch, k).cuda() for k in ("q", "k_cache", "v_cache", "page_table",
                                                "seq_lens")}
     B, H, D = batch.q.shape
-    need = attn.attn_paged_decode_workspace_size(B, H, D, batch.max_pages_per_seq,
-                                                 batch.page_size)
+    H_kv = batch.k_cache.shape[2]
+    need = attn.attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, batch.max_pages_per_seq,
+                                                     batch.page_size)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     o = torch.empty_like(g["q"])
     stream = torch.cuda.current_stream()
@@ -259,11 +262,12 @@ def bench_decode(attn, cfg, steps, warmup, clock):
 
     t = measure(step, steps, warmup, stream, clock)
     n_tok = int(batch.seq_lens.sum())
-    nbytes = n_tok * H * D * 2 * 2  # K and V rows of the live tokens
+    nbytes = n_tok * H_kv * D * 2 * 2  # K and V rows of the live tokens
     gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
-    n_splits, tps = attn.attn_paged_decode_num_splits(B, H, batch.max_pages_per_seq,
-                                                      batch.page_size)
-    cfg_out = {"workload": batch.meta["name"], "B": B, "H": H, "D": D, "dtype": "f16",
+    n_splits, tps = attn.attn_paged_decode_gqa_num_splits(B, H, H_kv, batch.max_pages_per_seq,
+                                                          batch.page_size)
+    cfg_out = {"workload": batch.meta["name"], "B": B, "H": H, "H_kv": H_kv, "D": D,
+               "dtype": batch.meta["dtype"],
                "page_size": batch.page_size, "num_pages": batch.num_pages,
                "live_tokens": n_tok, "n_splits": n_splits, "tokens_per_split": tps}
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
@@ -365,7 +369,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
@@ -386,6 +390,7 @@ def main():
 
     import torch
     import attention_flash_attn_prefill_amd as attn
+    import workloads
     attn.load_library()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -396,7 +401,7 @@ def main():
         copy_calibration(args.copy_calibration_mib)
 
     cfgs = [int(c) for c in args.configs.split(",") if c.strip()]
-    head_cfg = next((c for c in cfgs if c != 4), 2)
+    head_cfg = next((c for c in cfgs if c in workloads.PREFILL_CONFIGS), 2)
     if head_cfg not in cfgs:
         cfgs.insert(0, head_cfg)
 
@@ -406,7 +411,7 @@ def main():
     results = {}
     for c in cfgs:
         print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
-        if c == 4:
+        if c in workloads.DECODE_CONFIGS:
             results[c] = bench_decode(attn, c, args.steps, args.warmup, clock)
         else:
             results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock)

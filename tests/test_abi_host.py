@@ -150,6 +150,10 @@ def test_gqa_split_plan_and_workspace():
     assert 64 * 8 * n >= 8192 or tps == 64
     ws = attn.attn_paged_decode_gqa_workspace_size(64, 32, 8, 128, 512, 16)
     assert ws >= 64 * 32 * n * 129 * 4            # partials per query head
+    # 32 query heads per KV head: splits of at least 16 tokens per query head
+    # (512), so the per-head partial rows stay a few percent of the K/V bytes
+    assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (16, 512)
+    assert attn.attn_paged_decode_gqa_num_splits(1, 8, 1, 512, 16)[1] == 128
     assert attn.attn_paged_decode_gqa_num_splits(4, 6, 4, 8, 16) == (0, 0)
     assert attn.attn_paged_decode_gqa_workspace_size(4, 8, 2, 96, 8, 16) == 0
 
