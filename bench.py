@@ -39,6 +39,7 @@ PEAK_MFMA_F16 = 2516.6   # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 PREFILL_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode.hip")
+DECODE_GQA_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode_gqa.hip")
 
 
 def prefill_flops(m):
@@ -272,7 +273,8 @@ def bench_decode(attn, cfg, steps, warmup, clock):
                "live_tokens": n_tok, "n_splits": n_splits, "tokens_per_split": tps}
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM, 4),
-            "traffic": load_traffic(f"decode_split__{batch.meta['name']}", DECODE_SRC)}
+            "traffic": load_traffic(f"decode_split__{batch.meta['name']}", DECODE_SRC) if H_kv == H
+            else load_traffic(f"decode_gqa_split__{batch.meta['name']}", DECODE_GQA_SRC)}
     del g, ws, o
     torch.cuda.empty_cache()
     return dict(config=cfg_out, timing=t, bytes_per_step=nbytes, gbs=gbs, roofline=roof)
