@@ -18,7 +18,9 @@ in float64 from the exact upcast of the fp16/bf16 inputs.  Paged decode is the
 same function at Sq = 1 applied to each sequence's keys and values, gathered
 explicitly through the page table.  With fewer KV heads than query heads
 (grouped-query / multi-query attention, which the pages do not define), query
-head h reads KV head h // (H / H_kv).
+head h reads KV head h // (H / H_kv).  Extend attention (new tokens after a
+cached prefix) is causal attention over the prefix gathered through the page
+table followed by the new tokens, bottom-right aligned.
 
 Pinned by ``tests/test_oracle.py`` (brute force at 50 digits, the torch
 library routine, closed forms, invariants) and
@@ -27,6 +29,7 @@ library routine, closed forms, invariants) and
 from .attention import (  # noqa: F401
     attend_rows,
     attention_probs,
+    extend,
     gather_sequence,
     kv_head,
     n_visible,

@@ -181,3 +181,37 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: float | No
             out[n_out, h] = attend_rows(qf[h:h + 1], kf[:, g], vf[:, g], scale,
                                         np.array([n]))[0]
     return out
+
+
+def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *,
+           scale: float | None = None, seqs=None) -> np.ndarray:
+    """Extend attention (prefill of new tokens after a cached prefix), float64.
+
+    Sequence b has prefix_lens[b] tokens in the paged cache (read through
+    page_table[b] like paged decode) and E_b = qo_start[b+1] - qo_start[b] new
+    tokens, packed token-major in q [T, H, D] and k, v [T, H_kv, D] at rows
+    qo_start[b] .. qo_start[b+1]-1.  New token i attends to every prefix token
+    and to new tokens 0..i: causal attention over the concatenated sequence
+    (prefix, then new), bottom-right aligned.  Returns o [T, H, D] (rows of
+    sequences not in ``seqs`` stay zero).
+    """
+    T, H, D = q.shape
+    page_size, H_kv = int(k_cache.shape[1]), int(k_cache.shape[2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    as_np = lambda t: np.asarray(t.cpu() if isinstance(t, torch.Tensor) else t)
+    table, plen, starts = as_np(page_table), as_np(prefix_lens), as_np(qo_start)
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for b in (range(len(plen)) if seqs is None else seqs):
+        P, r0, r1 = int(plen[b]), int(starts[b]), int(starts[b + 1])
+        E = r1 - r0
+        keys = np.concatenate([to_f64(gather_sequence(k_cache, table[b], P, page_size)),
+                               to_f64(k[r0:r1])])                       # [P + E, H_kv, D]
+        vals = np.concatenate([to_f64(gather_sequence(v_cache, table[b], P, page_size)),
+                               to_f64(v[r0:r1])])
+        qf = to_f64(q[r0:r1])                                            # [E, H, D]
+        vis = n_visible(E, P + E, causal=True)
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            out[r0:r1, h] = attend_rows(qf[:, h], keys[:, g], vals[:, g], scale, vis)
+    return out

@@ -21,6 +21,8 @@ CASES = [
     dict(B=1, H=1, Sq=6, Skv=6, D=8, dtype="bf16", layout="BSHD", causal=False, seed=1002),
     dict(B=1, H=4, h_kv=2, Sq=4, Skv=6, D=4, dtype="f16", layout="BSHD", causal=True, seed=1004),
 ]
+EXTEND = dict(B=2, H=2, D=4, prefix_lens=[3, 17], extend_lens=[2, 4], dtype="f16", seed=1006,
+              h_kv=1)
 DECODE_GQA = dict(B=2, H=4, h_kv=1, D=4, dtype="bf16", page_size=16, num_pages=8, seed=1005,
                   seq_lens=[3, 18])
 DECODE = dict(B=3, H=2, D=4, dtype="f16", page_size=16, num_pages=8, seed=1003,
@@ -40,6 +42,10 @@ def build():
     b = workloads.paged_decode_inputs(**DECODE_GQA)
     o = oracle.paged_decode(b.q, b.k_cache, b.v_cache, b.page_table, b.seq_lens)
     out["decode_gqa"] = dict(case=DECODE_GQA, out=o.round(15).tolist())
+    e = workloads.extend_inputs(**EXTEND)
+    o = oracle.extend(e.q, e.k, e.v, e.k_cache, e.v_cache, e.page_table, e.prefix_lens,
+                      e.qo_start)
+    out["extend"] = dict(case=EXTEND, out=o.round(15).tolist())
     return out
 
 

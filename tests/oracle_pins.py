@@ -377,11 +377,118 @@ def check_gqa_rows_and_decode():
         _close(got[b], ref, 1e-12, f"gqa decode b{b}")
 
 
+# ----------------------------------------------------------- extend attention
+
+def _extend_library(batch, b, scale=None):
+    """torch's routine for sequence b: prefix K/V read by explicit (page, slot),
+    then the new tokens, with the bottom-right causal mask."""
+    P = int(batch.prefix_lens[b])
+    r0, r1 = int(batch.qo_start[b]), int(batch.qo_start[b + 1])
+    E = r1 - r0
+    tok = torch.arange(P)
+    pages = batch.page_table[b].long()[tok // batch.page_size]
+    kk = torch.cat([batch.k_cache[pages, tok % batch.page_size], batch.k[r0:r1]]).to(F64)
+    vv = torch.cat([batch.v_cache[pages, tok % batch.page_size], batch.v[r0:r1]]).to(F64)
+    qq = batch.q[r0:r1].to(F64)
+    mask = torch.ones(E, P + E, dtype=torch.bool).tril(diagonal=P)
+    out = F.scaled_dot_product_attention(qq.transpose(0, 1)[None], kk.transpose(0, 1)[None],
+                                         vv.transpose(0, 1)[None], attn_mask=mask, scale=scale,
+                                         enable_gqa=True)
+    return out[0].transpose(0, 1).numpy()            # [E, H, D]
+
+
+EXTEND_CASES = [  # (B, H, H_kv, D, prefix_lens, extend_lens)
+    (3, 4, 2, 8, [0, 17, 40], [5, 1, 9]),
+    (2, 3, 3, 16, [16, 3], [16, 20]),
+    (2, 6, 1, 8, [31, 0], [2, 7]),
+]
+
+
+def check_extend_library():
+    for n, (B, H, Hk, D, pl, el) in enumerate(EXTEND_CASES):
+        batch = workloads.extend_inputs(B, H, D, pl, el, "bf16", page_size=16, seed=600 + n,
+                                        h_kv=Hk)
+        got = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                            batch.page_table, batch.prefix_lens, batch.qo_start, scale=0.3)
+        for b in range(B):
+            r0, r1 = int(batch.qo_start[b]), int(batch.qo_start[b + 1])
+            _close(got[r0:r1], _extend_library(batch, b, 0.3), 1e-12, f"extend case {n} b{b}")
+
+
+def check_extend_without_prefix_is_causal_prefill():
+    batch = workloads.extend_inputs(2, 4, 16, [0, 0], [13, 30], "f16", seed=610, h_kv=2)
+    got = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        batch.page_table, batch.prefix_lens, batch.qo_start)
+    for b in range(2):
+        r0, r1 = int(batch.qo_start[b]), int(batch.qo_start[b + 1])
+        ref = oracle.sdpa(batch.q[None, r0:r1], batch.k[None, r0:r1], batch.v[None, r0:r1],
+                          causal=True, layout="BSHD")[0]
+        _close(got[r0:r1], ref, 1e-13, f"extend without prefix b{b}")
+
+
+def check_extend_one_token_is_decode():
+    """One new token: paged decode over the cache with that token appended."""
+    B, H, Hk, D = 3, 4, 2, 8
+    pl = [5, 16, 33]
+    batch = workloads.extend_inputs(B, H, D, pl, [1, 1, 1], "f16", seed=620, h_kv=Hk)
+    got = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        batch.page_table, batch.prefix_lens, batch.qo_start)
+    kc, vc = batch.k_cache.clone(), batch.v_cache.clone()
+    used = set(int(x) for b in range(B) for x in batch.page_table[b, :-(-pl[b] // 16)])
+    free = [p for p in range(kc.shape[0]) if p not in used]
+    table = torch.cat([batch.page_table, torch.zeros(B, 1, dtype=torch.int32)], dim=1)
+    for b in range(B):
+        P = pl[b]
+        if P % 16 == 0:                       # the new token starts a fresh page
+            table[b, P // 16] = free.pop()
+        page = int(table[b, P // 16])
+        kc[page, P % 16] = batch.k[b]
+        vc[page, P % 16] = batch.v[b]
+    ref = oracle.paged_decode(batch.q, kc, vc, table, torch.tensor(pl) + 1)
+    _close(got, ref, 1e-13, "extend of one token vs decode")
+
+
+def check_extend_chunking():
+    """Extending by E1 then E2 tokens (the first chunk written to the cache in
+    between) gives the same outputs as one extend by E1 + E2."""
+    B, H, Hk, D = 2, 2, 1, 8
+    pl, e1, e2 = [7, 32], [9, 16], [6, 3]
+    full = workloads.extend_inputs(B, H, D, pl, [a + b for a, b in zip(e1, e2)], "f16",
+                                   page_size=16, num_pages=64, seed=630, h_kv=Hk)
+    one = oracle.extend(full.q, full.k, full.v, full.k_cache, full.v_cache, full.page_table,
+                        full.prefix_lens, full.qo_start)
+    kc, vc = full.k_cache.clone(), full.v_cache.clone()
+    used = set(int(x) for b in range(B) for x in full.page_table[b, :-(-pl[b] // 16)])
+    free = [p for p in range(kc.shape[0]) if p not in used]
+    table = torch.zeros(B, 8, dtype=torch.int32)
+    table[:, :full.page_table.shape[1]] = full.page_table
+    rows1, rows2 = [], []
+    for b in range(B):
+        r0 = int(full.qo_start[b])
+        for t in range(e1[b]):                # write the first chunk behind the prefix
+            pos = pl[b] + t
+            if pos % 16 == 0 and pos // 16 >= -(-pl[b] // 16):
+                table[b, pos // 16] = free.pop()
+            kc[int(table[b, pos // 16]), pos % 16] = full.k[r0 + t]
+            vc[int(table[b, pos // 16]), pos % 16] = full.v[r0 + t]
+        rows1 += list(range(r0, r0 + e1[b]))
+        rows2 += list(range(r0 + e1[b], r0 + e1[b] + e2[b]))
+    starts1 = torch.tensor([0] + list(np.cumsum(e1)), dtype=torch.int32)
+    part1 = oracle.extend(full.q[rows1], full.k[rows1], full.v[rows1], full.k_cache,
+                          full.v_cache, full.page_table, full.prefix_lens, starts1)
+    starts2 = torch.tensor([0] + list(np.cumsum(e2)), dtype=torch.int32)
+    part2 = oracle.extend(full.q[rows2], full.k[rows2], full.v[rows2], kc, vc, table,
+                          torch.tensor([p + a for p, a in zip(pl, e1)], dtype=torch.int32),
+                          starts2)
+    _close(np.concatenate([part1, part2]), one[rows1 + rows2], 1e-13, "chunked extend")
+
+
 ALL_CHECKS = [
     check_bruteforce, check_library_sdpa, check_rows_match_full, check_ones_v, check_causal_row0,
     check_zero_keys, check_two_keys, check_dominant_key, check_zero_scale,
     check_probs_rows_sum_to_one, check_logit_shift, check_permutations, check_layouts_agree,
     check_decode_library, check_decode_matches_prefill_row, check_decode_pool_permutation,
     check_decode_nan_poison, check_gqa_library, check_gqa_group_locality,
-    check_gqa_rows_and_decode,
+    check_gqa_rows_and_decode, check_extend_library, check_extend_without_prefix_is_causal_prefill,
+    check_extend_one_token_is_decode, check_extend_chunking,
 ]

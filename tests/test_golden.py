@@ -14,7 +14,7 @@ def test_oracle_matches_stored_golden():
         assert s["case"] == f["case"]
         np.testing.assert_allclose(np.array(f["out"]), np.array(s["out"]), rtol=0, atol=1e-14)
     assert len(stored["prefill"]) == len(fresh["prefill"])
-    for key in ("decode", "decode_gqa"):
+    for key in ("decode", "decode_gqa", "extend"):
         assert stored[key]["case"] == fresh[key]["case"]
         np.testing.assert_allclose(np.array(fresh[key]["out"]), np.array(stored[key]["out"]),
                                    rtol=0, atol=1e-14)

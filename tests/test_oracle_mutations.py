@@ -72,6 +72,26 @@ def _kv_head_reversed(h, H, H_kv):
     return H_kv - 1 - h // (H // H_kv)
 
 
+def _extend_without_prefix(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *,
+                           scale=None, seqs=None):
+    return _real_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens * 0, qo_start,
+                        scale=scale, seqs=seqs)
+
+
+def _extend_top_left(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *,
+                     scale=None, seqs=None):
+    """New token i sees only i + 1 keys in all (causal mask not offset by the prefix)."""
+    real = oa.n_visible
+    try:
+        oa.n_visible = lambda Sq, Skv, causal: np.clip(np.arange(Sq) + 1, 0, Skv)
+        return _real_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start,
+                            scale=scale, seqs=seqs)
+    finally:
+        oa.n_visible = real
+
+
+_real_extend = oa.extend
+
 MUTATIONS = [
     ("n_visible", _top_left, [pins.check_library_sdpa, pins.check_bruteforce]),
     ("n_visible", _off_by_one, [pins.check_causal_row0, pins.check_library_sdpa]),
@@ -84,6 +104,10 @@ MUTATIONS = [
                                            pins.check_decode_matches_prefill_row]),
     ("kv_head", _kv_head_strided, [pins.check_gqa_library, pins.check_gqa_group_locality]),
     ("kv_head", _kv_head_reversed, [pins.check_gqa_library, pins.check_gqa_rows_and_decode]),
+    ("extend", _extend_without_prefix, [pins.check_extend_library,
+                                        pins.check_extend_one_token_is_decode]),
+    ("extend", _extend_top_left, [pins.check_extend_library, pins.check_extend_chunking]),
+    ("gather_sequence", _gather_slot_major, [pins.check_extend_library]),
 ]
 
 
@@ -91,6 +115,8 @@ MUTATIONS = [
                          ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
 def test_mutation_is_caught(monkeypatch, name, bad, checks):
     monkeypatch.setattr(oa, name, bad)
+    if hasattr(oracle, name):  # the package re-exports some functions by value
+        monkeypatch.setattr(oracle, name, bad)
     caught = []
     for check in checks:
         try:

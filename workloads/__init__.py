@@ -63,6 +63,14 @@ DECODE_CONFIGS = {
 }
 
 
+# Extend (chunked prefill after a cached prefix): a batch of sequences, each
+# with a cached prefix and a chunk of new tokens.
+EXTEND_CONFIGS = {
+    9: dict(name="extend-gqa-b8", B=8, H=32, H_kv=8, D=128, dtype="bf16", page_size=16,
+            min_prefix=0, max_prefix=8192, min_extend=256, max_extend=2048),
+}
+
+
 def default_scale(D: int) -> float:
     """Softmax scale used when a workload names none: 1/sqrt(head_dim)."""
     return 1.0 / math.sqrt(D)
@@ -196,6 +204,67 @@ def paged_decode_inputs(B, H, D, dtype="f16", page_size=16, num_pages=65536,
                 seed=seed, fill=fill, n_live_tokens=n_live, unused_page=unused_page)
     return PagedBatch(q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
                       seq_lens=lens.to(torch.int32), page_size=page_size, meta=meta)
+
+
+@dataclass
+class ExtendBatch:
+    q: torch.Tensor            # [T, H, D], new tokens of all sequences, packed
+    k: torch.Tensor            # [T, H_kv, D]
+    v: torch.Tensor            # [T, H_kv, D]
+    k_cache: torch.Tensor      # [num_pages, page_size, H_kv, D] (the prefixes)
+    v_cache: torch.Tensor
+    page_table: torch.Tensor   # [B, max_pages_per_seq] int32
+    prefix_lens: torch.Tensor  # [B] int32
+    qo_start: torch.Tensor     # [B + 1] int32, new tokens of b at rows qo_start[b] ..
+    page_size: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_extend_len(self) -> int:
+        return int((self.qo_start[1:] - self.qo_start[:-1]).max()) if len(self.qo_start) > 1 else 0
+
+
+def extend_inputs(B, H, D, prefix_lens, extend_lens, dtype="f16", page_size=16, num_pages=None,
+                  seed=0, h_kv=None, amp=1.0, fill=0.0):
+    """Seeded extend batch (CPU tensors): the prefixes are a paged-decode batch
+    (``paged_decode_inputs`` with seq_lens = prefix_lens, same seed); the new
+    tokens' q, k, v are then drawn from a generator seeded ``seed + 7919``, in
+    the order q, k, v, packed token-major."""
+    prefix_lens = [int(x) for x in prefix_lens]
+    extend_lens = [int(x) for x in extend_lens]
+    assert len(prefix_lens) == B and len(extend_lens) == B
+    hk = H if h_kv is None else h_kv
+    pages = sum(-(-p // page_size) for p in prefix_lens)
+    if num_pages is None:
+        num_pages = max(1, 2 * pages)
+    max_pages = max(1, -(-max(prefix_lens + [1]) // page_size))
+    pre = paged_decode_inputs(B, H, D, dtype, page_size, num_pages, seed=seed, fill=fill,
+                              seq_lens=prefix_lens, amp=amp, max_pages_per_seq=max_pages,
+                              h_kv=hk)
+    g = torch.Generator().manual_seed(seed + 7919)
+    T = sum(extend_lens)
+    q = _draw((T, H, D), g, amp, dtype)
+    k = _draw((T, hk, D), g, amp, dtype)
+    v = _draw((T, hk, D), g, amp, dtype)
+    starts = torch.tensor([0] + list(np.cumsum(extend_lens)), dtype=torch.int32)
+    meta = dict(B=B, H=H, H_kv=hk, D=D, dtype=dtype, page_size=page_size, num_pages=num_pages,
+                seed=seed, total_tokens=T)
+    return ExtendBatch(q=q, k=k, v=v, k_cache=pre.k_cache, v_cache=pre.v_cache,
+                       page_table=pre.page_table, prefix_lens=pre.seq_lens, qo_start=starts,
+                       page_size=page_size, meta=meta)
+
+
+def extend_config(cfg: int):
+    """ExtendBatch for one of the numbered extend workloads, seeded with its number:
+    prefix and extend lengths drawn uniformly (inclusive) from their ranges."""
+    c = dict(EXTEND_CONFIGS[cfg])
+    g = torch.Generator().manual_seed(cfg)
+    plen = torch.randint(c["min_prefix"], c["max_prefix"] + 1, (c["B"],), generator=g).tolist()
+    elen = torch.randint(c["min_extend"], c["max_extend"] + 1, (c["B"],), generator=g).tolist()
+    batch = extend_inputs(c["B"], c["H"], c["D"], plen, elen, c["dtype"], c["page_size"],
+                          seed=cfg, h_kv=c.get("H_kv"))
+    batch.meta.update(name=c["name"], scale=default_scale(c["D"]), config=cfg)
+    return batch
 
 
 def decode_config(cfg: int, fill=0.0):
