@@ -7,9 +7,9 @@ there is no CPU fallback: if the shared library is missing the calls raise.
 
 Low-level functions carry the C names (``attn_prefill``,
 ``attn_prefill_gqa``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
-workspace-size and split-plan queries, ``attn_status_string``) and take
-tensors or raw integer pointers; ``prefill`` and ``paged_decode`` are
-conveniences that derive the sizes (including the number of KV heads) from
+workspace-size and split-plan queries, ``attn_extend``, ``attn_status_string``)
+and take tensors or raw integer pointers; ``prefill``, ``paged_decode`` and
+``extend`` are conveniences that derive the sizes (including the number of KV heads) from
 tensor shapes and allocate the output.
 """
 from __future__ import annotations
@@ -41,6 +41,8 @@ SIGNATURES = {
                                    _F, _VP, _SZ, _VP]),
     "attn_paged_decode_gqa_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "attn_paged_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "attn_extend": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
+                         _I, _I, _I, _F, _VP]),
 }
 
 _lib = None
@@ -137,6 +139,16 @@ def attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H,
         H_kv, D, page_size, num_pages, max_pages_per_seq, dtype, float(scale), _ptr(workspace),
         int(workspace_bytes), _stream(stream))
+
+
+def attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H, H_kv, D,
+                total_tokens, max_extend_len, page_size, num_pages, max_pages_per_seq, dtype,
+                scale, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_extend(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        _ptr(prefix_lens), _ptr(qo_start), _ptr(o), B, H, H_kv, D, total_tokens, max_extend_len,
+        page_size, num_pages, max_pages_per_seq, dtype, float(scale), _stream(stream))
 
 
 def attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size) -> int:
@@ -254,4 +266,46 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=N
                                  page_size, num_pages, max_pages, code, scale, workspace,
                                  workspace.numel() * workspace.element_size(), stream),
            "attn_paged_decode_gqa")
+    return o
+
+
+def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *, max_extend_len=None,
+           scale=None, out=None, out_dtype=None, stream=None):
+    """Extend attention: new tokens (q [T,H,D], k, v [T,H_kv,D], packed by
+    qo_start [B+1]) after cached prefixes (k_cache, v_cache [P,16,H_kv,D],
+    page_table [B,max_pages], prefix_lens [B]); see attn_extend in attn.h.
+
+    max_extend_len bounds every sequence's new-token count; if omitted it is
+    read from qo_start, which synchronises with the device.
+    """
+    import torch
+    T, H, D = q.shape
+    H_kv = k.shape[1]
+    if tuple(k.shape) != (T, H_kv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_tokens, H_kv, D]")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (num_pages, page_size, H_kv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H_kv, D]")
+    for t in (page_table, prefix_lens, qo_start):
+        if t.dtype != torch.int32:
+            raise TypeError("page_table, prefix_lens and qo_start must be int32")
+    for t in (q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous GPU tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype != k_cache.dtype:
+        raise TypeError("q, k, v and the cache must share a dtype")
+    B = prefix_lens.shape[0]
+    if tuple(qo_start.shape) != (B + 1,) or page_table.shape[0] != B:
+        raise ValueError("qo_start must be [B+1] and page_table [B, max_pages]")
+    if max_extend_len is None:
+        max_extend_len = int((qo_start[1:] - qo_start[:-1]).max().item()) if B else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code, odt = _out_code(q, out, out_dtype)
+    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
+    if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped like q")
+    _check(attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H,
+                       H_kv, D, T, max_extend_len, page_size, num_pages, page_table.shape[1],
+                       code, scale, stream), "attn_extend")
     return o

@@ -139,7 +139,66 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B
   }
   a.c = exp2_multiplier(scale);
   a.causal_off = Skv - Sq;
+  a.k_cache = a.v_cache = nullptr;
+  a.page_table = a.prefix_lens = a.qo_start = nullptr;
+  a.max_pages = a.num_pages = a.total_tokens = 0;
   hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_extend(const void* q, const void* k, const void* v, const void* k_cache,
+                const void* v_cache, const int32_t* page_table, const int32_t* prefix_lens,
+                const int32_t* qo_start, void* o, int B, int H, int H_kv, int D,
+                int total_tokens, int max_extend_len, int page_size, int num_pages,
+                int max_pages_per_seq, int dtype, float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || total_tokens < 0 || max_extend_len < 0 || num_pages < 0 ||
+      max_pages_per_seq < 0)
+    return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * max_extend_len == 0 || total_tokens == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !qo_start) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  if ((uintptr_t)qo_start & 3u) return ATTN_E_INVALID;
+  if (max_pages_per_seq > 0) {  // prefixes may exist: the cache must be there
+    if (num_pages == 0 || !k_cache || !v_cache || !page_table || !prefix_lens)
+      return ATTN_E_INVALID;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return ATTN_E_INVALID;
+    if (((uintptr_t)page_table & 3u) || ((uintptr_t)prefix_lens & 3u)) return ATTN_E_INVALID;
+  }
+  // Row offsets within a sequence's new tokens are 32-bit in the kernel.
+  if ((int64_t)max_extend_len * H * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)kDecodePageSize * H_kv * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.group = H / H_kv;
+  a.Sq = max_extend_len;  // bounds every sequence's new tokens; sets the grid
+  a.Skv = 0;
+  a.causal_off = 0;
+  a.n_mtiles = 0;
+  a.total_tiles = 0;
+  a.q_sb = 0; a.q_sh = D; a.q_ss = H * D;          // [T, H, D]
+  a.k_sb = 0; a.k_sh = D; a.k_ss = H_kv * D;       // [T, H_kv, D]
+  a.c = exp2_multiplier(scale);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.prefix_lens = prefix_lens;
+  a.qo_start = qo_start;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.total_tokens = total_tokens;
+  hipError_t e = launch_extend(D, bf16, out_f32, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

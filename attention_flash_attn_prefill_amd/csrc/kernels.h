@@ -22,10 +22,23 @@ struct PrefillArgs {
   int k_ss;
   float c;             // scale * log2(e)
   int causal_off;      // Skv - Sq (bottom-right causal alignment)
+  // Extend kernels only: the new tokens of sequence b are rows qo_start[b] ..
+  // qo_start[b+1]-1 of q, k, v, o (token-major, Sq = max_extend_len bounds
+  // them), and its first prefix_lens[b] keys come from a paged cache
+  // [num_pages, 16, H_kv, D] through page_table [B, max_pages].
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* prefix_lens;
+  const int32_t* qo_start;
+  int max_pages, num_pages, total_tokens;
 };
 
 hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
                           int B, hipStream_t s);
+// Extend attention (causal over a paged prefix followed by the new tokens).
+hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
+                         hipStream_t s);
 
 // Paged decode.  H query heads share H_kv KV heads (group = H / H_kv).
 // group = 1: decode.hip, one wave per (sequence, head, split), four heads per

@@ -78,8 +78,10 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 }
 
 // NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
-// OF32: O is stored in fp32 instead of the input type.
-template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN>
+// OF32: O is stored in fp32 instead of the input type.  EXT (with CAUSAL):
+// extend attention -- a sequence's keys are its cached prefix, read through
+// the page table, followed by its new tokens (PrefillArgs, extend fields).
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   constexpr int LOADS = BN * CPR / NT;    // chunk loads per thread per K (or V) tile
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly over the threads");
   static_assert(BN % 32 == 0 && 2 * 2 * BN * D * 2 <= 160 * 1024, "tile shape");
+  static_assert(!EXT || (CAUSAL && BN % 16 == 0 && (64 / CPR) <= 16 && 16 % (64 / CPR) == 0),
+                "extend: causal, and each load instruction's rows within one page");
   // Two LDS stages each of K and V, as separate objects so the compiler can
   // tell the stage being filled from the stage being read.
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[BN * D];
@@ -115,15 +119,33 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const int hk = L % a.H_kv, b = L / a.H_kv;
   const int h = hk * a.group + g;
 
-  const uint16_t* __restrict__ qp = a.q + b * a.q_sb + h * a.q_sh;
-  const int64_t o_base = b * a.q_sb + h * a.q_sh;  // o shares q's element strides
-  const uint16_t* __restrict__ kp = a.k + b * a.k_sb + hk * a.k_sh;
-  const uint16_t* __restrict__ vp = a.v + b * a.k_sb + hk * a.k_sh;
+  // Sequence sizes.  Extend: Sq = the sequence's new tokens, Skv = prefix +
+  // new, bottom-right causal (offset = prefix length); the first n_pre tiles
+  // hold prefix keys [0, P) from the cache, the rest new keys from k, v.
+  int Sq = a.Sq, Skv = a.Skv, coff = a.causal_off, P = 0, n_pre = 0;
+  int64_t q_base = b * a.q_sb + h * a.q_sh;   // o shares q's element strides
+  int64_t kv_base = b * a.k_sb + hk * a.k_sh;
+  if constexpr (EXT) {
+    const int r0 = a.qo_start[b], r1 = a.qo_start[b + 1];
+    if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // invalid range: not computed
+    Sq = min(r1 - r0, a.Sq);                                // a.Sq = max_extend_len
+    P = a.max_pages > 0 ? max(0, min(a.prefix_lens[b], a.max_pages * kDecodePageSize)) : 0;
+    Skv = P + Sq;
+    coff = P;
+    n_pre = (P + BN - 1) / BN;
+    q_base = (int64_t)r0 * a.q_ss + h * a.q_sh;
+    kv_base = (int64_t)r0 * a.k_ss + hk * a.k_sh;
+  }
+  const uint16_t* __restrict__ qp = a.q + q_base;
+  const int64_t o_base = q_base;
+  const uint16_t* __restrict__ kp = a.k + kv_base;
+  const uint16_t* __restrict__ vp = a.v + kv_base;
 
   const int m0 = mt * BM;
+  if (EXT && m0 >= Sq) return;  // past this sequence's new tokens (workgroup-uniform)
   const int q0 = m0 + wave * 32;
   const int qi = q0 + li;
-  const bool q_ok = qi < a.Sq;
+  const bool q_ok = qi < Sq;
 
   // Q^T fragments (B operand): lane holds Q[qi][16s + 8hi .. +7].
   u32x4 qf[D / 16];
@@ -133,12 +155,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
                  : (u32x4){0u, 0u, 0u, 0u};
 
   // Keys this workgroup needs: [0, kv_end).
-  int kv_end = a.Skv;
-  if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + BM, a.Sq) + a.causal_off));
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  int kv_end = Skv;
+  if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + BM, Sq) + coff));
+  const int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
   // Keys this wave needs: [0, wave_kv_end).
-  const bool wave_active = q0 < a.Sq;
-  const int wave_kv_end = CAUSAL ? min(a.Skv, min(q0 + 32, a.Sq) + a.causal_off) : a.Skv;
+  const bool wave_active = q0 < Sq;
+  const int wave_kv_end = CAUSAL ? min(Skv, min(q0 + 32, Sq) + coff) : Skv;
+  // First key (in the whole key sequence) of tile t, and whether it is a
+  // prefix tile (extend only).
+  auto is_pre = [&](int t) { return EXT && t < n_pre; };
+  auto tile_key0 = [&](int t) { return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : t * BN; };
 
   // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
   // LDS chunk P = (wave * LOADS + i) * 64 + lane of the tile: row P / CPR,
@@ -146,37 +172,87 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   int g_off[LOADS];  // byte offset of the chunk within the tile's rows
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int P = (wave * LOADS + i) * 64 + lane;
-    const int row = P / CPR, pos = P % CPR;
+    const int chunk = (wave * LOADS + i) * 64 + lane;
+    const int row = chunk / CPR, pos = chunk % CPR;
     g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
   }
   const uint32_t row_bytes = (uint32_t)a.k_ss * 2u;
+  const int n_rows = EXT ? Sq : Skv;  // rows of k, v (the new tokens, for extend)
 
   auto tile_rsrc = [&](const uint16_t* base, int kv0) {
-    const uint32_t rows = (uint32_t)max(0, a.Skv - kv0);
+    const uint32_t rows = (uint32_t)max(0, n_rows - kv0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss), (short)0,
                                              (int)(rows * row_bytes), kBufferConfig);
+  };
+
+  // Extend prefix tiles: load i of a wave covers 64 / CPR rows of one page
+  // (rows are 16-aligned within the tile, pages hold 16 tokens).  Its buffer
+  // spans the page's slots below P, so rows past the prefix read as zero.
+  constexpr int ROWS_PER_LOAD = 64 / CPR;
+  const int64_t page_elems = (int64_t)kDecodePageSize * a.H_kv * D;
+  const uint32_t slot_bytes = (uint32_t)a.H_kv * D * 2u;
+  const int32_t* ptab = EXT ? a.page_table + (int64_t)b * a.max_pages : nullptr;
+  int pg_off[LOADS];  // byte offset of the chunk within its page
+  if constexpr (EXT) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int chunk = (wave * LOADS + i) * 64 + lane;
+      const int row = chunk / CPR, pos = chunk % CPR;
+      pg_off[i] = ((row % kDecodePageSize) * a.H_kv * D + hk * D + ((pos ^ swz<D>(row)) * 8)) * 2;
+    }
+  }
+  bool bad_page = false;  // workgroup-uniform: a prefix page id outside the pool
+  // Every wave checks every live page of a prefix tile, so all waves agree.
+  auto pages_ok = [&](int t) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < BN / kDecodePageSize; ++j) {
+      const int tok = t * BN + j * kDecodePageSize;
+      if (tok < P) ok &= (uint32_t)ptab[tok / kDecodePageSize] < (uint32_t)a.num_pages;
+    }
+    return ok;
+  };
+  auto page_rsrc = [&](const uint16_t* cache, int t, int i) {
+    const int row0 = (wave * LOADS + i) * ROWS_PER_LOAD;  // first row of load i
+    const int tok = t * BN + row0;
+    const int page_tok = tok - (tok % kDecodePageSize);
+    const int live = min(kDecodePageSize, P - page_tok);
+    const uint16_t* base =
+        live > 0 ? cache + (int64_t)ptab[tok / kDecodePageSize] * page_elems : cache;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                             (int)(max(live, 0) * slot_bytes), kBufferConfig);
   };
 
   // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
   // first for the fp16 conversion; store_v writes it to LDS).
   u32x4 vreg[LOADS];
-  auto issue_k = [&](int kv0, LDS_AS uint16_t* k_dst) {
-    const auto rk = tile_rsrc(kp, kv0);
+  auto issue_k = [&](int t, LDS_AS uint16_t* k_dst) {
+    if (is_pre(t)) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(a.k_cache, t, i),
+                                                 (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
+                                                 16, pg_off[i], 0, 0, 0);
+      return;
+    }
+    const auto rk = tile_rsrc(kp, tile_key0(t) - P);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
                                                16, g_off[i], 0, 0, 0);
   };
-  auto issue_v = [&](int kv0, LDS_AS uint16_t* v_dst) {
-    const auto rv = tile_rsrc(vp, kv0);
+  auto issue_v = [&](int t, LDS_AS uint16_t* v_dst) {
+    const bool pre = is_pre(t);
+    const auto rv = tile_rsrc(vp, pre ? 0 : tile_key0(t) - P);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
+      const auto r = pre ? page_rsrc(a.v_cache, t, i) : rv;
+      const int off = pre ? pg_off[i] : g_off[i];
       if constexpr (BF16)
-        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, g_off[i], 0, 0));
+        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
-                                                 16, g_off[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
+                                                 16, off, 0, 0, 0);
     }
   };
   // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
@@ -241,11 +317,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
       for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk<BF16>(kf[s][jb], qf[s], sc[jb]);
   };
 
-  // Mask keys past the sequence end and (causal) above the diagonal.
-  auto mask_tile = [&](int kv0, f32x16 (&sc)[BN / 32]) {
-    const bool need_mask = (kv0 + BN > a.Skv) || (CAUSAL && kv0 + BN - 1 > q0 + a.causal_off);
+  // Mask keys past the sequence end and (causal) above the diagonal; in an
+  // extend prefix tile, the rows past the prefix.
+  auto mask_tile = [&](int t, f32x16 (&sc)[BN / 32]) {
+    const int kv0 = tile_key0(t);
+    const bool pre = is_pre(t);
+    const bool need_mask = pre ? kv0 + BN > P
+                               : (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0 + coff);
     if (need_mask) {
-      const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
+      const int lim = pre ? P - 1 : (CAUSAL ? min(Skv - 1, qi + coff) : Skv - 1);
 #pragma unroll
       for (int jb = 0; jb < BN / 32; ++jb)
 #pragma unroll
@@ -330,32 +410,37 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
   LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
 
-  if (n_tiles > 0) {
+  // A tile is loaded only when its pages check out (dense tiles always do).
+  auto load_ok = [&](int t) {
+    if (is_pre(t) && !pages_ok(t)) bad_page = true;
+    return !bad_page;
+  };
+  if (n_tiles > 0 && load_ok(0)) {
     issue_v(0, Vs[0]);
     issue_k(0, Ks[0]);
     store_v(Vs[0]);
   }
   auto iteration = [&](int t, auto par) {
-    constexpr int P = decltype(par)::value;  // t % 2
+    constexpr int S = decltype(par)::value;  // t % 2
     // Tile t has landed for this wave; after the barrier for every wave, and
     // every wave is done with tile t-1, whose stages are refilled next.
     wait_vmcnt<0>();
     __syncthreads();
-    const bool more = t + 1 < n_tiles;
+    const bool more = t + 1 < n_tiles && load_ok(t + 1);
     if (more) {
-      issue_v((t + 1) * BN, Vs[P ^ 1]);
-      issue_k((t + 1) * BN, Ks[P ^ 1]);
+      issue_v(t + 1, Vs[S ^ 1]);
+      issue_k(t + 1, Ks[S ^ 1]);
     }
-    if (wave_active && t * BN < wave_kv_end) {
+    if (wave_active && (is_pre(t) || tile_key0(t) < wave_kv_end)) {
       f32x16 sc[BN / 32];
-      qk(Ks[P], sc);
-      mask_tile(t * BN, sc);
+      qk(Ks[S], sc);
+      mask_tile(t, sc);
       const float base = max_rescale(sc);
       u32x4 pf[BN / 16];
       exp_tile(sc, base, pf);
-      pv(pf, Vs[P]);
+      pv(pf, Vs[S]);
     }
-    if (more) store_v(Vs[P ^ 1]);
+    if (more) store_v(Vs[S ^ 1]);
   };
   for (int t = 0; t < n_tiles; t += 2) {
     iteration(t, std::integral_constant<int, 0>{});
@@ -365,7 +450,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
   // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // A rejected prefix page makes the rows NaN (the key set is unknown).
+  const float inv = bad_page ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
   if (q_ok) {
     const int64_t row = o_base + (int64_t)qi * a.q_ss;
 #pragma unroll
@@ -393,15 +479,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN>
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false>
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
   const int64_t n_mtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t total = (int64_t)B * a.H * n_mtiles;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;
   a.total_tiles = (int)total;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN>), dim3(a.total_tiles),
-                     dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN, EXT>),
+                     dim3(a.total_tiles), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -434,6 +520,26 @@ hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const Pre
                           int B, hipStream_t s) {
   if (D == 128) return launch_o<128>(bf16, causal, out_f32, a, B, s);
   if (D == 64) return launch_o<64>(bf16, causal, out_f32, a, B, s);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+template <int D>
+hipError_t launch_ext_d(bool bf16, bool out_f32, const PrefillArgs& a, int B, hipStream_t s) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int BN = 64;
+  if (bf16)
+    return out_f32 ? launch_t<D, true, true, true, NW, BN, true>(a, B, s)
+                   : launch_t<D, true, true, false, NW, BN, true>(a, B, s);
+  return out_f32 ? launch_t<D, false, true, true, NW, BN, true>(a, B, s)
+                 : launch_t<D, false, true, false, NW, BN, true>(a, B, s);
+}
+}  // namespace
+
+hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
+                         hipStream_t s) {
+  if (D == 128) return launch_ext_d<128>(bf16, out_f32, a, B, s);
+  if (D == 64) return launch_ext_d<64>(bf16, out_f32, a, B, s);
   return hipErrorInvalidValue;
 }
 

@@ -106,6 +106,43 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o,
                      int causal, float scale, hipStream_t stream);
 
 /*
+ * Extend attention: prefill of new tokens after a cached prefix (chunked
+ * prefill; the "extend" call of an LLM serving backend: "WAVE: A Symbolic
+ * Python DSL and Compiler for High Performance Machine Learning (MLSys 2026)",
+ * integration notes; extend attention in the "Wave February 2025 Release"
+ * roadmap).  For each of the B sequences:
+ *
+ *   - prefix_lens[b] tokens are already in a paged cache k_cache, v_cache
+ *     [num_pages, page_size, H_kv, D], token t at page page_table[b][t / 16],
+ *     slot t % 16 (page_table [B, max_pages_per_seq] int32), as in
+ *     attn_paged_decode_gqa;
+ *   - its E_b = qo_start[b+1] - qo_start[b] new tokens are rows qo_start[b] ..
+ *     qo_start[b+1]-1 of q [total_tokens, H, D], k, v [total_tokens, H_kv, D]
+ *     and o [total_tokens, H, D] (packed token-major; qo_start [B+1] int32);
+ *   - new token i attends to every prefix token and to new tokens 0..i
+ *     (causal attention over prefix + new tokens, aligned bottom-right), query
+ *     head h to KV head h / (H / H_kv).
+ *
+ * The pages do not define the operation further; this is the plain reading
+ * (the new tokens' K/V are not written to the cache here).  max_extend_len
+ * >= every E_b bounds the grid: rows of a sequence past max_extend_len are
+ * not written.  page_size: 16; D: 64 or 128.  Arithmetic as attn_prefill.
+ *
+ * Device data (read only on the device): prefix_lens[b] is clamped to
+ * [0, max_pages_per_seq * 16]; a sequence whose qo_start range is not within
+ * [0, total_tokens] is skipped (its rows are not written); a prefix page id
+ * outside [0, num_pages) is never dereferenced and makes the sequence's rows
+ * NaN.  With max_pages_per_seq = 0 there is no prefix and k_cache, v_cache,
+ * page_table and prefix_lens may be NULL.
+ */
+int attn_extend(const void* q, const void* k, const void* v,
+                const void* k_cache, const void* v_cache,
+                const int32_t* page_table, const int32_t* prefix_lens, const int32_t* qo_start,
+                void* o, int B, int H, int H_kv, int D, int total_tokens, int max_extend_len,
+                int page_size, int num_pages, int max_pages_per_seq, int dtype, float scale,
+                hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_paged_decode needs for these sizes: the
  * per-split partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
  */

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
                             "attn_paged_decode_workspace_size", "attn_paged_decode_num_splits",
                             "attn_prefill_gqa", "attn_paged_decode_gqa",
                             "attn_paged_decode_gqa_workspace_size",
-                            "attn_paged_decode_gqa_num_splits"])
+                            "attn_paged_decode_gqa_num_splits", "attn_extend"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -209,3 +209,35 @@ def test_split_plan_and_workspace():
 def test_no_cpu_fallback(tmp_path):
     with pytest.raises(ImportError):
         attn.load_library(str(tmp_path / "missing.so"))
+
+
+def _extend(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE,
+             prefix_lens=FAKE, qo_start=FAKE, o=FAKE, B=4, H=8, H_kv=2, D=128, total_tokens=100,
+             max_extend_len=64, page_size=16, num_pages=64, max_pages_per_seq=8, dtype=1,
+             scale=0.1, stream=0)
+    a.update(kw)
+    return attn.attn_extend(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(max_extend_len=-1), attn.ATTN_E_INVALID),
+    (dict(total_tokens=-1), attn.ATTN_E_INVALID),
+    (dict(D=32), attn.ATTN_E_UNSUPPORTED),
+    (dict(page_size=8), attn.ATTN_E_UNSUPPORTED),
+    (dict(qo_start=None), attn.ATTN_E_INVALID),
+    (dict(qo_start=FAKE + 2), attn.ATTN_E_INVALID),
+    (dict(k_cache=None), attn.ATTN_E_INVALID),          # a prefix may exist
+    (dict(num_pages=0), attn.ATTN_E_INVALID),
+    (dict(q=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(max_extend_len=1 << 20, H=64, H_kv=8), attn.ATTN_E_UNSUPPORTED),
+])
+def test_extend_validation(kw, status):
+    assert _extend(**kw) == status
+
+
+def test_extend_empty_is_a_noop():
+    assert _extend(B=0, q=None, k=None, v=None, o=None, qo_start=None) == attn.ATTN_OK
+    assert _extend(max_extend_len=0) == attn.ATTN_OK
+    assert _extend(total_tokens=0) == attn.ATTN_OK

@@ -1,0 +1,139 @@
+"""GPU parity of extend attention (attn_extend: new tokens after a paged
+prefix) through the C ABI against the fp64 oracle; same bar as prefill."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(batch):
+    return {n: getattr(batch, n).cuda() for n in ("q", "k", "v", "k_cache", "v_cache",
+                                                 "page_table", "prefix_lens", "qo_start")}
+
+
+def _run(attn, batch, **kw):
+    g = _gpu(batch)
+    print(f"[case] extend B{len(batch.prefix_lens)} H{batch.q.shape[1]}/{batch.k.shape[1]} "
+          f"D{batch.q.shape[2]} {batch.q.dtype} prefix={batch.prefix_lens.tolist()[:6]} "
+          f"starts={batch.qo_start.tolist()[:7]}", flush=True)
+    o = attn.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                    g["prefix_lens"], g["qo_start"], **kw)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _ref(batch, **kw):
+    return oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                         batch.page_table, batch.prefix_lens, batch.qo_start, **kw)
+
+
+CASES = [  # (prefix_lens, extend_lens)
+    ([0, 1, 15, 16, 17, 63, 64, 65], [1, 2, 17, 64, 65, 100, 255, 256]),
+    ([300, 1000, 0], [700, 5, 513]),
+    ([128, 4096], [1, 300]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (8, 2), (6, 1)])
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (128, "f16"), (64, "f16"), (64, "bf16")])
+def test_extend_parity_nan_poisoned(gpu_lib, case, H, H_kv, D, dtype):
+    pl, el = CASES[case]
+    batch = workloads.extend_inputs(len(pl), H, D, pl, el, dtype, seed=80 + case + H_kv + D,
+                                    h_kv=H_kv, fill=float("nan"))
+    o = _run(gpu_lib, batch)
+    assert torch.isfinite(o.float()).all(), "NaN from a free cache slot leaked into O"
+    assert_parity(o.double().numpy(), _ref(batch), f"extend case {case} H{H}/{H_kv} D{D} {dtype}")
+
+
+def test_extend_without_prefix_equals_causal_prefill_bitwise(gpu_lib):
+    el = [300, 77]
+    batch = workloads.extend_inputs(2, 8, 128, [0, 0], el, "bf16", seed=90, h_kv=2)
+    o = _run(gpu_lib, batch)
+    for b in range(2):
+        r0, r1 = int(batch.qo_start[b]), int(batch.qo_start[b + 1])
+        ref = gpu_lib.prefill(batch.q[None, r0:r1].cuda(), batch.k[None, r0:r1].cuda(),
+                              batch.v[None, r0:r1].cuda(), causal=True, layout="BSHD")
+        torch.cuda.synchronize()
+        assert torch.equal(o[r0:r1], ref[0].cpu()), f"sequence {b}"
+
+
+def test_extend_equals_prefill_on_concatenated_kv_bitwise(gpu_lib):
+    """With a prefix of whole 64-key tiles, extend walks the same tiles as a
+    bottom-right causal prefill over prefix + new keys."""
+    P, E = 256, 190
+    batch = workloads.extend_inputs(1, 4, 128, [P], [E], "f16", seed=91, h_kv=4)
+    o = _run(gpu_lib, batch)
+    tok = torch.arange(P)
+    pages = batch.page_table[0].long()[tok // 16]
+    kk = torch.cat([batch.k_cache[pages, tok % 16], batch.k])[None]
+    vv = torch.cat([batch.v_cache[pages, tok % 16], batch.v])[None]
+    ref = gpu_lib.prefill(batch.q[None].cuda(), kk.cuda(), vv.cuda(), causal=True, layout="BSHD")
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0].cpu())
+
+
+def test_extend_out_f32(gpu_lib):
+    batch = workloads.extend_inputs(3, 8, 128, [40, 0, 500], [100, 33, 260], "bf16", seed=92,
+                                    h_kv=2)
+    o32 = _run(gpu_lib, batch, out_dtype=torch.float32)
+    o16 = _run(gpu_lib, batch)
+    assert_parity(o32.double().numpy(), _ref(batch), "extend out_f32", max_abs_tol=3e-3,
+                  rel_fro_tol=5e-4)
+    assert torch.equal(o32.to(o16.dtype), o16)
+
+
+def test_extend_bad_page_id_gives_nan(gpu_lib):
+    batch = workloads.extend_inputs(3, 4, 128, [40, 100, 20], [30, 20, 10], "f16", seed=93,
+                                    num_pages=64)
+    P = batch.k_cache.shape[0]
+    table = batch.page_table.clone()
+    table[1, 2] = P            # a live prefix page of sequence 1: one past the pool
+    table[0, 5] = P + 500      # past sequence 0's prefix: never read
+    batch.page_table = table
+    pad = (P + 2,) + tuple(batch.k_cache.shape[1:])
+    k_pad = torch.zeros(pad, dtype=batch.k_cache.dtype, device="cuda")
+    v_pad = torch.zeros(pad, dtype=batch.v_cache.dtype, device="cuda")
+    k_pad[1:P + 1].copy_(batch.k_cache)
+    v_pad[1:P + 1].copy_(batch.v_cache)
+    g = _gpu(batch)
+    print("[case] extend bad page id", flush=True)
+    o = gpu_lib.extend(g["q"], g["k"], g["v"], k_pad[1:P + 1], v_pad[1:P + 1], g["page_table"],
+                       g["prefix_lens"], g["qo_start"]).float().cpu()
+    torch.cuda.synchronize()
+    s = batch.qo_start.tolist()
+    assert torch.isnan(o[s[1]:s[2]]).all()
+    good = list(range(s[0], s[1])) + list(range(s[2], s[3]))
+    ref = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        torch.where(table >= P, torch.zeros_like(table), table),
+                        batch.prefix_lens, batch.qo_start, seqs=[0, 2])
+    assert_parity(o[good].double().numpy(), ref[good], "extend sequences with valid pages")
+
+
+def test_extend_rows_past_max_extend_len_untouched(gpu_lib):
+    batch = workloads.extend_inputs(2, 4, 64, [10, 20], [40, 100], "f16", seed=94)
+    g = _gpu(batch)
+    out = torch.full(batch.q.shape, 7.0, dtype=batch.q.dtype, device="cuda")
+    print("[case] extend max_extend_len 64", flush=True)
+    gpu_lib.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                   g["prefix_lens"], g["qo_start"], max_extend_len=64, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    ref = _ref(batch)
+    rows = list(range(0, 40)) + list(range(40, 104))
+    assert_parity(o[rows].double().numpy(), ref[rows], "rows within max_extend_len")
+    assert torch.all(o[104:140] == 7.0)
+
+
+def test_extend_full_config9_sampled(gpu_lib):
+    batch = workloads.extend_config(9)
+    o = _run(gpu_lib, batch, scale=batch.meta["scale"])
+    seqs = [0, 3, 7]
+    ref = _ref(batch, scale=batch.meta["scale"], seqs=seqs)
+    rows = [r for b in seqs for r in range(int(batch.qo_start[b]), int(batch.qo_start[b + 1]))]
+    assert_parity(o[rows].double().numpy(), ref[rows], f"config 9 ({len(rows)} rows of {seqs})")
