@@ -202,23 +202,39 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     }
   }
   bool bad_page = false;  // workgroup-uniform: a prefix page id outside the pool
-  // Every wave checks every live page of a prefix tile, so all waves agree.
-  auto pages_ok = [&](int t) {
+  // Page ids of the next prefix tile to load (-1: no live token there),
+  // fetched a tile ahead by a vector load -- lane j & 3 reads page j of the
+  // tile -- so the read is waited for with the tile loads (vmcnt) at the next
+  // barrier; a scalar load would share its counter with the LDS operand reads
+  // and stall the compute in between.
+  constexpr int PPT = BN / kDecodePageSize;  // pages per tile
+  static_assert(PPT == 4, "page ids of a tile are kept in one 4-vector");
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  int pgv_next = -1;
+  auto fetch_pages = [&](int t) {
+    const int tok = t * BN + (lane & 3) * kDecodePageSize;
+    pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : -1;
+  };
+  auto next_pages = [&]() {
+    return (i32x4){__builtin_amdgcn_readlane(pgv_next, 0), __builtin_amdgcn_readlane(pgv_next, 1),
+                   __builtin_amdgcn_readlane(pgv_next, 2), __builtin_amdgcn_readlane(pgv_next, 3)};
+  };
+  // Every wave checks every live page of the tile, so all waves agree.
+  auto pages_ok = [&](i32x4 pg) {
     bool ok = true;
 #pragma unroll
-    for (int j = 0; j < BN / kDecodePageSize; ++j) {
-      const int tok = t * BN + j * kDecodePageSize;
-      if (tok < P) ok &= (uint32_t)ptab[tok / kDecodePageSize] < (uint32_t)a.num_pages;
-    }
+    for (int j = 0; j < PPT; ++j) ok &= pg[j] < a.num_pages;  // -1 (no page) passes
     return ok;
   };
+  i32x4 pg_cur = {-1, -1, -1, -1};  // page ids of the tile being loaded
   auto page_rsrc = [&](const uint16_t* cache, int t, int i) {
     const int row0 = (wave * LOADS + i) * ROWS_PER_LOAD;  // first row of load i
-    const int tok = t * BN + row0;
-    const int page_tok = tok - (tok % kDecodePageSize);
-    const int live = min(kDecodePageSize, P - page_tok);
-    const uint16_t* base =
-        live > 0 ? cache + (int64_t)ptab[tok / kDecodePageSize] * page_elems : cache;
+    const int j = row0 / kDecodePageSize;
+    const int live = min(kDecodePageSize, P - (t * BN + j * kDecodePageSize));
+    int pg = pg_cur[0];
+#pragma unroll
+    for (int jj = 1; jj < PPT; ++jj) pg = j == jj ? pg_cur[jj] : pg;
+    const uint16_t* base = live > 0 ? cache + (int64_t)pg * page_elems : cache;
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
                                              (int)(max(live, 0) * slot_bytes), kBufferConfig);
   };
@@ -410,11 +426,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
   LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
 
-  // A tile is loaded only when its pages check out (dense tiles always do).
+  // A tile is loaded only when its pages check out (dense tiles always do);
+  // its page ids move to pg_cur and the following tile's are fetched.
   auto load_ok = [&](int t) {
-    if (is_pre(t) && !pages_ok(t)) bad_page = true;
+    if constexpr (EXT) {
+      pg_cur = next_pages();
+      if (is_pre(t) && !pages_ok(pg_cur)) bad_page = true;
+      fetch_pages(t + 1);
+    }
     return !bad_page;
   };
+  if constexpr (EXT) fetch_pages(0);
   if (n_tiles > 0 && load_ok(0)) {
     issue_v(0, Vs[0]);
     issue_k(0, Ks[0]);

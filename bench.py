@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -10,8 +10,8 @@ Sq=Skv=4096 D=128 fp16 BHSD non-causal, with inputs resident in HBM.  The
 headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
 step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
-multi-query paged decode) are measured the same way and reported under
-"extra", decode in GB/s of algorithmic K/V bytes.
+multi-query paged decode, extend after a paged prefix) are measured the same
+way and reported under "extra", decode in GB/s of algorithmic K/V bytes.
 
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
 run on, bracketed by torch.cuda.synchronize(); HIP events around every step
@@ -280,6 +280,48 @@ def bench_decode(attn, cfg, steps, warmup, clock):
     return dict(config=cfg_out, timing=t, bytes_per_step=nbytes, gbs=gbs, roofline=roof)
 
 
+def extend_flops(batch):
+    """4 * H * D * (keys seen by each new token), summed: token i of sequence b
+    sees prefix_lens[b] + i + 1 keys."""
+    H, D = batch.q.shape[1], batch.q.shape[2]
+    total = 0
+    for b in range(len(batch.prefix_lens)):
+        P = int(batch.prefix_lens[b])
+        E = int(batch.qo_start[b + 1] - batch.qo_start[b])
+        total += E * P + E * (E + 1) // 2
+    return 4.0 * H * D * total
+
+
+def bench_extend(attn, cfg, steps, warmup, clock):
+    import torch
+    import workloads
+    batch = workloads.extend_config(cfg)
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k", "v", "k_cache", "v_cache", "page_table",
+                                              "prefix_lens", "qo_start")}
+    o = torch.empty_like(g["q"])
+    stream = torch.cuda.current_stream()
+    mx = batch.max_extend_len
+
+    def step():
+        attn.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                    g["prefix_lens"], g["qo_start"], max_extend_len=mx, scale=batch.meta["scale"],
+                    out=o, stream=stream)
+
+    t = measure(step, steps, warmup, stream, clock)
+    flops = extend_flops(batch)
+    tflops = flops / (t["mean_ms"] * 1e-3) / 1e12
+    cfg_out = {"workload": batch.meta["name"], "B": len(batch.prefix_lens),
+               "H": batch.q.shape[1], "H_kv": batch.k.shape[1], "D": batch.q.shape[2],
+               "dtype": batch.meta["dtype"], "new_tokens": int(batch.q.shape[0]),
+               "prefix_tokens": int(batch.prefix_lens.sum()), "max_extend_len": mx}
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16, 4),
+            "traffic": load_traffic(f"prefill_fwd__{batch.meta['name']}", PREFILL_SRC)}
+    del g, o
+    torch.cuda.empty_cache()
+    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof)
+
+
 def copy_calibration(mib):
     """A plain elementwise copy of known size (reads and writes mib MiB each),
     run so HBM byte counters can be scaled against it."""
@@ -371,7 +413,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
@@ -415,6 +457,8 @@ def main():
         print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
         if c in workloads.DECODE_CONFIGS:
             results[c] = bench_decode(attn, c, args.steps, args.warmup, clock)
+        elif c in workloads.EXTEND_CONFIGS:
+            results[c] = bench_extend(attn, c, args.steps, args.warmup, clock)
         else:
             results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock)
         r = results[c]
