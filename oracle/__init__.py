@@ -20,7 +20,9 @@ explicitly through the page table.  With fewer KV heads than query heads
 (grouped-query / multi-query attention, which the pages do not define), query
 head h reads KV head h // (H / H_kv).  Extend attention (new tokens after a
 cached prefix) is causal attention over the prefix gathered through the page
-table followed by the new tokens, bottom-right aligned.
+table followed by the new tokens, bottom-right aligned.  FP8 attention is
+the same function of the dequantised inputs (e4m3fn code x per-tensor
+descale).
 
 Pinned by ``tests/test_oracle.py`` (brute force at 50 digits, the torch
 library routine, closed forms, invariants) and
@@ -29,6 +31,7 @@ library routine, closed forms, invariants) and
 from .attention import (  # noqa: F401
     attend_rows,
     attention_probs,
+    dequantize_fp8,
     extend,
     gather_sequence,
     kv_head,

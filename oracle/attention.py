@@ -215,3 +215,9 @@ def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *,
             g = kv_head(h, H, H_kv)
             out[r0:r1, h] = attend_rows(qf[:, h], keys[:, g], vals[:, g], scale, vis)
     return out
+
+
+def dequantize_fp8(codes, descale: float) -> np.ndarray:
+    """float64 values of e4m3fn codes (a torch.float8_e4m3fn tensor) times the
+    per-tensor descale: the inputs an fp8 attention computes with."""
+    return codes.detach().to("cpu").to(torch.float64).numpy() * float(descale)

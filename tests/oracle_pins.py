@@ -483,6 +483,42 @@ def check_extend_chunking():
     _close(np.concatenate([part1, part2]), one[rows1 + rows2], 1e-13, "chunked extend")
 
 
+# ----------------------------------------------------------------- fp8 inputs
+
+def _e4m3fn_by_formula(code: int) -> float:
+    """OCP e4m3fn from its bit fields: sign, 4-bit exponent (bias 7), 3-bit
+    mantissa; exponent 0 is subnormal; S.1111.111 is NaN; no infinities."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def check_fp8_decode():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    got = oracle.dequantize_fp8(codes, 1.0)
+    ref = np.array([_e4m3fn_by_formula(c) for c in range(256)])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), np.nonzero(~same)
+    assert np.nanmax(np.abs(ref)) == 448.0
+
+
+def check_fp8_quantize_round_trip():
+    """Codes times descale reproduce the drawn values to e4m3fn precision, and
+    attention of the dequantised inputs matches the library routine."""
+    q8, k8, v8, (qs, ks, vs) = workloads.prefill_inputs_fp8(1, 2, 9, 12, 16, seed=700, h_kv=1)
+    q = oracle.dequantize_fp8(q8, qs)
+    assert np.abs(q).max() <= 448.0 * qs * (1 + 1e-12)
+    got = oracle.sdpa(torch.from_numpy(q), torch.from_numpy(oracle.dequantize_fp8(k8, ks)),
+                      torch.from_numpy(oracle.dequantize_fp8(v8, vs)), causal=True)
+    mask = torch.ones(9, 12, dtype=torch.bool).tril(diagonal=12 - 9)  # bottom-right
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(oracle.dequantize_fp8(k8, ks)),
+        torch.from_numpy(oracle.dequantize_fp8(v8, vs)), attn_mask=mask, enable_gqa=True).numpy()
+    _close(got, ref, 1e-12, "fp8 dequantised attention")
+
+
 ALL_CHECKS = [
     check_bruteforce, check_library_sdpa, check_rows_match_full, check_ones_v, check_causal_row0,
     check_zero_keys, check_two_keys, check_dominant_key, check_zero_scale,
@@ -490,5 +526,6 @@ ALL_CHECKS = [
     check_decode_library, check_decode_matches_prefill_row, check_decode_pool_permutation,
     check_decode_nan_poison, check_gqa_library, check_gqa_group_locality,
     check_gqa_rows_and_decode, check_extend_library, check_extend_without_prefix_is_causal_prefill,
-    check_extend_one_token_is_decode, check_extend_chunking,
+    check_extend_one_token_is_decode, check_extend_chunking, check_fp8_decode,
+    check_fp8_quantize_round_trip,
 ]

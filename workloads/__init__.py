@@ -48,6 +48,9 @@ PREFILL_CONFIGS = {
     # like the causal 8k workload.
     6: dict(name="gqa-causal-bshd-8k", B=2, H=32, H_kv=8, Sq=8192, Skv=8192, D=128,
             dtype="bf16", layout="BSHD", causal=True, amp=0.5, scale=None),
+    # FP8 (e4m3fn, per-tensor descales) inputs in the headline shape; O in fp16.
+    10: dict(name="fp8-llama2-13b-prefill", B=4, H=40, Sq=4096, Skv=4096, D=128, dtype="fp8",
+             layout="BHSD", causal=False, amp=1.0, scale=None, out_dtype="f16"),
 }
 
 # Paged decode workload.
@@ -102,11 +105,44 @@ def prefill_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, seed=0
     return q, k, v
 
 
+FP8_MAX = 448.0  # largest finite e4m3fn value
+
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-tensor e4m3fn quantisation: descale = amax / 448, codes = RNE(x / descale).
+    Returns (codes as torch.float8_e4m3fn, descale as a Python float)."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = amax / FP8_MAX if amax > 0 else 1.0
+    return (x / descale).to(torch.float8_e4m3fn), descale
+
+
+def prefill_inputs_fp8(B, H, Sq, Skv, D, layout="BHSD", amp=1.0, seed=0, h_kv=None):
+    """Seeded e4m3fn q, k, v with per-tensor descales: float32 N(0,1)*amp drawn
+    as in ``prefill_inputs`` (q, then k, then v), each quantised by
+    ``quantize_fp8``.  Returns (q8, k8, v8, (q_descale, k_descale, v_descale))."""
+    g = torch.Generator().manual_seed(seed)
+    hk = H if h_kv is None else h_kv
+    out, scales = [], []
+    for heads, S in ((H, Sq), (hk, Skv), (hk, Skv)):
+        x = torch.randn(layout_shape(B, heads, S, D, layout), generator=g, dtype=torch.float32)
+        if amp != 1.0:
+            x.mul_(amp)
+        c, d = quantize_fp8(x)
+        out.append(c)
+        scales.append(d)
+    return out[0], out[1], out[2], tuple(scales)
+
+
 def prefill_config(cfg: int):
     """(q, k, v, meta) for one of the numbered prefill workloads, seeded with its number."""
     c = dict(PREFILL_CONFIGS[cfg])
-    q, k, v = prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
-                             c["layout"], c["amp"], seed=cfg, h_kv=c.get("H_kv"))
+    if c["dtype"] == "fp8":
+        q, k, v, c["descales"] = prefill_inputs_fp8(c["B"], c["H"], c["Sq"], c["Skv"], c["D"],
+                                                    c["layout"], c["amp"], seed=cfg,
+                                                    h_kv=c.get("H_kv"))
+    else:
+        q, k, v = prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                 c["layout"], c["amp"], seed=cfg, h_kv=c.get("H_kv"))
     c.setdefault("H_kv", c["H"])
     if c["scale"] is None:
         c["scale"] = default_scale(c["D"])
