@@ -7,9 +7,10 @@ there is no CPU fallback: if the shared library is missing the calls raise.
 
 Low-level functions carry the C names (``attn_prefill``,
 ``attn_prefill_gqa``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
-workspace-size and split-plan queries, ``attn_extend``, ``attn_status_string``)
-and take tensors or raw integer pointers; ``prefill``, ``paged_decode`` and
-``extend`` are conveniences that derive the sizes (including the number of KV heads) from
+workspace-size and split-plan queries, ``attn_prefill_fp8``, ``attn_extend``,
+``attn_status_string``)
+and take tensors or raw integer pointers; ``prefill``, ``prefill_fp8``,
+``paged_decode`` and ``extend`` are conveniences that derive the sizes (including the number of KV heads) from
 tensor shapes and allocate the output.
 """
 from __future__ import annotations
@@ -41,6 +42,8 @@ SIGNATURES = {
                                    _F, _VP, _SZ, _VP]),
     "attn_paged_decode_gqa_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "attn_paged_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "attn_prefill_fp8": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _F,
+                              _F, _VP]),
     "attn_extend": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
                          _I, _I, _I, _F, _VP]),
 }
@@ -139,6 +142,15 @@ def attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H,
         H_kv, D, page_size, num_pages, max_pages_per_seq, dtype, float(scale), _ptr(workspace),
         int(workspace_bytes), _stream(stream))
+
+
+def attn_prefill_fp8(q, k, v, o, B, H, H_kv, Sq, Skv, D, layout, out_dtype, causal, scale,
+                     q_descale, k_descale, v_descale, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, H_kv, Sq,
+                                           Skv, D, layout, out_dtype, int(bool(causal)),
+                                           float(scale), float(q_descale), float(k_descale),
+                                           float(v_descale), _stream(stream))
 
 
 def attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H, H_kv, D,
@@ -308,4 +320,43 @@ def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *, max_
     _check(attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H,
                        H_kv, D, T, max_extend_len, page_size, num_pages, page_table.shape[1],
                        code, scale, stream), "attn_extend")
+    return o
+
+
+def prefill_fp8(q, k, v, descales, *, causal=False, scale=None, layout="BHSD",
+                out_dtype=None, out=None, stream=None):
+    """FP8 prefill: q, k, v are torch.float8_e4m3fn GPU tensors (shapes as in
+    ``prefill``), descales = (q_descale, k_descale, v_descale) per tensor.
+    O is fp16 by default, or out_dtype / out's dtype (fp16, bf16, fp32)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError("q, k, v must be torch.float8_e4m3fn")
+    if layout == "BHSD":
+        B, H, Sq, D = q.shape
+        H_kv, Skv = k.shape[1], k.shape[2]
+        kv_shape = (B, H_kv, Skv, D)
+    else:
+        B, Sq, H, D = q.shape
+        Skv, H_kv = k.shape[1], k.shape[2]
+        kv_shape = (B, Skv, H_kv, D)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"k and v must have shape {kv_shape}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    odt = out.dtype if out is not None else (out_dtype or torch.float16)
+    codes = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16,
+             torch.float32: ATTN_F16 | ATTN_OUT_F32}
+    if odt not in codes:
+        raise TypeError("the output dtype must be float16, bfloat16 or float32")
+    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
+    if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped like q")
+    qd, kd, vd = descales
+    _check(attn_prefill_fp8(q, k, v, o, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], codes[odt],
+                            causal, scale, qd, kd, vd, stream), "attn_prefill_fp8")
     return o

@@ -138,11 +138,67 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B
     a.k_sb = (int64_t)Skv * H_kv * D; a.k_sh = D; a.k_ss = H_kv * D;
   }
   a.c = exp2_multiplier(scale);
+  a.o_scale = 1.f;
   a.causal_off = Skv - Sq;
   a.k_cache = a.v_cache = nullptr;
   a.page_table = a.prefix_lens = a.qo_start = nullptr;
   a.max_pages = a.num_pages = a.total_tokens = 0;
   hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, int B, int H,
+                     int H_kv, int Sq, int Skv, int D, int layout, int out_dtype, int causal,
+                     float scale, float q_descale, float k_descale, float v_descale,
+                     hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
+  bool out_bf16, out_f32;
+  if (!parse_dtype(out_dtype, &out_bf16, &out_f32)) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!isfinite(d) || d < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * Sq == 0) return ATTN_OK;
+  if (!q || !o) return ATTN_E_INVALID;
+  if (Skv > 0 && (!k || !v)) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(o) || (Skv > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_E_INVALID;
+  const int64_t q_row = layout == ATTN_BHSD ? D : (int64_t)H * D;
+  const int64_t kv_row = layout == ATTN_BHSD ? D : (int64_t)H_kv * D;
+  if ((int64_t)Sq * q_row * 4 >= ((int64_t)1 << 31) || (int64_t)Skv * kv_row >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);  // e4m3fn bytes; the kernel addresses them bytewise
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.group = H / H_kv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.n_mtiles = 0;
+  a.total_tiles = 0;
+  if (layout == ATTN_BHSD) {
+    a.q_sb = (int64_t)H * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)H_kv * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
+  } else {
+    a.q_sb = (int64_t)Sq * H * D; a.q_sh = D; a.q_ss = H * D;
+    a.k_sb = (int64_t)Skv * H_kv * D; a.k_sh = D; a.k_ss = H_kv * D;
+  }
+  // The q and k descales multiply every score: fold them into the exponent
+  // multiplier; the v descale multiplies O.
+  a.c = exp2_multiplier(scale * q_descale * k_descale);
+  a.o_scale = v_descale;
+  a.causal_off = Skv - Sq;
+  a.k_cache = a.v_cache = nullptr;
+  a.page_table = a.prefix_lens = a.qo_start = nullptr;
+  a.max_pages = a.num_pages = a.total_tokens = 0;
+  hipError_t e = launch_prefill_fp8(D, out_bf16, causal != 0, out_f32, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -190,6 +246,7 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
   a.q_sb = 0; a.q_sh = D; a.q_ss = H * D;          // [T, H, D]
   a.k_sb = 0; a.k_sh = D; a.k_ss = H_kv * D;       // [T, H_kv, D]
   a.c = exp2_multiplier(scale);
+  a.o_scale = 1.f;
   a.k_cache = static_cast<const uint16_t*>(k_cache);
   a.v_cache = static_cast<const uint16_t*>(v_cache);
   a.page_table = page_table;

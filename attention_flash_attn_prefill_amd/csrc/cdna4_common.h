@@ -79,6 +79,34 @@ __device__ __forceinline__ int swz(int row) {
   else return row & 7;
 }
 
+// XOR swizzle of the 16-byte chunk index within an LDS row of D fp8 bytes
+// (8 chunks for D = 128, 4 for D = 64): the 16 lanes of a 128-bit read pass
+// (rows r .. r+15 at one logical chunk) land on 16 distinct 16-byte bank
+// groups.
+template <int D>
+__device__ __forceinline__ int swz_fp8(int row) {
+  if constexpr (D == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// S^T block += K (fp8, 32 x 64) * Q^T (fp8, 64 x 32) on the gfx950 fp8 MFMA
+// (e4m3fn operands, unit E8M0 scales).  Lane l holds 32 consecutive head
+// dims of row / column l % 32; both operands use the same split of the 64.
+__device__ __forceinline__ f32x16 mfma_qk_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  constexpr int kUnitScale = 127;  // E8M0 exponent code of 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0,
+                                                          kUnitScale);
+}
+
+// Four e4m3fn bytes -> two packed fp16x2 (exact: every e4m3fn value is an fp16).
+__device__ __forceinline__ u32x2 fp8x4_to_f16x4(uint32_t w) {
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // s_waitcnt that waits until at most N vector-memory operations are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -20,7 +20,8 @@ struct PrefillArgs {
   int q_ss;            // element stride between query rows
   int64_t k_sb, k_sh;  // element strides of k and v (per batch, per KV head)
   int k_ss;
-  float c;             // scale * log2(e)
+  float c;             // scale * log2(e) (fp8: times the q and k descales)
+  float o_scale;       // factor on O (fp8: the v descale; else 1)
   int causal_off;      // Skv - Sq (bottom-right causal alignment)
   // Extend kernels only: the new tokens of sequence b are rows qo_start[b] ..
   // qo_start[b+1]-1 of q, k, v, o (token-major, Sq = max_extend_len bounds
@@ -36,6 +37,10 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
                           int B, hipStream_t s);
+// FP8 (e4m3fn) q, k, v: Q.K^T on the fp8 MFMA, V widened to fp16 on staging;
+// O in fp16 (out_bf16 = false), bf16 or fp32.  Strides are in elements (bytes).
+hipError_t launch_prefill_fp8(int D, bool out_bf16, bool causal, bool out_f32,
+                              const PrefillArgs& a, int B, hipStream_t s);
 // Extend attention (causal over a paged prefix followed by the new tokens).
 hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
                          hipStream_t s);

@@ -81,14 +81,19 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // OF32: O is stored in fp32 instead of the input type.  EXT (with CAUSAL):
 // extend attention -- a sequence's keys are its cached prefix, read through
 // the page table, followed by its new tokens (PrefillArgs, extend fields).
-template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false>
+// FP8: q, k, v are e4m3fn bytes; Q.K^T runs on the fp8 MFMA (32x32x64), V is
+// widened to fp16 on staging, and BF16 then selects only the output type.
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false,
+          bool FP8 = false>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(!(EXT && FP8), "extend takes fp16/bf16");
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;
-  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int EB = FP8 ? 1 : 2;         // bytes per q/k/v element
+  constexpr int CPR = D * EB / 16;        // 16-byte chunks per K/V row
   constexpr int LOADS = BN * CPR / NT;    // chunk loads per thread per K (or V) tile
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly over the threads");
   static_assert(BN % 32 == 0 && 2 * 2 * BN * D * 2 <= 160 * 1024, "tile shape");
@@ -142,10 +147,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     q_base = (int64_t)r0 * a.q_ss + h * a.q_sh;
     kv_base = (int64_t)r0 * a.k_ss + hk * a.k_sh;
   }
-  const uint16_t* __restrict__ qp = a.q + q_base;
+  const char* __restrict__ qp = reinterpret_cast<const char*>(a.q) + q_base * EB;
   const int64_t o_base = q_base;
-  const uint16_t* __restrict__ kp = a.k + kv_base;
-  const uint16_t* __restrict__ vp = a.v + kv_base;
+  const char* __restrict__ kp = reinterpret_cast<const char*>(a.k) + kv_base * EB;
+  const char* __restrict__ vp = reinterpret_cast<const char*>(a.v) + kv_base * EB;
 
   const int m0 = mt * BM;
   if (EXT && m0 >= Sq) return;  // past this sequence's new tokens (workgroup-uniform)
@@ -153,12 +158,29 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const int qi = q0 + li;
   const bool q_ok = qi < Sq;
 
-  // Q^T fragments (B operand): lane holds Q[qi][16s + 8hi .. +7].
-  u32x4 qf[D / 16];
+  // Q^T fragments (B operand): lane holds Q[qi][16s + 8hi .. +7] (16-bit), or
+  // Q[qi][64s + 32hi .. +31] (fp8).
+  constexpr int QF = FP8 ? 1 : D / 16;
+  constexpr int QF8 = FP8 ? D / 64 : 1;
+  u32x4 qf[QF];
+  i32x8 qf8[QF8];
+  const char* qrow = qp + (int64_t)qi * a.q_ss * EB;
+  if constexpr (FP8) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + qi * a.q_ss + 16 * s + 8 * hi)
-                 : (u32x4){0u, 0u, 0u, 0u};
+    for (int s = 0; s < QF8; ++s) {
+      const u32x4 lo = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi)
+                            : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 up = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi + 16)
+                            : (u32x4){0u, 0u, 0u, 0u};
+      qf8[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < QF; ++s)
+      qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 2 * (16 * s + 8 * hi))
+                   : (u32x4){0u, 0u, 0u, 0u};
+  }
 
   // Keys this workgroup needs: [0, kv_end).
   int kv_end = Skv;
@@ -180,14 +202,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   for (int i = 0; i < LOADS; ++i) {
     const int chunk = (wave * LOADS + i) * 64 + lane;
     const int row = chunk / CPR, pos = chunk % CPR;
-    g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
+    if constexpr (FP8)
+      g_off[i] = row * a.k_ss + (pos ^ swz_fp8<D>(row)) * 16;
+    else
+      g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
   }
-  const uint32_t row_bytes = (uint32_t)a.k_ss * 2u;
+  const uint32_t row_bytes = (uint32_t)a.k_ss * EB;
   const int n_rows = EXT ? Sq : Skv;  // rows of k, v (the new tokens, for extend)
 
-  auto tile_rsrc = [&](const uint16_t* base, int kv0) {
+  auto tile_rsrc = [&](const char* base, int kv0) {
     const uint32_t rows = (uint32_t)max(0, n_rows - kv0);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss), (short)0,
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss * EB), (short)0,
                                              (int)(rows * row_bytes), kBufferConfig);
   };
 
@@ -270,16 +295,35 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     for (int i = 0; i < LOADS; ++i) {
       const auto r = pre ? page_rsrc(a.v_cache, t, i) : rv;
       const int off = pre ? pg_off[i] : g_off[i];
-      if constexpr (BF16)
+      if constexpr (BF16 || FP8)
         vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
                                                  16, off, 0, 0, 0);
     }
   };
-  // bf16 only: convert the staged V chunks to fp16 and write them to LDS.
+  // fp8: widen the staged V chunk (16 e4m3fn values of row r, logical chunk
+  // c) to fp16 and write its two fp16 chunks 2c, 2c+1 of row r to LDS.
+  // bf16: convert the staged V chunks to fp16 and write them to LDS.
   auto store_v = [&](LDS_AS uint16_t* v_dst) {
-    if constexpr (BF16) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int chunk = (wave * LOADS + i) * 64 + lane;
+        const int row = chunk / CPR, c = (chunk % CPR) ^ swz_fp8<D>(row);
+        u32x4 w[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 h = fp8x4_to_f16x4(vreg[i][j]);
+          w[j >> 1][2 * (j & 1)] = h[0];
+          w[j >> 1][2 * (j & 1) + 1] = h[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          *reinterpret_cast<LDS_AS u32x4*>(v_dst + row * D + (((2 * c + u) ^ swz<D>(row)) * 8)) =
+              w[u];
+      }
+    } else if constexpr (BF16) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int base = (wave * LOADS + i) * 64 * 8 + lane * 8;
@@ -293,9 +337,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 
   // ---- LDS read offsets (halves, loop invariant).
   // K (A operand of S^T): lane reads row 32jb + li, logical chunk 2s + hi.
-  int k_rd[D / 16];
+  // fp8: lane reads row 32jb + li, logical chunks 4s + 2hi and +1 (halves
+  // offsets into rows of D bytes).
+  int k_rd[FP8 ? 2 * (D / 64) : D / 16];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
+    for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        k_rd[2 * s + u] = (li * D + (((4 * s + 2 * hi + u) ^ swz_fp8<D>(li)) * 16)) / 2;
+  } else {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
+  }
   // V (transposing reads): lane (group g = lane/16, r, c) names 4 halves of
   // key 16s + 8half + 4hi + r at d = 32db + 16(g & 1) + 4c.
   const int g16 = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
@@ -321,6 +375,27 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // S^T = K Q^T for one tile: one 32-key accumulator chain per 32 keys,
   // interleaved.
   auto qk = [&](const LDS_AS uint16_t* ks, f32x16 (&sc)[BN / 32]) {
+    if constexpr (FP8) {
+      // Rows of D bytes: block jb starts at byte 32 jb D.
+      i32x8 kf8[D / 64][BN / 32];
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb) {
+          const u32x4 lo = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s]);
+          const u32x4 up = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s + 1]);
+          kf8[s][jb] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk_fp8(kf8[s][jb], qf8[s], sc[jb]);
+      return;
+    }
     // All K fragments are read before the first MFMA (the fence keeps the
     // scheduler from recycling two registers and exposing an LDS round trip
     // per MFMA pair).
@@ -479,7 +554,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
   const float l_tot = pair_sum(l_run);
   // A rejected prefix page makes the rows NaN (the key set is unknown).
-  const float inv = bad_page ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
+  const float inv =
+      bad_page ? __builtin_nanf("") : (l_tot > 0.f ? a.o_scale / l_tot : 0.f);
   if (q_ok) {
     const int64_t row = o_base + (int64_t)qi * a.q_ss;
 #pragma unroll
@@ -507,14 +583,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false>
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false,
+          bool FP8 = false>
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
   const int64_t n_mtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t total = (int64_t)B * a.H * n_mtiles;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;
   a.total_tiles = (int)total;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN, EXT>),
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN, EXT, FP8>),
                      dim3(a.total_tiles), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
@@ -563,6 +640,30 @@ hipError_t launch_ext_d(bool bf16, bool out_f32, const PrefillArgs& a, int B, hi
                  : launch_t<D, false, true, false, NW, BN, true>(a, B, s);
 }
 }  // namespace
+
+namespace {
+template <int D, bool CAUSAL>
+hipError_t launch_fp8_c(bool out_bf16, bool out_f32, const PrefillArgs& a, int B, hipStream_t s) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int BN = 64;
+  if (out_f32) return launch_t<D, false, CAUSAL, true, NW, BN, false, true>(a, B, s);
+  return out_bf16 ? launch_t<D, true, CAUSAL, false, NW, BN, false, true>(a, B, s)
+                  : launch_t<D, false, CAUSAL, false, NW, BN, false, true>(a, B, s);
+}
+template <int D>
+hipError_t launch_fp8_d(bool out_bf16, bool causal, bool out_f32, const PrefillArgs& a, int B,
+                        hipStream_t s) {
+  return causal ? launch_fp8_c<D, true>(out_bf16, out_f32, a, B, s)
+                : launch_fp8_c<D, false>(out_bf16, out_f32, a, B, s);
+}
+}  // namespace
+
+hipError_t launch_prefill_fp8(int D, bool out_bf16, bool causal, bool out_f32,
+                              const PrefillArgs& a, int B, hipStream_t s) {
+  if (D == 128) return launch_fp8_d<128>(out_bf16, causal, out_f32, a, B, s);
+  if (D == 64) return launch_fp8_d<64>(out_bf16, causal, out_f32, a, B, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
                          hipStream_t s) {

@@ -106,6 +106,28 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o,
                      int causal, float scale, hipStream_t stream);
 
 /*
+ * FP8 prefill: attn_prefill_gqa with q, k, v in OCP e4m3fn (one byte per
+ * element, same shapes and layouts) and per-tensor descales: the inputs are
+ * q_descale * Q, k_descale * K, v_descale * V.  (FP8 flash attention is a
+ * roadmap item of "Wave February 2025 Release"; e4m3fn with per-tensor
+ * scales is the format of the fp8 kernels in "[FlyDSL] FP8 MQA logits
+ * improvements for gfx950".)
+ *
+ *   out_dtype: ATTN_F16 or ATTN_BF16 -- the type of o -- optionally OR-ed
+ *              with ATTN_OUT_F32 (o in fp32)
+ *   descales: finite and >= 0 (else ATTN_E_INVALID)
+ *
+ * Arithmetic: Q.K^T on the gfx950 fp8 MFMA (exact products, fp32
+ * accumulation) with scale * q_descale * k_descale * log2(e) folded in fp32
+ * into the exponent; P rounded to fp16 and P.V on fp16 MFMA with V widened
+ * e4m3fn -> fp16 (exact) on staging; O = v_descale * (P.V) / l.
+ */
+int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int out_dtype,
+                     int causal, float scale, float q_descale, float k_descale, float v_descale,
+                     hipStream_t stream);
+
+/*
  * Extend attention: prefill of new tokens after a cached prefix (chunked
  * prefill; the "extend" call of an LLM serving backend: "WAVE: A Symbolic
  * Python DSL and Compiler for High Performance Machine Learning (MLSys 2026)",

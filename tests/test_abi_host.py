@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
                             "attn_paged_decode_workspace_size", "attn_paged_decode_num_splits",
                             "attn_prefill_gqa", "attn_paged_decode_gqa",
                             "attn_paged_decode_gqa_workspace_size",
-                            "attn_paged_decode_gqa_num_splits", "attn_extend"])
+                            "attn_paged_decode_gqa_num_splits", "attn_extend",
+                            "attn_prefill_fp8"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -241,3 +242,29 @@ def test_extend_empty_is_a_noop():
     assert _extend(B=0, q=None, k=None, v=None, o=None, qo_start=None) == attn.ATTN_OK
     assert _extend(max_extend_len=0) == attn.ATTN_OK
     assert _extend(total_tokens=0) == attn.ATTN_OK
+
+
+def _prefill_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=4, H_kv=2, Sq=16, Skv=16, D=128, layout=0,
+             out_dtype=0, causal=0, scale=0.1, q_descale=0.01, k_descale=0.01, v_descale=0.01,
+             stream=0)
+    a.update(kw)
+    return attn.attn_prefill_fp8(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_descale=float("nan")), attn.ATTN_E_INVALID),
+    (dict(v_descale=-1.0), attn.ATTN_E_INVALID),
+    (dict(k_descale=float("inf")), attn.ATTN_E_INVALID),
+    (dict(out_dtype=2), attn.ATTN_E_INVALID),
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(D=256), attn.ATTN_E_UNSUPPORTED),
+    (dict(layout=3), attn.ATTN_E_INVALID),
+    (dict(k=FAKE + 1), attn.ATTN_E_INVALID),
+])
+def test_prefill_fp8_validation(kw, status):
+    assert _prefill_fp8(**kw) == status
+
+
+def test_prefill_fp8_empty_is_a_noop():
+    assert _prefill_fp8(Sq=0, q=None, o=None) == attn.ATTN_OK
