@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -10,8 +10,9 @@ Sq=Skv=4096 D=128 fp16 BHSD non-causal, with inputs resident in HBM.  The
 headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
 step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
-multi-query paged decode, extend after a paged prefix) are measured the same
-way and reported under "extra", decode in GB/s of algorithmic K/V bytes.
+multi-query paged decode, extend after a paged prefix, fp8 prefill) are
+measured the same way and reported under "extra", decode in GB/s of
+algorithmic K/V bytes.
 
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
 run on, bracketed by torch.cuda.synchronize(); HIP events around every step
@@ -36,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16 = 2516.6   # TFLOP/s, MI355X dense fp16/bf16
+PEAK_MFMA_FP8 = 5033.2   # TFLOP/s, MI355X dense fp8
 PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 PREFILL_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode.hip")
@@ -212,12 +214,19 @@ def bench_prefill(attn, cfg, steps, warmup, clock):
     import workloads
     q, k, v, m = workloads.prefill_config(cfg)
     q, k, v = q.cuda(), k.cuda(), v.cuda()
-    o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    if m["dtype"] == "fp8":
+        o = torch.empty(q.shape, dtype=torch.float16, device="cuda")
 
-    def step():
-        attn.prefill(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"], out=o,
-                     stream=stream)
+        def step():
+            attn.prefill_fp8(q, k, v, m["descales"], causal=m["causal"], scale=m["scale"],
+                             layout=m["layout"], out=o, stream=stream)
+    else:
+        o = torch.empty_like(q)
+
+        def step():
+            attn.prefill(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"],
+                         out=o, stream=stream)
 
     t = measure(step, steps, warmup, stream, clock)
     if m["Sq"] * m["Skv"] <= 128 * 128:  # launch-bound: also time it from a HIP graph
@@ -234,8 +243,11 @@ def bench_prefill(attn, cfg, steps, warmup, clock):
                "Sq": m["Sq"], "Skv": m["Skv"],
                "D": m["D"], "layout": m["layout"], "causal": m["causal"], "dtype": m["dtype"]}
     traffic = load_traffic(f"prefill_fwd__{m['name']}", PREFILL_SRC)
-    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": traffic}
+    # fp8: the Q.K^T half of the flops runs on the fp8 MFMA (5.0 PFLOP/s), the
+    # P.V half on fp16 (2.5): the peak for the mix is their harmonic blend.
+    peak = PEAK_MFMA_F16 if m["dtype"] != "fp8" else 2.0 / (1.0 / PEAK_MFMA_FP8 + 1.0 / PEAK_MFMA_F16)
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1),
+            "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
     del q, k, v, o
     torch.cuda.empty_cache()
     return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof,
@@ -413,7 +425,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
