@@ -22,7 +22,9 @@ head h reads KV head h // (H / H_kv).  Extend attention (new tokens after a
 cached prefix) is causal attention over the prefix gathered through the page
 table followed by the new tokens, bottom-right aligned.  FP8 attention is
 the same function of the dequantised inputs (e4m3fn code x per-tensor
-descale).
+descale).  The backward pass is the gradient of sum(O * dO) by the chain rule
+(``sdpa_backward``; ``sdpa_backward_dq_rows`` and ``sdpa_backward_kv_rows``
+form selected rows of it at full size); ``lse_rows`` is each row's log-sum-exp.
 
 Pinned by ``tests/test_oracle.py`` (brute force at 50 digits, the torch
 library routine, closed forms, invariants) and
@@ -35,6 +37,10 @@ from .attention import (  # noqa: F401
     extend,
     gather_sequence,
     kv_head,
+    lse_rows,
+    sdpa_backward,
+    sdpa_backward_dq_rows,
+    sdpa_backward_kv_rows,
     n_visible,
     paged_decode,
     sdpa,

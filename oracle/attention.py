@@ -221,3 +221,135 @@ def dequantize_fp8(codes, descale: float) -> np.ndarray:
     """float64 values of e4m3fn codes (a torch.float8_e4m3fn tensor) times the
     per-tensor descale: the inputs an fp8 attention computes with."""
     return codes.detach().to("cpu").to(torch.float64).numpy() * float(descale)
+
+
+def lse_rows(q, k, *, causal: bool, scale: float | None = None, layout: str = "BHSD") -> np.ndarray:
+    """Natural log-sum-exp of each query row's scaled, masked logits [B, H, Sq]
+    (-inf for a row with no visible key): log sum_j exp(scale <q_i, k_j> + M_ij)."""
+    qf, kf = (_bhsd(to_f64(t), layout) for t in (q, k))
+    B, H, Sq, D = qf.shape
+    H_kv, Skv = kf.shape[1], kf.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    mask = np.arange(Skv)[None, :] < vis[:, None]
+    out = np.full((B, H, Sq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            logits = np.where(mask, scale * (qf[b, h] @ kf[b, kv_head(h, H, H_kv)].T), -np.inf)
+            m = logits.max(axis=1) if Skv else np.full(Sq, -np.inf)
+            ok = np.isfinite(m)
+            out[b, h, ok] = m[ok] + np.log(np.exp(logits[ok] - m[ok, None]).sum(axis=1))
+    return out
+
+
+def sdpa_backward(q, k, v, do, *, causal: bool, scale: float | None = None,
+                  layout: str = "BHSD"):
+    """Gradients (dq, dk, dv) of L = sum(O * dO) for O = sdpa(q, k, v), float64,
+    in the inputs' layout, from the chain rule written out:
+        P = softmax rows,   dV_j = sum_i P_ij dO_i,   dP_ij = <dO_i, V_j>,
+        dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+        dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
+    Grouped heads: dK and dV of a KV head sum over the query heads sharing it."""
+    qf, kf, vf, gf = (_bhsd(to_f64(t), layout) for t in (q, k, v, do))
+    B, H, Sq, D = qf.shape
+    H_kv, Skv = kf.shape[1], kf.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    dq = np.zeros_like(qf)
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            P = attention_probs(qf[b, h], kf[b, g], scale, vis)       # [Sq, Skv]
+            dv[b, g] += P.T @ gf[b, h]
+            dP = gf[b, h] @ vf[b, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[b, h] = scale * (dS @ kf[b, g])
+            dk[b, g] += scale * (dS.T @ qf[b, h])
+    return _bhsd(dq, layout), _bhsd(dk, layout), _bhsd(dv, layout)
+
+
+def _head_getter(layout: str):
+    if layout == "BHSD":
+        return lambda t, b, h: t[b, h]
+    if layout == "BSHD":
+        return lambda t, b, h: t[b, :, h]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def sdpa_backward_dq_rows(q, k, v, do, rows, *, causal: bool, scale: float | None = None,
+                          layout: str = "BHSD") -> np.ndarray:
+    """dQ [len(rows), D] at selected query rows ``(b, h, i)``, each exactly as
+    ``sdpa_backward`` forms it: the row's P and dP_ij = <dO_i, V_j> over all
+    keys, dS_ij = P_ij (dP_ij - sum_l P_il dP_il), dQ_i = scale sum_j dS_ij K_j.
+    For full problem sizes, where the whole gradient is too costly here."""
+    head = _head_getter(layout)
+    B, H, Sq, D = _bhsd_shape(q, layout)
+    H_kv, Skv = _bhsd_shape(k, layout)[1:3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    groups: dict = {}
+    for n, (b, h, i) in enumerate(rows):
+        groups.setdefault((int(b), int(h)), []).append((n, int(i)))
+    for (b, h), items in groups.items():
+        g = kv_head(h, H, H_kv)
+        kf, vf = to_f64(head(k, b, g)), to_f64(head(v, b, g))
+        idx = torch.as_tensor([i for _, i in items])
+        qr = to_f64(head(q, b, h)[idx])
+        dor = to_f64(head(do, b, h)[idx])
+        P = attention_probs(qr, kf, scale, vis[idx.numpy()])
+        dP = dor @ vf.T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        for (n, _), r in zip(items, scale * (dS @ kf)):
+            out[n] = r
+    return out
+
+
+def sdpa_backward_kv_rows(q, k, v, do, keys, *, causal: bool, scale: float | None = None,
+                          layout: str = "BHSD"):
+    """(dK, dV), each [len(keys), D], at selected keys ``(b, g, j)`` of KV head
+    g, exactly as ``sdpa_backward`` forms them: sums over every query row of
+    every query head sharing KV head g of dV_j = P_ij dO_i and
+    dK_j = scale dS_ij Q_i.  For full problem sizes."""
+    head = _head_getter(layout)
+    B, H, Sq, D = _bhsd_shape(q, layout)
+    H_kv, Skv = _bhsd_shape(k, layout)[1:3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    vis = n_visible(Sq, Skv, causal)
+    dk = np.zeros((len(keys), D), dtype=np.float64)
+    dv = np.zeros((len(keys), D), dtype=np.float64)
+    groups: dict = {}
+    for n, (b, g, j) in enumerate(keys):
+        groups.setdefault((int(b), int(g)), []).append((n, int(j)))
+    for (b, g), items in groups.items():
+        kf, vf = to_f64(head(k, b, g)), to_f64(head(v, b, g))
+        js = np.array([j for _, j in items])
+        for h in range(H):
+            if kv_head(h, H, H_kv) != g:
+                continue
+            qf, dof = to_f64(head(q, b, h)), to_f64(head(do, b, h))
+            P = attention_probs(qf, kf, scale, vis)                   # [Sq, Skv]
+            dP = dof @ vf.T
+            delta = (P * dP).sum(axis=1, keepdims=True)
+            dS = P[:, js] * (dP[:, js] - delta)
+            del dP
+            for t, (n, _) in enumerate(items):
+                dv[n] += P[:, js[t]] @ dof
+                dk[n] += scale * (dS[:, t] @ qf)
+    return dk, dv
+
+
+def _bhsd_shape(t, layout: str) -> tuple:
+    """(B, heads, S, D) of a BHSD or BSHD tensor."""
+    if layout == "BHSD":
+        return tuple(t.shape)
+    if layout == "BSHD":
+        B, S, H, D = t.shape
+        return (B, H, S, D)
+    raise ValueError(f"unknown layout {layout!r}")

@@ -519,6 +519,98 @@ def check_fp8_quantize_round_trip():
     _close(got, ref, 1e-12, "fp8 dequantised attention")
 
 
+# ------------------------------------------------------------------ backward
+
+BWD_CASES = [  # (B, H, H_kv, Sq, Skv, D, causal, layout)
+    (1, 2, 2, 7, 9, 8, False, "BHSD"),
+    (2, 4, 2, 10, 10, 8, True, "BSHD"),
+    (1, 3, 1, 6, 11, 4, True, "BHSD"),
+]
+
+
+def _autograd(q, k, v, do, causal, scale, layout):
+    qt, kt, vt = ((t.transpose(1, 2) if layout == "BSHD" else t).to(F64).clone().requires_grad_()
+                  for t in (q, k, v))
+    Sq, Skv = qt.shape[2], kt.shape[2]
+    mask = torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq) if causal else None
+    out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=True)
+    dot = (do.transpose(1, 2) if layout == "BSHD" else do).to(F64)
+    out.backward(dot)
+    grads = [t.grad for t in (qt, kt, vt)]
+    return [(g.transpose(1, 2) if layout == "BSHD" else g).numpy() for g in grads]
+
+
+def check_backward_autograd():
+    for n, (B, H, Hk, Sq, Skv, D, causal, layout) in enumerate(BWD_CASES):
+        q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "bf16", layout, seed=800 + n, h_kv=Hk)
+        do = workloads.prefill_inputs(B, H, Sq, Sq, D, "bf16", layout, seed=850 + n)[0]
+        got = oracle.sdpa_backward(q, k, v, do, causal=causal, scale=0.4, layout=layout)
+        ref = _autograd(q, k, v, do, causal, 0.4, layout)
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            _close(a, b, 1e-11, f"backward case {n} {name}")
+
+
+def check_backward_finite_differences():
+    """Central differences of sum(sdpa(q, k, v) * dO) on a tiny case."""
+    q, k, v = (t.double() for t in workloads.prefill_inputs(1, 2, 3, 4, 3, "f16", seed=860, h_kv=1))
+    do = workloads.prefill_inputs(1, 2, 3, 3, 3, "f16", seed=861)[0].double()
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, do, causal=True, scale=0.7)
+    L = lambda q_, k_, v_: float((oracle.sdpa(q_, k_, v_, causal=True, scale=0.7) * do.numpy()).sum())
+    h = 1e-6
+    for name, t, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(*t.shape):
+            tp, tm = t.clone(), t.clone()
+            tp[idx] += h
+            tm[idx] -= h
+            args_p = {"q": (tp, k, v), "k": (q, tp, v), "v": (q, k, tp)}[name]
+            args_m = {"q": (tm, k, v), "k": (q, tm, v), "v": (q, k, tm)}[name]
+            fd = (L(*args_p) - L(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def check_backward_closed_forms():
+    """Softmax is invariant to a shift shared by all keys, so sum_j dK_j = 0 per
+    KV head; and rows of P sum to 1, so sum_j dV_j = the sum of dO over the
+    group's query rows."""
+    B, H, Hk, Sq, Skv, D = 2, 4, 2, 9, 13, 8
+    q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "f16", seed=870, h_kv=Hk)
+    do = workloads.prefill_inputs(B, H, Sq, Sq, D, "f16", seed=871)[0]
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, do, causal=False)
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+    dos = do.double().numpy().reshape(B, Hk, H // Hk, Sq, D).sum(axis=(2, 3))
+    _close(dv.sum(axis=2), dos, 1e-13, "sum of dV")
+
+
+def check_backward_sampled_rows_autograd():
+    """dQ at selected query rows and dK, dV at selected keys match autograd's
+    full gradients (grouped heads, both layouts, causal with Sq != Skv)."""
+    for n, (B, H, Hk, Sq, Skv, D, causal, layout) in enumerate(BWD_CASES):
+        q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "bf16", layout, seed=890 + n, h_kv=Hk)
+        do = workloads.prefill_inputs(B, H, Sq, Sq, D, "bf16", layout, seed=895 + n)[0]
+        rdq, rdk, rdv = _autograd(q, k, v, do, causal, 0.4, layout)
+        if layout == "BSHD":
+            rdq, rdk, rdv = (x.transpose(0, 2, 1, 3) for x in (rdq, rdk, rdv))
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in (0, Sq // 2, Sq - 1)]
+        keys = [(b, g, j) for b in range(B) for g in range(Hk) for j in (0, Skv // 3, Skv - 1)]
+        got = oracle.sdpa_backward_dq_rows(q, k, v, do, rows, causal=causal, scale=0.4,
+                                           layout=layout)
+        _close(got, np.stack([rdq[b, h, i] for b, h, i in rows]), 1e-11, f"dq rows case {n}")
+        gk, gv = oracle.sdpa_backward_kv_rows(q, k, v, do, keys, causal=causal, scale=0.4,
+                                              layout=layout)
+        _close(gk, np.stack([rdk[b, g, j] for b, g, j in keys]), 1e-11, f"dk rows case {n}")
+        _close(gv, np.stack([rdv[b, g, j] for b, g, j in keys]), 1e-11, f"dv rows case {n}")
+
+
+def check_lse_rows():
+    B, H, Hk, Sq, Skv, D = 1, 2, 1, 6, 9, 8
+    q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "f16", seed=880, h_kv=Hk)
+    got = oracle.lse_rows(q, k, causal=True, scale=0.5)
+    logits = 0.5 * (q.double() @ k.double().transpose(-1, -2))               # [1, 2, Sq, Skv]
+    mask = torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq)
+    ref = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1).numpy()
+    _close(got, ref, 1e-13, "lse rows")
+
+
 ALL_CHECKS = [
     check_bruteforce, check_library_sdpa, check_rows_match_full, check_ones_v, check_causal_row0,
     check_zero_keys, check_two_keys, check_dominant_key, check_zero_scale,
@@ -527,5 +619,6 @@ ALL_CHECKS = [
     check_decode_nan_poison, check_gqa_library, check_gqa_group_locality,
     check_gqa_rows_and_decode, check_extend_library, check_extend_without_prefix_is_causal_prefill,
     check_extend_one_token_is_decode, check_extend_chunking, check_fp8_decode,
-    check_fp8_quantize_round_trip,
+    check_fp8_quantize_round_trip, check_backward_autograd, check_backward_finite_differences,
+    check_backward_closed_forms, check_backward_sampled_rows_autograd, check_lse_rows,
 ]

@@ -92,6 +92,61 @@ def _extend_top_left(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_star
 
 _real_extend = oa.extend
 
+
+def _bwd_without_delta(q, k, v, do, *, causal, scale=None, layout="BHSD"):
+    """dS = P * dP (the row term sum_l P dP dropped)."""
+    real = oa.attention_probs
+    qf, kf, vf, gf = (oa._bhsd(oa.to_f64(t), layout) for t in (q, k, v, do))
+    B, H, Sq, D = qf.shape
+    H_kv, Skv = kf.shape[1], kf.shape[2]
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    vis = oa.n_visible(Sq, Skv, causal)
+    dq, dk, dv = np.zeros_like(qf), np.zeros_like(kf), np.zeros_like(vf)
+    for b in range(B):
+        for h in range(H):
+            g = oa.kv_head(h, H, H_kv)
+            P = real(qf[b, h], kf[b, g], scale, vis)
+            dv[b, g] += P.T @ gf[b, h]
+            dS = P * (gf[b, h] @ vf[b, g].T)
+            dq[b, h] = scale * (dS @ kf[b, g])
+            dk[b, g] += scale * (dS.T @ qf[b, h])
+    return oa._bhsd(dq, layout), oa._bhsd(dk, layout), oa._bhsd(dv, layout)
+
+
+def _bwd_unscaled(q, k, v, do, *, causal, scale=None, layout="BHSD"):
+    """dQ and dK without the softmax scale."""
+    dq, dk, dv = _real_bwd(q, k, v, do, causal=causal, scale=scale, layout=layout)
+    D = dq.shape[-1]
+    s = 1.0 / np.sqrt(D) if scale is None else scale
+    return dq / s, dk / s, dv
+
+
+_real_bwd = oa.sdpa_backward
+_real_dq_rows = oa.sdpa_backward_dq_rows
+_real_kv_rows = oa.sdpa_backward_kv_rows
+
+
+def _dq_rows_unscaled(q, k, v, do, rows, *, causal, scale=None, layout="BHSD"):
+    """Sampled dQ without the softmax scale."""
+    D = q.shape[-1]
+    s = 1.0 / np.sqrt(D) if scale is None else scale
+    return _real_dq_rows(q, k, v, do, rows, causal=causal, scale=scale, layout=layout) / s
+
+
+def _kv_rows_first_head_only(q, k, v, do, keys, *, causal, scale=None, layout="BHSD"):
+    """Sampled dK, dV summed over the first query head of each group only (the
+    other heads' dO zeroed, which removes exactly their terms)."""
+    H_kv = k.shape[1] if layout == "BHSD" else k.shape[2]
+    H = q.shape[1] if layout == "BHSD" else q.shape[2]
+    do2 = do.clone()
+    for h in range(H):
+        if h % (H // H_kv):
+            if layout == "BHSD":
+                do2[:, h] = 0
+            else:
+                do2[:, :, h] = 0
+    return _real_kv_rows(q, k, v, do2, keys, causal=causal, scale=scale, layout=layout)
+
 MUTATIONS = [
     ("n_visible", _top_left, [pins.check_library_sdpa, pins.check_bruteforce]),
     ("n_visible", _off_by_one, [pins.check_causal_row0, pins.check_library_sdpa]),
@@ -108,6 +163,13 @@ MUTATIONS = [
                                         pins.check_extend_one_token_is_decode]),
     ("extend", _extend_top_left, [pins.check_extend_library, pins.check_extend_chunking]),
     ("gather_sequence", _gather_slot_major, [pins.check_extend_library]),
+    ("sdpa_backward", _bwd_without_delta, [pins.check_backward_autograd,
+                                           pins.check_backward_closed_forms]),
+    ("sdpa_backward", _bwd_unscaled, [pins.check_backward_autograd,
+                                      pins.check_backward_finite_differences]),
+    ("sdpa_backward_dq_rows", _dq_rows_unscaled, [pins.check_backward_sampled_rows_autograd]),
+    ("sdpa_backward_kv_rows", _kv_rows_first_head_only,
+     [pins.check_backward_sampled_rows_autograd]),
 ]
 
 

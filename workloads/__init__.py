@@ -53,6 +53,13 @@ PREFILL_CONFIGS = {
              layout="BHSD", causal=False, amp=1.0, scale=None, out_dtype="f16"),
 }
 
+# Backward workloads: the gradients of the causal 8k BSHD prefill (a training
+# step's attention), with dO drawn like the inputs.
+BACKWARD_CONFIGS = {
+    11: dict(name="bwd-causal-bshd-8k", B=2, H=32, Sq=8192, Skv=8192, D=128, dtype="bf16",
+             layout="BSHD", causal=True, amp=0.5, amp_do=1.0, scale=None),
+}
+
 # Paged decode workload.
 DECODE_CONFIGS = {
     4: dict(name="paged-decode-b64", B=64, H=32, D=128, dtype="f16", page_size=16,
@@ -103,6 +110,33 @@ def prefill_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, seed=0
     k = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
     v = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
     return q, k, v
+
+
+def backward_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, amp_do=1.0, seed=0,
+                    h_kv=None):
+    """Seeded q, k, v, dO: q, k, v exactly as ``prefill_inputs`` draws them for
+    the same seed, then dO (shaped like q, N(0,1) * amp_do) from the same
+    generator."""
+    g = torch.Generator().manual_seed(seed)
+    hk = H if h_kv is None else h_kv
+    q = _draw(layout_shape(B, H, Sq, D, layout), g, amp, dtype)
+    k = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
+    v = _draw(layout_shape(B, hk, Skv, D, layout), g, amp, dtype)
+    do = _draw(layout_shape(B, H, Sq, D, layout), g, amp_do, dtype)
+    return q, k, v, do
+
+
+def backward_config(cfg: int):
+    """(q, k, v, dO, meta) for one of the numbered backward workloads, seeded with its number."""
+    c = dict(BACKWARD_CONFIGS[cfg])
+    q, k, v, do = backward_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                  c["layout"], c["amp"], c["amp_do"], seed=cfg,
+                                  h_kv=c.get("H_kv"))
+    c.setdefault("H_kv", c["H"])
+    if c["scale"] is None:
+        c["scale"] = default_scale(c["D"])
+    c["seed"] = cfg
+    return q, k, v, do, c
 
 
 FP8_MAX = 448.0  # largest finite e4m3fn value
