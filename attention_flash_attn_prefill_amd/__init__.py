@@ -46,6 +46,11 @@ SIGNATURES = {
                               _F, _VP]),
     "attn_extend": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
                          _I, _I, _I, _F, _VP]),
+    "attn_prefill_lse": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                              _VP]),
+    "attn_prefill_bwd_workspace_size": (_SZ, [_I, _I, _I]),
+    "attn_prefill_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
+                              _I, _I, _I, _F, _VP, _SZ, _VP]),
 }
 
 _lib = None
@@ -119,6 +124,27 @@ def attn_prefill_gqa(q, k, v, o, B, H, H_kv, Sq, Skv, D, layout, dtype, causal, 
     return load_library().attn_prefill_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, H_kv, Sq,
                                            Skv, D, layout, dtype, int(bool(causal)),
                                            float(scale), _stream(stream))
+
+
+def attn_prefill_lse(q, k, v, o, lse, B, H, H_kv, Sq, Skv, D, layout, dtype, causal, scale,
+                     stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                           H_kv, Sq, Skv, D, layout, dtype, int(bool(causal)),
+                                           float(scale), _stream(stream))
+
+
+def attn_prefill_bwd_workspace_size(B, H, Sq) -> int:
+    return int(load_library().attn_prefill_bwd_workspace_size(B, H, Sq))
+
+
+def attn_prefill_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, Sq, Skv, D, layout, dtype,
+                     causal, scale, workspace, workspace_bytes, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B,
+        H, H_kv, Sq, Skv, D, layout, dtype, int(bool(causal)), float(scale), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
 
 
 def attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size) -> int:
@@ -205,24 +231,13 @@ def _out_code(q, out, out_dtype):
     raise TypeError(f"output dtype must be {q.dtype} or torch.float32, not {want}")
 
 
-def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_dtype=None,
-            stream=None):
-    """O = softmax(Q K^T * scale [+ causal mask]) V on the GPU.
-
-    q: [B,H,Sq,D] (layout "BHSD") or [B,Sq,H,D] ("BSHD"); k, v likewise with
-    Skv keys and H_kv heads (H_kv divides H: grouped-query attention, query
-    head h reads KV head h // (H // H_kv)); fp16 or bf16 GPU tensors,
-    contiguous.  Returns o like q, or in fp32 (unrounded) with
-    out_dtype=torch.float32 or an fp32 `out`.
-    """
-    import torch
+def _prefill_shapes(q, k, v, layout):
+    """(B, H, H_kv, Sq, Skv, D) of contiguous 4-D GPU tensors in `layout`."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share a dtype")
     if layout == "BHSD":
         B, H, Sq, D = q.shape
         H_kv, Skv = k.shape[1], k.shape[2]
@@ -233,15 +248,100 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_d
         kv_shape = (B, Skv, H_kv, D)
     if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
         raise ValueError(f"k and v must have shape {kv_shape}")
+    return B, H, H_kv, Sq, Skv, D
+
+
+def _like(t, ref, dtype, name):
+    """`t` checked to be a contiguous GPU tensor shaped like `ref`, or a new one."""
+    import torch
+    if t is None:
+        return torch.empty(ref.shape, dtype=dtype, device=ref.device)
+    if t.shape != ref.shape or not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor shaped like {tuple(ref.shape)}")
+    return t
+
+
+def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_dtype=None,
+            stream=None):
+    """O = softmax(Q K^T * scale [+ causal mask]) V on the GPU.
+
+    q: [B,H,Sq,D] (layout "BHSD") or [B,Sq,H,D] ("BSHD"); k, v likewise with
+    Skv keys and H_kv heads (H_kv divides H: grouped-query attention, query
+    head h reads KV head h // (H // H_kv)); fp16 or bf16 GPU tensors,
+    contiguous.  Returns o like q, or in fp32 (unrounded) with
+    out_dtype=torch.float32 or an fp32 `out`.
+    """
+    B, H, H_kv, Sq, Skv, D = _prefill_shapes(q, k, v, layout)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code, odt = _out_code(q, out, out_dtype)
-    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
-    if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
-        raise ValueError("out must be a contiguous GPU tensor shaped like q")
+    o = _like(out, q, odt, "out")
     _check(attn_prefill_gqa(q, k, v, o, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], code,
                             causal, scale, stream), "attn_prefill_gqa")
     return o
+
+
+def prefill_with_lse(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None,
+                     out_dtype=None, lse=None, stream=None):
+    """``prefill`` that also returns the natural-log log-sum-exp of every
+    query row's scaled scores: (o, lse) with lse [B, H, Sq] fp32 (-inf for a
+    row with no visible key), the statistic ``prefill_backward`` needs."""
+    import torch
+    B, H, H_kv, Sq, Skv, D = _prefill_shapes(q, k, v, layout)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code, odt = _out_code(q, out, out_dtype)
+    o = _like(out, q, odt, "out")
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_cuda
+          or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor of shape {(B, H, Sq)}")
+    _check(attn_prefill_lse(q, k, v, o, lse, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], code,
+                            causal, scale, stream), "attn_prefill_lse")
+    return o, lse
+
+
+def prefill_backward(q, k, v, o, dO, lse, *, causal=False, scale=None, layout="BHSD",
+                     grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(O * dO) for O = prefill(q, k, v) (same
+    causal, scale and layout), given O and lse from ``prefill_with_lse``.
+
+    dO is like q and in q's dtype.  The gradients are in q's dtype, or fp32
+    with grad_dtype=torch.float32 (or fp32 dq/dk/dv).  With H_kv < H the
+    query heads of a group sum into their KV head's dk, dv.  The workspace (a
+    uint8 GPU tensor of ``attn_prefill_bwd_workspace_size`` bytes) is
+    allocated here if not given.
+    """
+    import torch
+    B, H, H_kv, Sq, Skv, D = _prefill_shapes(q, k, v, layout)
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dO.dtype):
+        raise TypeError("q, k, v, o and dO must share a dtype")
+    for t, name in ((o, "o"), (dO, "dO")):
+        if t.shape != q.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped like q")
+    if (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor of shape {(B, H, Sq)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    given = next((t for t in (dq, dk, dv) if t is not None), None)
+    code, gdt = _out_code(q, given, grad_dtype)
+    dq = _like(dq, q, gdt, "dq")
+    dk = _like(dk, k, gdt, "dk")
+    dv = _like(dv, v, gdt, "dv")
+    need = attn_prefill_bwd_workspace_size(B, H, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(attn_prefill_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, Sq, Skv, D,
+                            LAYOUTS[layout], code, causal, scale, workspace,
+                            workspace.numel() * workspace.element_size(), stream),
+           "attn_prefill_bwd")
+    return dq, dk, dv
 
 
 def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=None,

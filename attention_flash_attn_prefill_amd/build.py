@@ -22,7 +22,7 @@ LIB_NAME = "libmi355attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "decode_gqa.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "decode_gqa.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

@@ -98,6 +98,13 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int B, in
 int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B, int H,
                      int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
                      float scale, hipStream_t stream) {
+  return attn_prefill_lse(q, k, v, o, nullptr, B, H, H_kv, Sq, Skv, D, layout, dtype, causal,
+                          scale, stream);
+}
+
+int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
+                     float scale, hipStream_t stream) {
   if (B < 0 || H < 0 || H_kv < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
   if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
   if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
@@ -110,12 +117,15 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B
   if (Skv > 0 && (!k || !v)) return ATTN_E_INVALID;
   if (!aligned16(q) || !aligned16(o) || (Skv > 0 && (!aligned16(k) || !aligned16(v))))
     return ATTN_E_INVALID;
+  if ((uintptr_t)lse & 3u) return ATTN_E_INVALID;
 
   // In-head offsets (row * row_stride) are 32-bit in the kernel.
   const int64_t q_row = layout == ATTN_BHSD ? D : (int64_t)H * D;
   const int64_t kv_row = layout == ATTN_BHSD ? D : (int64_t)H_kv * D;
   if ((int64_t)Sq * q_row >= ((int64_t)1 << 31) || (int64_t)Skv * kv_row >= ((int64_t)1 << 31))
     return ATTN_E_UNSUPPORTED;
+  // Byte offsets inside a 64-row tile are 32-bit too.
+  if (q_row >= ((int64_t)1 << 24) || kv_row >= ((int64_t)1 << 24)) return ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
   PrefillArgs a;
@@ -143,7 +153,77 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B
   a.k_cache = a.v_cache = nullptr;
   a.page_table = a.prefix_lens = a.qo_start = nullptr;
   a.max_pages = a.num_pages = a.total_tokens = 0;
+  a.lse = lse;
   hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+size_t attn_prefill_bwd_workspace_size(int B, int H, int Sq) {
+  if (B < 0 || H < 0 || Sq < 0) return 0;
+  return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv,
+                     int Sq, int Skv, int D, int layout, int dtype, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H == 0 || ((int64_t)Sq == 0 && (int64_t)Skv == 0)) return ATTN_OK;
+  if (Sq > 0 && (!q || !o || !dO || !lse || !dq)) return ATTN_E_INVALID;
+  if (Skv > 0 && (!k || !v || !dk || !dv)) return ATTN_E_INVALID;
+  for (const void* p : {q, k, v, o, dO, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (p && !aligned16(p)) return ATTN_E_INVALID;
+  if ((uintptr_t)lse & 3u) return ATTN_E_INVALID;
+  const size_t need = attn_prefill_bwd_workspace_size(B, H, Sq);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return ATTN_E_INVALID;
+  const int64_t q_row = layout == ATTN_BHSD ? D : (int64_t)H * D;
+  const int64_t kv_row = layout == ATTN_BHSD ? D : (int64_t)H_kv * D;
+  if ((int64_t)Sq * q_row >= ((int64_t)1 << 31) || (int64_t)Skv * kv_row >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;
+  if (q_row >= ((int64_t)1 << 24) || kv_row >= ((int64_t)1 << 24)) return ATTN_E_UNSUPPORTED;
+  // Grids: delta (16 rows per workgroup), dK/dV (128 keys), dQ (128 or 256 queries).
+  const int64_t grid_limit = (int64_t)1 << 31;
+  if ((int64_t)B * H * Sq / 16 >= grid_limit ||
+      (int64_t)B * H_kv * ((Skv + 127) / 128) >= grid_limit ||
+      (int64_t)B * H * ((Sq + 127) / 128) >= grid_limit)
+    return ATTN_E_UNSUPPORTED;
+
+  BackwardArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.group = H / H_kv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  if (layout == ATTN_BHSD) {
+    a.q_sb = (int64_t)H * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)H_kv * Skv * D; a.k_sh = (int64_t)Skv * D; a.k_ss = D;
+  } else {
+    a.q_sb = (int64_t)Sq * H * D; a.q_sh = D; a.q_ss = H * D;
+    a.k_sb = (int64_t)Skv * H_kv * D; a.k_sh = D; a.k_ss = H_kv * D;
+  }
+  a.scale = scale;
+  a.c = exp2_multiplier(scale);  // the forward's multiplier: P matches its LSE
+  a.causal_off = Skv - Sq;
+  a.n_tiles = a.total = 0;
+  hipError_t e = launch_prefill_backward(D, bf16, causal != 0, out_f32, a, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -169,6 +249,7 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, int B
   const int64_t kv_row = layout == ATTN_BHSD ? D : (int64_t)H_kv * D;
   if ((int64_t)Sq * q_row * 4 >= ((int64_t)1 << 31) || (int64_t)Skv * kv_row >= ((int64_t)1 << 31))
     return ATTN_E_UNSUPPORTED;
+  if (q_row >= ((int64_t)1 << 24) || kv_row >= ((int64_t)1 << 24)) return ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
   PrefillArgs a;
@@ -198,6 +279,7 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, int B
   a.k_cache = a.v_cache = nullptr;
   a.page_table = a.prefix_lens = a.qo_start = nullptr;
   a.max_pages = a.num_pages = a.total_tokens = 0;
+  a.lse = nullptr;
   hipError_t e = launch_prefill_fp8(D, out_bf16, causal != 0, out_f32, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
@@ -255,6 +337,7 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
   a.max_pages = max_pages_per_seq;
   a.num_pages = num_pages;
   a.total_tokens = total_tokens;
+  a.lse = nullptr;
   hipError_t e = launch_extend(D, bf16, out_f32, a, B, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }

@@ -67,6 +67,15 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+// Workgroup -> work item.  The dispatcher sends workgroup w to XCD w % 8; give
+// each XCD a contiguous range of work items so one head's tiles share an L2.
+// Bijective on [0, total).
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = w & 7, k = w >> 3;
+  return x * q + min(x, r) + k;
+}
+
 // XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
 // D = 128 (16 chunks) it swaps the two 2-bit halves of the row's low nibble:
 // 16 consecutive rows read at one logical chunk (the K operand reads) land on

@@ -33,6 +33,9 @@ struct PrefillArgs {
   const int32_t* prefix_lens;
   const int32_t* qo_start;
   int max_pages, num_pages, total_tokens;
+  // Forward only: if not null, the natural log-sum-exp of each query row's
+  // scaled logits, [B, H, Sq] fp32 (-inf for a row with no visible key).
+  float* lse;
 };
 
 hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
@@ -41,6 +44,31 @@ hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const Pre
 // O in fp16 (out_bf16 = false), bf16 or fp32.  Strides are in elements (bytes).
 hipError_t launch_prefill_fp8(int D, bool out_bf16, bool causal, bool out_f32,
                               const PrefillArgs& a, int B, hipStream_t s);
+// Backward of dense prefill (fp16/bf16, BHSD/BSHD, grouped heads, causal).
+struct BackwardArgs {
+  const uint16_t* q;    // [B, H, Sq, D] / [B, Sq, H, D]
+  const uint16_t* k;    // H_kv heads, Skv keys
+  const uint16_t* v;
+  const uint16_t* o;    // forward output, like q
+  const uint16_t* dO;   // like q
+  const float* lse;     // [B, H, Sq] natural log-sum-exp from the forward
+  float* delta;         // [B, H, Sq] workspace: rowsum(dO * O)
+  void* dq;             // like q (dtype, or fp32 with out_f32)
+  void* dk;             // like k
+  void* dv;             // like v
+  int B, H, H_kv, group, Sq, Skv;
+  int64_t q_sb, q_sh;   // element strides of q, o, dO, dq
+  int q_ss;
+  int64_t k_sb, k_sh;   // element strides of k, v, dk, dv
+  int k_ss;
+  float scale;          // softmax scale
+  float c;              // scale * log2(e)
+  int causal_off;       // Skv - Sq
+  int n_tiles, total;   // set by the launcher
+};
+hipError_t launch_prefill_backward(int D, bool bf16, bool causal, bool out_f32,
+                                   const BackwardArgs& a, hipStream_t s);
+
 // Extend attention (causal over a paged prefix followed by the new tokens).
 hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
                          hipStream_t s);

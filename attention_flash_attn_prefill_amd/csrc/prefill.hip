@@ -68,15 +68,6 @@ namespace {
 
 #include "cdna4_common.h"
 
-// Workgroup -> work item.  The dispatcher sends workgroup w to XCD w % 8; give
-// each XCD a contiguous range of work items so one head's query tiles share
-// an L2.  Bijective on [0, total).
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int x = w & 7, k = w >> 3;
-  return x * q + min(x, r) + k;
-}
-
 // NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
 // OF32: O is stored in fp32 instead of the input type.  EXT (with CAUSAL):
 // extend attention -- a sequence's keys are its cached prefix, read through
@@ -553,6 +544,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
   // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
   const float l_tot = pair_sum(l_run);
+  if (a.lse != nullptr && q_ok && hi == 0) {
+    // log2-sum-exp of s c is m_run + log2(l); the natural one of s scale is
+    // that times ln 2.
+    const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+    a.lse[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
+  }
   // A rejected prefix page makes the rows NaN (the key set is unknown).
   const float inv =
       bad_page ? __builtin_nanf("") : (l_tot > 0.f ? a.o_scale / l_tot : 0.f);

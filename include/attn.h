@@ -106,6 +106,48 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o,
                      int causal, float scale, hipStream_t stream);
 
 /*
+ * attn_prefill_gqa that also stores each query row's log-sum-exp, for the
+ * backward pass: lse [B, H, Sq] fp32 (BHSD order whatever the layout), the
+ * natural log of sum_j exp(scale <q_i, k_j> + M_ij), -inf for a row with no
+ * visible key.  lse may be NULL (then this is attn_prefill_gqa); it must be
+ * 4-byte aligned.
+ */
+int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
+                     int causal, float scale, hipStream_t stream);
+
+/* Workspace bytes of attn_prefill_bwd: one fp32 per query row (delta). */
+size_t attn_prefill_bwd_workspace_size(int B, int H, int Sq);
+
+/*
+ * Backward of attn_prefill_gqa (backward flash attention: "Wave February 2025
+ * Release" roadmap): the gradients dq, dk, dv of sum(O * dO) for
+ * O = attention(q, k, v), by the chain rule with P recomputed from lse:
+ *
+ *   dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, V_j>,  delta_i = <dO_i, O_i>,
+ *   dS_ij = P_ij (dP_ij - delta_i),
+ *   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
+ *
+ * grouped heads summing into their KV head's dk, dv.
+ *
+ *   q, o, dO, dq: like q of attn_prefill_gqa; k, v, dk, dv: like k; lse: from
+ *   attn_prefill_lse on the same inputs.  dq, dk, dv: the input dtype, or
+ *   fp32 with ATTN_OUT_F32 in dtype.  Every row of dq, dk and dv is written.
+ *   workspace: >= attn_prefill_bwd_workspace_size(B, H, Sq) bytes, 16-byte
+ *   aligned, no initialisation needed.
+ *
+ * Arithmetic: S and dP on MFMA in the input dtype with fp32 accumulation; P
+ * and dS rounded to the input dtype as MFMA operands; dO, Q, K, V used as
+ * given.  Deterministic: no atomics (dk, dv are summed inside one workgroup,
+ * dq by a second kernel).
+ */
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
+                     int causal, float scale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
  * FP8 prefill: attn_prefill_gqa with q, k, v in OCP e4m3fn (one byte per
  * element, same shapes and layouts) and per-tensor descales: the inputs are
  * q_descale * Q, k_descale * K, v_descale * V.  (FP8 flash attention is a

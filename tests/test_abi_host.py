@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                             "attn_prefill_gqa", "attn_paged_decode_gqa",
                             "attn_paged_decode_gqa_workspace_size",
                             "attn_paged_decode_gqa_num_splits", "attn_extend",
-                            "attn_prefill_fp8"])
+                            "attn_prefill_fp8", "attn_prefill_lse", "attn_prefill_bwd",
+                            "attn_prefill_bwd_workspace_size"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -82,6 +83,7 @@ def _prefill(**kw):
     (dict(q=FAKE + 8), attn.ATTN_E_INVALID),
     (dict(v=FAKE + 2), attn.ATTN_E_INVALID),
     (dict(layout=1, H=1 << 20, Sq=4096, Skv=4096), attn.ATTN_E_UNSUPPORTED),  # 32-bit offsets
+    (dict(layout=1, H=1 << 17, Sq=2, Skv=2), attn.ATTN_E_UNSUPPORTED),  # in-tile byte offsets
 ])
 def test_prefill_validation(kw, status):
     assert _prefill(**kw) == status
@@ -117,6 +119,81 @@ def test_prefill_gqa_validation(kw, status):
 def test_prefill_gqa_empty_is_a_noop():
     assert _prefill_gqa(H=0, H_kv=0, q=None, k=None, v=None, o=None) == attn.ATTN_OK
     assert _prefill_gqa(Sq=0) == attn.ATTN_OK
+
+
+def _prefill_lse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=8, H_kv=2, Sq=16, Skv=16, D=128,
+             layout=0, dtype=0, causal=0, scale=0.1, stream=0)
+    a.update(kw)
+    return attn.attn_prefill_lse(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=FAKE + 2), attn.ATTN_E_INVALID),   # lse must be 4-byte aligned
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(o=None), attn.ATTN_E_INVALID),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(dtype=9), attn.ATTN_E_INVALID),
+])
+def test_prefill_lse_validation(kw, status):
+    assert _prefill_lse(**kw) == status
+
+
+def test_prefill_lse_empty_is_a_noop():
+    assert _prefill_lse(Sq=0, q=None, o=None, lse=None) == attn.ATTN_OK
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dO=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+             H=8, H_kv=2, Sq=16, Skv=16, D=128, layout=0, dtype=0, causal=0, scale=0.1,
+             workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+    a.update(kw)
+    return attn.attn_prefill_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), attn.ATTN_E_INVALID),
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(H_kv=0), attn.ATTN_E_INVALID),
+    (dict(layout=2), attn.ATTN_E_INVALID),
+    (dict(dtype=7), attn.ATTN_E_INVALID),
+    (dict(scale=float("nan")), attn.ATTN_E_INVALID),
+    (dict(scale=-1.0), attn.ATTN_E_INVALID),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(D=0), attn.ATTN_E_INVALID),
+    (dict(dO=None), attn.ATTN_E_INVALID),
+    (dict(lse=None), attn.ATTN_E_INVALID),
+    (dict(dq=None), attn.ATTN_E_INVALID),
+    (dict(dk=None), attn.ATTN_E_INVALID),
+    (dict(dv=None), attn.ATTN_E_INVALID),
+    (dict(dq=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(lse=FAKE + 2), attn.ATTN_E_INVALID),
+    (dict(workspace=None), attn.ATTN_E_WORKSPACE),
+    (dict(workspace_bytes=16 * 8 * 4 - 4), attn.ATTN_E_WORKSPACE),
+    (dict(workspace=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(layout=1, H=1 << 20, H_kv=1 << 20, Sq=4096, Skv=4096, workspace_bytes=1 << 40),
+     attn.ATTN_E_UNSUPPORTED),                   # 32-bit in-head offsets
+    (dict(layout=1, H=1 << 17, H_kv=1 << 17, Sq=2, Skv=2), attn.ATTN_E_UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 10, H_kv=1 << 10, Sq=1 << 10, Skv=1 << 10, workspace_bytes=1 << 62),
+     attn.ATTN_E_UNSUPPORTED),                   # grid sizes
+])
+def test_prefill_bwd_validation(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_prefill_bwd_empty_is_a_noop():
+    none = dict(q=None, k=None, v=None, o=None, dO=None, lse=None, dq=None, dk=None, dv=None,
+                workspace=None, workspace_bytes=0)
+    assert _bwd(B=0, **none) == attn.ATTN_OK
+    assert _bwd(Sq=0, Skv=0, **none) == attn.ATTN_OK
+
+
+def test_prefill_bwd_workspace_size():
+    # one fp32 per query row, rounded up to 256 bytes
+    assert attn.attn_prefill_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 4
+    assert attn.attn_prefill_bwd_workspace_size(1, 1, 3) == 256
+    assert attn.attn_prefill_bwd_workspace_size(0, 4, 4) == 0
+    assert attn.attn_prefill_bwd_workspace_size(-1, 4, 4) == 0
 
 
 def _decode_gqa(**kw):
