@@ -158,9 +158,14 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+// Two fp32 arrays of B*H*Sq (delta, then -LSE log2 e), each padded to 256 bytes.
+static size_t bwd_row_array_bytes(int B, int H, int Sq) {
+  return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~(size_t)255;
+}
+
 size_t attn_prefill_bwd_workspace_size(int B, int H, int Sq) {
   if (B < 0 || H < 0 || Sq < 0) return 0;
-  return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~(size_t)255;
+  return 2 * bwd_row_array_bytes(B, H, Sq);
 }
 
 int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -203,6 +208,8 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
   a.dO = static_cast<const uint16_t*>(dO);
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
+  a.nl2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                   bwd_row_array_bytes(B, H, Sq));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

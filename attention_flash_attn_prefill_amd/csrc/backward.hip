@@ -61,12 +61,14 @@ __device__ __forceinline__ uint32_t pack_in(float x, float y) {
   else return pack_f16(x, y);
 }
 
-// LSE in log2 units; a row with no visible key (-inf) gives P = 0.
-__device__ __forceinline__ float lse2_of(float lse) {
-  return lse > kNegInf ? lse * kLog2e : __builtin_huge_valf();
+// -LSE in log2 units, so that P = exp2(S c + nl2); a row with no visible key
+// (LSE = -inf) gets -inf, hence P = 0.
+__device__ __forceinline__ float nl2_of(float lse) {
+  return lse > kNegInf ? -lse * kLog2e : kNegInf;
 }
 
 // ------------------------------------------------------------------ delta
+// Per query row: delta = rowsum(dO * O) and nl2 = -LSE log2(e).
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
@@ -90,7 +92,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (gl == 0 && row < rows) a.delta[row] = acc;
+  if (gl == 0 && row < rows) {
+    a.delta[row] = acc;
+    a.nl2[row] = nl2_of(a.lse[row]);
+  }
 }
 
 // Store 4 consecutive values of a gradient row (dtype or fp32).
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[BQ * D];
   __shared__ __attribute__((aligned(1024))) uint16_t do_lds0[BQ * D];
   __shared__ __attribute__((aligned(1024))) uint16_t do_lds1[BQ * D];
-  // LSE (floats 0..63) and delta (64..127) of a tile's rows.
+  // nl2 (floats 0..63) and delta (64..127) of a tile's rows.
   __shared__ __attribute__((aligned(512))) float rs_lds0[2 * BQ];
   __shared__ __attribute__((aligned(512))) float rs_lds1[2 * BQ];
 
@@ -167,10 +172,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     g_off[i] = (row * a.q_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
   }
   const uint32_t row_bytes = (uint32_t)a.q_ss * 2u;
-  auto step_head = [&](int u) __attribute__((always_inline)) { return hk * a.group + u / n_qt; };
-  auto step_q0 = [&](int u) __attribute__((always_inline)) { return (qt0 + u % n_qt) * BQ; };
-  auto issue = [&](int u, LDS_AS uint16_t* qd, LDS_AS uint16_t* dd, LDS_AS float* rd) __attribute__((always_inline)) {
-    const int h = step_head(u), i0 = step_q0(u);
+  // A step's position: query head h (of the group), query tile t.  Steps go
+  // through the tiles of one head, then the next head.
+  struct Pos {
+    int h, t;
+  };
+  const int qt_end = qt0 + n_qt;
+  auto advance = [&](Pos p) __attribute__((always_inline)) {
+    return p.t + 1 < qt_end ? Pos{p.h, p.t + 1} : Pos{p.h + 1, qt0};
+  };
+  auto issue = [&](Pos p, LDS_AS uint16_t* qd, LDS_AS uint16_t* dd, LDS_AS float* rd) __attribute__((always_inline)) {
+    const int h = p.h, i0 = p.t * BQ;
     const int64_t base = b * a.q_sb + h * a.q_sh + (int64_t)i0 * a.q_ss;
     const uint32_t rows = (uint32_t)max(0, a.Sq - i0);
     const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + base), (short)0,
@@ -184,11 +196,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (LDS_AS void*)(dd + (wave * LOADS + i) * 512),
                                                16, g_off[i], 0, 0, 0);
     }
-    if (wave == 0) {  // 64 rows of LSE and of delta: one float per lane (the
+    if (wave == 0) {  // 64 rows of nl2 and of delta: one float per lane (the
       // rows start at any float, so no wider access); rows past Sq read 0.
       const int64_t rbase = ((int64_t)b * a.H + h) * a.Sq + i0;
       const int nb = (int)(min((uint32_t)BQ, rows) * 4u);
-      const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + rbase), (short)0, nb,
+      const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.nl2 + rbase), (short)0, nb,
                                                         kBufferConfig);
       const auto rt = __builtin_amdgcn_make_buffer_rsrc((void*)(a.delta + rbase), (short)0, nb,
                                                         kBufferConfig);
@@ -227,30 +239,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = (f32x16){};
 
-  auto compute = [&](int u, const LDS_AS uint16_t* qs, const LDS_AS uint16_t* ds,
+  // Rows past Sq read Q, dO, LSE and delta as zeros (buffer bounds), so P = 1
+  // and dS = 0 there, and they add exactly 0 to dV = P^T dO and dK = dS^T Q;
+  // keys past Skv are never stored; a row that sees no key has LSE = -inf and
+  // P = 0.  Only the causal diagonal needs a mask.
+  auto compute = [&](int i0, const LDS_AS uint16_t* qs, const LDS_AS uint16_t* ds,
                      const LDS_AS float* rs) __attribute__((always_inline)) {
-    const int i0 = step_q0(u);
-    // Queries of this tile that can see a key of this wave.
-    if (CAUSAL && i0 + BQ - 1 < jw - a.causal_off) return;
+    // Causal mask without branches: value r of block ib is visible iff its
+    // query row i0 + 32ib + 8(r/4) + 4hi + r%4 >= jl - off, i.e. iff
+    // dq >= -(32ib + 8(r/4) + r%4) with dq = i0 + 4hi - (jl - off); a tile
+    // off the diagonal of this wave's keys takes a dq that passes every test.
+    const bool diag = CAUSAL && jw + 31 > i0 + a.causal_off;
+    const int dq = diag ? i0 + 4 * hi - (jl - a.causal_off) : (1 << 20);
+    // S = Q K^T and dP = dO V^T of both 32-query blocks first (rows = queries,
+    // lane = key), so the softmax arithmetic of one block can run beside the
+    // MFMAs of the other.
+    f32x16 sc[BQ / 32], dp[BQ / 32];
 #pragma unroll
     for (int ib = 0; ib < BQ / 32; ++ib) {
-      // S = Q K^T and dP = dO V^T: 32 queries (rows) x 32 keys (lane).
-      u32x4 fq[D / 16];
+      u32x4 fq[D / 16], fd[D / 16];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
+      for (int s = 0; s < D / 16; ++s) {
         fq[s] = *reinterpret_cast<const LDS_AS u32x4*>(qs + 32 * ib * D + r_rd[s]);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sc = (f32x16){};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) sc = mfma_qk<BF16>(fq[s], ktf[s], sc);
-      u32x4 fd[D / 16];
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s)
         fd[s] = *reinterpret_cast<const LDS_AS u32x4*>(ds + 32 * ib * D + r_rd[s]);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 dp = (f32x16){};
+      }
+      sc[ib] = dp[ib] = (f32x16){};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) dp = mfma_qk<BF16>(fd[s], vtf[s], dp);
+      for (int s = 0; s < D / 16; ++s) sc[ib] = mfma_qk<BF16>(fq[s], ktf[s], sc[ib]);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) dp[ib] = mfma_qk<BF16>(fd[s], vtf[s], dp[ib]);
+    }
+#pragma unroll
+    for (int ib = 0; ib < BQ / 32; ++ib) {
       // P and dS; lane value r is query row 8(r/4) + 4hi + r%4 of the block.
       u32x4 pf[2], sf[2];
 #pragma unroll
@@ -262,10 +282,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * grp + e;
-          const int qi = i0 + rloc + e;
-          const bool vis = qi < a.Sq && k_ok && (!CAUSAL || jl <= qi + a.causal_off);
-          p[e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.c, -lse2_of(l4[e]))) : 0.f;
-          d[e] = p[e] * (dp[r] - t4[e]);
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ib][r], a.c, l4[e]));
+          if constexpr (CAUSAL) x = dq >= -(32 * ib + 8 * grp + e) ? x : 0.f;
+          p[e] = x;
+          d[e] = x * (dp[ib][r] - t4[e]);
         }
         // Values r = 8 s2 + j go to operand s2, slot j (the forward's P layout).
         const int s2 = grp >> 1, w0 = 2 * (grp & 1);
@@ -283,7 +303,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
           td[db] = tr_frag(ds, (32 * ib + 16 * s2) * D, db);
           tq[db] = tr_frag(qs, (32 * ib + 16 * s2) * D, db);
         }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           dv[db] = mfma_qk<BF16>(td[db], pf[s2], dv[db]);
@@ -296,13 +315,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   LDS_AS uint16_t* const Qs[2] = {(LDS_AS uint16_t*)q_lds0, (LDS_AS uint16_t*)q_lds1};
   LDS_AS uint16_t* const Ds[2] = {(LDS_AS uint16_t*)do_lds0, (LDS_AS uint16_t*)do_lds1};
   LDS_AS float* const Rs[2] = {(LDS_AS float*)rs_lds0, (LDS_AS float*)rs_lds1};
-  if (steps > 0) issue(0, Qs[0], Ds[0], Rs[0]);
+  Pos cur{hk * a.group, qt0};
+  Pos nxt = advance(cur);
+  if (steps > 0) issue(cur, Qs[0], Ds[0], Rs[0]);
   auto iteration = [&](int u, auto par) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     wait_vmcnt<0>();
     __syncthreads();
-    if (u + 1 < steps) issue(u + 1, Qs[P ^ 1], Ds[P ^ 1], Rs[P ^ 1]);
-    compute(u, Qs[P], Ds[P], Rs[P]);
+    if (u + 1 < steps) issue(nxt, Qs[P ^ 1], Ds[P ^ 1], Rs[P ^ 1]);
+    const int i0 = cur.t * BQ;
+    // Skip a tile whose queries all precede this wave's keys.
+    if (!CAUSAL || i0 + BQ - 1 >= jw - a.causal_off) compute(i0, Qs[P], Ds[P], Rs[P]);
+    cur = nxt;
+    nxt = advance(nxt);
   };
   for (int u = 0; u < steps; u += 2) {
     iteration(u, std::integral_constant<int, 0>{});
@@ -371,7 +396,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
                  : (u32x4){0u, 0u, 0u, 0u};
   }
   const int64_t rid = ((int64_t)b * a.H + h) * a.Sq + qi;
-  const float lse2 = q_ok ? lse2_of(a.lse[rid]) : __builtin_huge_valf();
+  const float nl2 = q_ok ? a.nl2[rid] : kNegInf;
   const float delta = q_ok ? a.delta[rid] : 0.f;
 
   int kv_end = a.Skv;
@@ -453,7 +478,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * s2 + j;
         const int key = kv0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.c, -lse2));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.c, nl2));
         if (need_mask && key > lim) p = 0.f;
         d[j] = p * (dp[r] - delta);
       }

@@ -53,6 +53,7 @@ struct BackwardArgs {
   const uint16_t* dO;   // like q
   const float* lse;     // [B, H, Sq] natural log-sum-exp from the forward
   float* delta;         // [B, H, Sq] workspace: rowsum(dO * O)
+  float* nl2;           // [B, H, Sq] workspace: -LSE * log2(e) (-inf for a row with no key)
   void* dq;             // like q (dtype, or fp32 with out_f32)
   void* dk;             // like k
   void* dv;             // like v

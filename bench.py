@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -10,9 +10,10 @@ Sq=Skv=4096 D=128 fp16 BHSD non-causal, with inputs resident in HBM.  The
 headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
 step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
-multi-query paged decode, extend after a paged prefix, fp8 prefill) are
-measured the same way and reported under "extra", decode in GB/s of
-algorithmic K/V bytes.
+multi-query paged decode, extend after a paged prefix, fp8 prefill, and the
+backward of the causal 8k workload) are measured the same way and reported
+under "extra", decode in GB/s of algorithmic K/V bytes, the backward in
+TFLOP/s of its five products (2.5x the forward's flops).
 
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
 run on, bracketed by torch.cuda.synchronize(); HIP events around every step
@@ -42,6 +43,7 @@ PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 PREFILL_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode.hip")
 DECODE_GQA_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode_gqa.hip")
+BACKWARD_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "backward.hip")
 
 
 def prefill_flops(m):
@@ -334,6 +336,46 @@ def bench_extend(attn, cfg, steps, warmup, clock):
     return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof)
 
 
+def backward_flops(m):
+    """The backward's five products (S, dP, dV, dK, dQ, each 2*Sq*Skv*D per
+    head; half under the causal mask): 2.5x the forward's two."""
+    return 2.5 * prefill_flops(m)
+
+
+def bench_backward(attn, cfg, steps, warmup, clock):
+    """One step: one attn_prefill_bwd call (delta, dK/dV and dQ kernels) on
+    the forward's O and LSE, which are computed once before timing."""
+    import torch
+    import workloads
+    q, k, v, do, m = workloads.backward_config(cfg)
+    q, k, v, do = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    stream = torch.cuda.current_stream()
+    o, lse = attn.prefill_with_lse(q, k, v, causal=m["causal"], scale=m["scale"],
+                                   layout=m["layout"], stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(attn.attn_prefill_bwd_workspace_size(m["B"], m["H"], m["Sq"]), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        attn.prefill_backward(q, k, v, o, do, lse, causal=m["causal"], scale=m["scale"],
+                              layout=m["layout"], dq=dq, dk=dk, dv=dv, workspace=ws,
+                              stream=stream)
+
+    t = measure(step, steps, warmup, stream, clock)
+    flops = backward_flops(m)
+    tflops = flops / (t["mean_ms"] * 1e-3) / 1e12
+    cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "H_kv": m["H_kv"],
+               "Sq": m["Sq"], "Skv": m["Skv"], "D": m["D"], "layout": m["layout"],
+               "causal": m["causal"], "dtype": m["dtype"], "pass": "backward"}
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16, 4),
+            "scope": "the whole backward call (3 kernels)",
+            "traffic": load_traffic(f"prefill_bwd__{m['name']}", BACKWARD_SRC)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof)
+
+
 def copy_calibration(mib):
     """A plain elementwise copy of known size (reads and writes mib MiB each),
     run so HBM byte counters can be scaled against it."""
@@ -425,7 +467,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
@@ -471,6 +513,8 @@ def main():
             results[c] = bench_decode(attn, c, args.steps, args.warmup, clock)
         elif c in workloads.EXTEND_CONFIGS:
             results[c] = bench_extend(attn, c, args.steps, args.warmup, clock)
+        elif c in workloads.BACKWARD_CONFIGS:
+            results[c] = bench_backward(attn, c, args.steps, args.warmup, clock)
         else:
             results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock)
         r = results[c]

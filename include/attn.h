@@ -116,7 +116,8 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
                      int causal, float scale, hipStream_t stream);
 
-/* Workspace bytes of attn_prefill_bwd: one fp32 per query row (delta). */
+/* Workspace bytes of attn_prefill_bwd: two fp32 per query row (delta =
+ * rowsum(dO * O) and -LSE log2(e)), each array padded to 256 bytes. */
 size_t attn_prefill_bwd_workspace_size(int B, int H, int Sq);
 
 /*

@@ -169,11 +169,12 @@ def _bwd(**kw):
     (dict(dq=FAKE + 8), attn.ATTN_E_INVALID),
     (dict(lse=FAKE + 2), attn.ATTN_E_INVALID),
     (dict(workspace=None), attn.ATTN_E_WORKSPACE),
-    (dict(workspace_bytes=16 * 8 * 4 - 4), attn.ATTN_E_WORKSPACE),
+    (dict(workspace_bytes=2 * 16 * 8 * 4 - 4), attn.ATTN_E_WORKSPACE),
     (dict(workspace=FAKE + 8), attn.ATTN_E_INVALID),
     (dict(layout=1, H=1 << 20, H_kv=1 << 20, Sq=4096, Skv=4096, workspace_bytes=1 << 40),
      attn.ATTN_E_UNSUPPORTED),                   # 32-bit in-head offsets
-    (dict(layout=1, H=1 << 17, H_kv=1 << 17, Sq=2, Skv=2), attn.ATTN_E_UNSUPPORTED),
+    (dict(layout=1, H=1 << 17, H_kv=1 << 17, Sq=2, Skv=2, workspace_bytes=1 << 40),
+     attn.ATTN_E_UNSUPPORTED),                   # in-tile byte offsets
     (dict(B=1 << 20, H=1 << 10, H_kv=1 << 10, Sq=1 << 10, Skv=1 << 10, workspace_bytes=1 << 62),
      attn.ATTN_E_UNSUPPORTED),                   # grid sizes
 ])
@@ -189,9 +190,9 @@ def test_prefill_bwd_empty_is_a_noop():
 
 
 def test_prefill_bwd_workspace_size():
-    # one fp32 per query row, rounded up to 256 bytes
-    assert attn.attn_prefill_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 4
-    assert attn.attn_prefill_bwd_workspace_size(1, 1, 3) == 256
+    # two fp32 per query row, each array rounded up to 256 bytes
+    assert attn.attn_prefill_bwd_workspace_size(2, 32, 8192) == 2 * (2 * 32 * 8192 * 4)
+    assert attn.attn_prefill_bwd_workspace_size(1, 1, 3) == 512
     assert attn.attn_prefill_bwd_workspace_size(0, 4, 4) == 0
     assert attn.attn_prefill_bwd_workspace_size(-1, 4, 4) == 0
 
