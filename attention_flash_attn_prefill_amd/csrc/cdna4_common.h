@@ -72,6 +72,18 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x * q + min(x, r) + k;
 }
 
+// Workgroup -> work item for work made of `pairs` blocks of `m` items that
+// read the same data (a sequence's KV head): block j runs on XCD j % 8, so a
+// block's items share one L2, and every XCD gets every eighth block (with
+// ragged sequences that balances the XCDs, where contiguous ranges would
+// give each XCD about one sequence).  Identity unless pairs % 8 == 0.
+// Bijective on [0, pairs * m).
+__device__ __forceinline__ int xcd_interleave(int w, int pairs, int m) {
+  if (pairs & 7) return w;
+  const int x = w & 7, k = w >> 3;
+  return ((k / m) * 8 + x) * m + k % m;
+}
+
 // XOR swizzle of the 16-byte chunk index within an LDS row of D halves.  For
 // D = 128 (16 chunks) it swaps the two 2-bit halves of the row's low nibble:
 // 16 consecutive rows read at one logical chunk (the K operand reads) land on

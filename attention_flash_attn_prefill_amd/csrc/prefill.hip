@@ -112,7 +112,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // one sequence -- so the XCD with the longest sequence would finish last;
   // extend keeps the dispatcher's round-robin, which spreads every sequence
   // over all XCDs (measured: +19% on a ragged batch, even on uniform ones).
-  int L = EXT ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.total_tiles);
+  // Extend: a (sequence, KV head)'s n_mtiles * group work items on one XCD.
+  int L = EXT ? xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * a.group),
+                               a.n_mtiles * a.group)
+              : xcd_remap(blockIdx.x, a.total_tiles);
   const int g = L % a.group;
   L /= a.group;
   int mt = L % a.n_mtiles;
