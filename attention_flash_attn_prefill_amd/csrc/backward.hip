@@ -272,27 +272,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
     for (int ib = 0; ib < BQ / 32; ++ib) {
       // P and dS; lane value r is query row 8(r/4) + 4hi + r%4 of the block.
-      u32x4 pf[2], sf[2];
+      float p[16], t[16];
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int rloc = 32 * ib + 8 * grp + 4 * hi;  // first of 4 consecutive rows
         const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + rloc);
         const f32x4 t4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + BQ + rloc);
-        float p[4], d[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * grp + e;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ib][r], a.c, l4[e]));
-          if constexpr (CAUSAL) x = dq >= -(32 * ib + 8 * grp + e) ? x : 0.f;
-          p[e] = x;
-          d[e] = x * (dp[ib][r] - t4[e]);
+          p[4 * grp + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ib][4 * grp + e], a.c, l4[e]));
+          t[4 * grp + e] = t4[e];
         }
-        // Values r = 8 s2 + j go to operand s2, slot j (the forward's P layout).
-        const int s2 = grp >> 1, w0 = 2 * (grp & 1);
-        pf[s2][w0] = pack_in<BF16>(p[0], p[1]);
-        pf[s2][w0 + 1] = pack_in<BF16>(p[2], p[3]);
-        sf[s2][w0] = pack_in<BF16>(d[0], d[1]);
-        sf[s2][w0 + 1] = pack_in<BF16>(d[2], d[3]);
+      }
+      // The mask only on blocks that cross the diagonal of this wave's keys
+      // (a wave-uniform branch; dq is exact whenever it is taken).
+      if (CAUSAL && jw + 31 > i0 + 32 * ib + a.causal_off) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[r] = dq >= -(32 * ib + 8 * (r >> 2) + (r & 3)) ? p[r] : 0.f;
+      }
+      // Values r = 8 s2 + j go to operand s2, slot j (the forward's P layout).
+      u32x4 pf[2], sf[2];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int r = 2 * w;
+        pf[w >> 2][w & 3] = pack_in<BF16>(p[r], p[r + 1]);
+        sf[w >> 2][w & 3] = pack_in<BF16>(p[r] * (dp[ib][r] - t[r]),
+                                          p[r + 1] * (dp[ib][r + 1] - t[r + 1]));
       }
       // dV^T += dO^T P and dK^T += Q^T dS (contraction over the block's rows).
 #pragma unroll
