@@ -75,12 +75,13 @@ namespace {
 // FP8: q, k, v are e4m3fn bytes; Q.K^T runs on the fp8 MFMA (32x32x64), V is
 // widened to fp16 on staging, and BF16 then selects only the output type.
 template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false,
-          bool FP8 = false>
+          bool FP8 = false, int HPW = 1>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(!(EXT && FP8), "extend takes fp16/bf16");
+  static_assert(NW % HPW == 0, "whole waves per query head");
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;
   constexpr int EB = FP8 ? 1 : 2;         // bytes per q/k/v element
@@ -102,27 +103,28 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 31, hi = lane >> 5;
 
-  // Work item L = ((b * H_kv + kv_head) * n_mtiles + mt) * group + g: the
-  // query heads that share a KV head are adjacent, so they run the same query
-  // tile at the same time on one XCD and read the same K/V tiles through its
-  // L2 (group = 1 is plain (b, h, mt) order).
-  //
-  // Extend batches are ragged (each sequence its own prefix and new-token
-  // count) and the XCD remap would give each XCD a contiguous range -- about
-  // one sequence -- so the XCD with the longest sequence would finish last;
-  // extend keeps the dispatcher's round-robin, which spreads every sequence
-  // over all XCDs (measured: +19% on a ragged batch, even on uniform ones).
-  // Extend: a (sequence, KV head)'s n_mtiles * group work items on one XCD.
-  int L = EXT ? xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * a.group),
-                               a.n_mtiles * a.group)
+  // HPW query heads of one KV group per workgroup (1 or 4): the workgroup
+  // covers RPW = BM / HPW rows of each, waves w*WPH .. w*WPH+WPH-1 taking
+  // head w; every K/V tile staged in LDS then serves the HPW heads, and a
+  // partial or causal query tile is RPW rows rather than BM.
+  constexpr int RPW = BM / HPW, WPH = NW / HPW;
+  // Work item L = ((b * H_kv + kv_head) * n_mtiles + mt) * (group / HPW) + gg:
+  // the query heads that share a KV head are adjacent, so they run the same
+  // query tile at the same time on one XCD and read the same K/V tiles
+  // through its L2 (group = 1 is plain (b, h, mt) order).  Extend batches are
+  // ragged, so there the (sequence, KV head) blocks are interleaved over the
+  // XCDs instead of given out in contiguous ranges.
+  const int hgroups = a.group / HPW;
+  int L = EXT ? xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * hgroups),
+                               a.n_mtiles * hgroups)
               : xcd_remap(blockIdx.x, a.total_tiles);
-  const int g = L % a.group;
-  L /= a.group;
+  const int gg = L % hgroups;
+  L /= hgroups;
   int mt = L % a.n_mtiles;
   L /= a.n_mtiles;
   if (CAUSAL) mt = a.n_mtiles - 1 - mt;  // heaviest query tiles first
   const int hk = L % a.H_kv, b = L / a.H_kv;
-  const int h = hk * a.group + g;
+  const int h = hk * a.group + gg * HPW + wave / WPH;  // wave-uniform
 
   // Sequence sizes.  Extend: Sq = the sequence's new tokens, Skv = prefix +
   // new, bottom-right causal (offset = prefix length); the first n_pre tiles
@@ -146,9 +148,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   const char* __restrict__ kp = reinterpret_cast<const char*>(a.k) + kv_base * EB;
   const char* __restrict__ vp = reinterpret_cast<const char*>(a.v) + kv_base * EB;
 
-  const int m0 = mt * BM;
+  const int m0 = mt * RPW;
   if (EXT && m0 >= Sq) return;  // past this sequence's new tokens (workgroup-uniform)
-  const int q0 = m0 + wave * 32;
+  const int q0 = m0 + (wave % WPH) * 32;
   const int qi = q0 + li;
   const bool q_ok = qi < Sq;
 
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 
   // Keys this workgroup needs: [0, kv_end).
   int kv_end = Skv;
-  if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + BM, Sq) + coff));
+  if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + RPW, Sq) + coff));
   const int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
   // Keys this wave needs: [0, wave_kv_end).
   const bool wave_active = q0 < Sq;
@@ -584,16 +586,26 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 }
 
 template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false,
-          bool FP8 = false>
+          bool FP8 = false, int HPW = 1>
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
-  const int64_t n_mtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
-  const int64_t total = (int64_t)B * a.H * n_mtiles;
+  constexpr int RPW = 32 * NW / HPW;  // query rows per head in a workgroup
+  const int64_t n_mtiles = (a.Sq + RPW - 1) / RPW;
+  const int64_t total = (int64_t)B * (a.H / HPW) * n_mtiles;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;
   a.total_tiles = (int)total;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN, EXT, FP8>),
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, OF32, NW, BN, EXT, FP8, HPW>),
                      dim3(a.total_tiles), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+
+// Four query heads per workgroup when the KV group allows it (group % 4 == 0),
+// for causal and extend work, where the shorter query tiles pay.
+template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false>
+hipError_t launch_g(const PrefillArgs& a, int B, hipStream_t s) {
+  if ((CAUSAL || EXT) && a.group % 4 == 0)
+    return launch_t<D, BF16, CAUSAL, OF32, NW, BN, EXT, false, 4>(a, B, s);
+  return launch_t<D, BF16, CAUSAL, OF32, NW, BN, EXT, false, 1>(a, B, s);
 }
 
 // D = 128: eight waves (256 query rows) share each 64-key K/V tile, one
@@ -602,7 +614,7 @@ template <int D, bool BF16, bool OF32>
 hipError_t launch_c(bool causal, const PrefillArgs& a, int B, hipStream_t s) {
   constexpr int NW = D == 128 ? 8 : 4;
   constexpr int BN = 64;
-  return causal ? launch_t<D, BF16, true, OF32, NW, BN>(a, B, s)
+  return causal ? launch_g<D, BF16, true, OF32, NW, BN>(a, B, s)
                 : launch_t<D, BF16, false, OF32, NW, BN>(a, B, s);
 }
 
@@ -634,10 +646,10 @@ hipError_t launch_ext_d(bool bf16, bool out_f32, const PrefillArgs& a, int B, hi
   constexpr int NW = D == 128 ? 8 : 4;
   constexpr int BN = 64;
   if (bf16)
-    return out_f32 ? launch_t<D, true, true, true, NW, BN, true>(a, B, s)
-                   : launch_t<D, true, true, false, NW, BN, true>(a, B, s);
-  return out_f32 ? launch_t<D, false, true, true, NW, BN, true>(a, B, s)
-                 : launch_t<D, false, true, false, NW, BN, true>(a, B, s);
+    return out_f32 ? launch_g<D, true, true, true, NW, BN, true>(a, B, s)
+                   : launch_g<D, true, true, false, NW, BN, true>(a, B, s);
+  return out_f32 ? launch_g<D, false, true, true, NW, BN, true>(a, B, s)
+                 : launch_g<D, false, true, false, NW, BN, true>(a, B, s);
 }
 }  // namespace
 
