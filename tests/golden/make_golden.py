@@ -27,6 +27,9 @@ DECODE_GQA = dict(B=2, H=4, h_kv=1, D=4, dtype="bf16", page_size=16, num_pages=8
                   seq_lens=[3, 18])
 DECODE = dict(B=3, H=2, D=4, dtype="f16", page_size=16, num_pages=8, seed=1003,
               seq_lens=[1, 16, 21])
+BACKWARD = dict(B=1, H=2, Sq=5, Skv=7, D=4, dtype="f16", layout="BSHD", causal=True, seed=1007,
+                h_kv=1)
+FP8 = dict(B=1, H=2, Sq=4, Skv=6, D=8, layout="BHSD", causal=True, seed=1008, h_kv=2)
 
 
 def build():
@@ -46,6 +49,21 @@ def build():
     o = oracle.extend(e.q, e.k, e.v, e.k_cache, e.v_cache, e.page_table, e.prefix_lens,
                       e.qo_start)
     out["extend"] = dict(case=EXTEND, out=o.round(15).tolist())
+    c = BACKWARD
+    q, k, v, do = workloads.backward_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                            c["layout"], seed=c["seed"], h_kv=c["h_kv"])
+    grads = oracle.sdpa_backward(q, k, v, do, causal=c["causal"], layout=c["layout"])
+    lse = oracle.lse_rows(q, k, causal=c["causal"], layout=c["layout"])
+    out["backward"] = dict(case=BACKWARD, dq=grads[0].round(15).tolist(),
+                           dk=grads[1].round(15).tolist(), dv=grads[2].round(15).tolist(),
+                           lse=lse.round(15).tolist())
+    c = FP8
+    q8, k8, v8, (qd, kd, vd) = workloads.prefill_inputs_fp8(c["B"], c["H"], c["Sq"], c["Skv"],
+                                                             c["D"], c["layout"], seed=c["seed"],
+                                                             h_kv=c["h_kv"])
+    qf, kf, vf = (oracle.dequantize_fp8(t, d) for t, d in ((q8, qd), (k8, kd), (v8, vd)))
+    o = oracle.sdpa(qf, kf, vf, causal=c["causal"], layout=c["layout"])
+    out["fp8"] = dict(case=FP8, out=o.round(15).tolist())
     return out
 
 
