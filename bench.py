@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11,12]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -11,7 +11,7 @@ headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
 step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
 multi-query paged decode, extend after a paged prefix, fp8 prefill, and the
-backward of the causal 8k workload) are measured the same way and reported
+backward of the causal 8k workload with and without grouped KV heads) are measured the same way and reported
 under "extra", decode in GB/s of algorithmic K/V bytes, the backward in
 TFLOP/s of its five products (2.5x the forward's flops).
 
@@ -467,7 +467,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11,12",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")

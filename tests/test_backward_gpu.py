@@ -153,14 +153,16 @@ def test_backward_writes_every_row(gpu_lib):
     assert torch.count_nonzero(dq[:, :170]) == 0   # rows 0..169 see no key
 
 
-def test_backward_full_config11_sampled(gpu_lib):
-    """The 8k causal BSHD backward at full size, in the bench's launch
-    configuration: dq at sampled query rows, dk and dv at sampled keys."""
-    q, k, v, do, m = workloads.backward_config(11)
-    print(f"[case] backward config 11 {m['name']}", flush=True)
+@pytest.mark.parametrize("cfg", [11, 12])
+def test_backward_full_config_sampled(gpu_lib, cfg):
+    """The 8k causal BSHD backward at full size (config 11; config 12 with
+    four query heads per KV head), in the bench's launch configuration: dq at
+    sampled query rows, dk and dv at sampled keys."""
+    q, k, v, do, m = workloads.backward_config(cfg)
+    print(f"[case] backward config {cfg} {m['name']}", flush=True)
     _, _, (dq, dk, dv) = _run(gpu_lib, q, k, v, do, m["causal"], m["layout"], scale=m["scale"])
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
-    rng = np.random.default_rng(11)
+    rng = np.random.default_rng(cfg)
     S = m["Sq"]
     rows = [(b, h, i) for b in range(m["B"]) for h in (0, 31) for i in (1, 127, 128, 4095, S - 1)]
     rows += [(int(rng.integers(m["B"])), int(rng.integers(m["H"])), int(rng.integers(S)))
@@ -168,12 +170,14 @@ def test_backward_full_config11_sampled(gpu_lib):
     ref = oracle.sdpa_backward_dq_rows(q, k, v, do, rows, causal=True, scale=m["scale"],
                                        layout=m["layout"])
     got = np.stack([dq[b, i, h].double().numpy() for b, h, i in rows])
-    _check_grad(got, ref, m["dtype"], f"config 11 dq ({len(rows)} rows)")
-    keys = [(b, g, j) for b, g in ((0, 0), (1, 17), (1, 31))
+    _check_grad(got, ref, m["dtype"], f"config {cfg} dq ({len(rows)} rows)")
+    Hk = m["H_kv"]
+    pairs = ((0, 0), (1, Hk // 2 + 1), (1, Hk - 1)) if Hk == m["H"] else ((0, 0), (1, Hk - 1))
+    keys = [(b, g, j) for b, g in pairs
             for j in (0, 1, 127, 128, 4096, S - 2, S - 1, int(rng.integers(S)))]
     rk, rv = oracle.sdpa_backward_kv_rows(q, k, v, do, keys, causal=True, scale=m["scale"],
                                           layout=m["layout"])
     gk = np.stack([dk[b, j, g].double().numpy() for b, g, j in keys])
     gv = np.stack([dv[b, j, g].double().numpy() for b, g, j in keys])
-    _check_grad(gk, rk, m["dtype"], f"config 11 dk ({len(keys)} keys)")
-    _check_grad(gv, rv, m["dtype"], f"config 11 dv ({len(keys)} keys)")
+    _check_grad(gk, rk, m["dtype"], f"config {cfg} dk ({len(keys)} keys)")
+    _check_grad(gv, rv, m["dtype"], f"config {cfg} dv ({len(keys)} keys)")

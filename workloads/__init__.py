@@ -58,6 +58,9 @@ PREFILL_CONFIGS = {
 BACKWARD_CONFIGS = {
     11: dict(name="bwd-causal-bshd-8k", B=2, H=32, Sq=8192, Skv=8192, D=128, dtype="bf16",
              layout="BSHD", causal=True, amp=0.5, amp_do=1.0, scale=None),
+    # The same with four query heads per KV head.
+    12: dict(name="bwd-gqa-causal-bshd-8k", B=2, H=32, H_kv=8, Sq=8192, Skv=8192, D=128,
+             dtype="bf16", layout="BSHD", causal=True, amp=0.5, amp_do=1.0, scale=None),
 }
 
 # Paged decode workload.
