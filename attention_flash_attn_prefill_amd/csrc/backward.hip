@@ -112,12 +112,21 @@ __device__ __forceinline__ void store4(void* base, int64_t off, const float* v, 
 
 // ------------------------------------------------------------------- dK/dV
 
+// One workgroup per (batch, KV head, 128 keys): four pairs of waves, a pair
+// per 32 keys.  In a pair the P-wave (waves 0-3) holds the keys' K as MFMA
+// operand and dV^T as accumulator, the D-wave (waves 4-7) holds V and dK^T;
+// both walk the same 64-query tiles of Q and dO (every query head of the
+// group) staged in LDS.  Per tile: the P-wave forms S = Q K^T and
+// P = exp2(S c + nl2) (fp32) while the D-wave forms dP = dO V^T; P goes to
+// LDS; after a barrier the P-wave accumulates dV^T += dO^T P and the D-wave
+// reads P, forms dS = P (dP - delta) and accumulates dK^T += Q^T dS.  Each
+// wave issues half of the tile's MFMAs, and two waves share each SIMD.
 template <int D, bool BF16, bool CAUSAL, bool OF32>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BackwardArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 4;                 // waves: 32 keys each
+  constexpr int NW = 8;                 // four pairs of waves
   constexpr int NT = 64 * NW;
-  constexpr int BK = 32 * NW;           // keys per workgroup
+  constexpr int BK = 32 * (NW / 2);     // keys per workgroup
   constexpr int BQ = 64;                // queries per streamed tile
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int LOADS = BQ * CPR / NT;  // chunk loads per thread per Q (or dO) tile
@@ -129,10 +138,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   // nl2 (floats 0..63) and delta (64..127) of a tile's rows.
   __shared__ __attribute__((aligned(512))) float rs_lds0[2 * BQ];
   __shared__ __attribute__((aligned(512))) float rs_lds1[2 * BQ];
+  // P of a tile, P-wave -> D-wave: [pair][block][4 quads][64 lanes] x f32x4.
+  __shared__ __attribute__((aligned(1024))) f32x4 p_lds[(NW / 2) * (BQ / 32) * 4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave / (NW / 2);  // 0: P-wave (K, dV), 1: D-wave (V, dK); wave-uniform
+  const int kw = wave % (NW / 2);    // the pair
   const int li = lane & 31, hi = lane >> 5;
 
   const int n_kb = a.n_tiles;
@@ -142,18 +155,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   const int hk = L % a.H_kv, b = L / a.H_kv;
 
   const int j0 = kb * BK;
-  const int jw = j0 + 32 * wave;  // this wave's first key
-  const int jl = jw + li;         // this lane's key
+  const int jw = j0 + 32 * kw;  // the pair's first key
+  const int jl = jw + li;       // this lane's key
   const bool k_ok = jl < a.Skv;
   const int64_t kv_base = b * a.k_sb + hk * a.k_sh;
 
-  // K^T and V^T fragments (B operands): lane holds row jl, dims 16s + 8hi .. +7.
-  u32x4 ktf[D / 16], vtf[D / 16];
+  // K^T (P-wave) or V^T (D-wave) fragments (B operands): lane holds row jl,
+  // dims 16s + 8hi .. +7.
+  const uint16_t* const kv_src = role == 0 ? a.k : a.v;
+  u32x4 kvf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const int64_t off = kv_base + (int64_t)jl * a.k_ss + 16 * s + 8 * hi;
-    ktf[s] = k_ok ? *reinterpret_cast<const u32x4*>(a.k + off) : (u32x4){0u, 0u, 0u, 0u};
-    vtf[s] = k_ok ? *reinterpret_cast<const u32x4*>(a.v + off) : (u32x4){0u, 0u, 0u, 0u};
+    kvf[s] = k_ok ? *reinterpret_cast<const u32x4*>(kv_src + off) : (u32x4){0u, 0u, 0u, 0u};
   }
 
   // Query tiles: every query head of the group, from the first tile with a
@@ -234,85 +248,113 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     const u32x2 h2 = __builtin_bit_cast(u32x2, up);
     return (u32x4){l2[0], l2[1], h2[0], h2[1]};
   };
+  // This lane's quad q of block ib in the pair's P exchange.
+  LDS_AS f32x4* const xch = (LDS_AS f32x4*)p_lds + kw * (BQ / 32) * 4 * 64 + lane;
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (D-wave)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = (f32x16){};
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
   // Rows past Sq read Q, dO, LSE and delta as zeros (buffer bounds), so P = 1
   // and dS = 0 there, and they add exactly 0 to dV = P^T dO and dK = dS^T Q;
   // keys past Skv are never stored; a row that sees no key has LSE = -inf and
   // P = 0.  Only the causal diagonal needs a mask.
-  auto compute = [&](int i0, const LDS_AS uint16_t* qs, const LDS_AS uint16_t* ds,
-                     const LDS_AS float* rs) __attribute__((always_inline)) {
-    // Causal mask without branches: value r of block ib is visible iff its
-    // query row i0 + 32ib + 8(r/4) + 4hi + r%4 >= jl - off, i.e. iff
-    // dq >= -(32ib + 8(r/4) + r%4) with dq = i0 + 4hi - (jl - off); a tile
-    // off the diagonal of this wave's keys takes a dq that passes every test.
-    const bool diag = CAUSAL && jw + 31 > i0 + a.causal_off;
-    const int dq = diag ? i0 + 4 * hi - (jl - a.causal_off) : (1 << 20);
-    // S = Q K^T and dP = dO V^T of both 32-query blocks first (rows = queries,
-    // lane = key), so the softmax arithmetic of one block can run beside the
-    // MFMAs of the other.
-    f32x16 sc[BQ / 32], dp[BQ / 32];
+  //
+  // Before the barrier: the P-wave's S, P (written to LDS and packed as the
+  // dV operand), or the D-wave's dP; lane value r of block ib is query row
+  // i0 + 32ib + 8(r/4) + 4hi + r%4, key jl.  keep[ib] carries across the
+  // barrier the D-wave's dP, or in its first 8 words the P-wave's packed P
+  // (the roles are exclusive, so they share the registers).
+  f32x16 keep[BQ / 32];
+  auto phase1 = [&](auto role_c, int i0, const LDS_AS uint16_t* qs, const LDS_AS uint16_t* ds,
+                    const LDS_AS float* rs) __attribute__((always_inline)) {
+    if constexpr (decltype(role_c)::value == 0) {
+      // Causal mask: visible iff dq >= -(32ib + 8(r/4) + r%4).
+      const int dq = i0 + 4 * hi - (jl - a.causal_off);
 #pragma unroll
-    for (int ib = 0; ib < BQ / 32; ++ib) {
-      u32x4 fq[D / 16], fd[D / 16];
+      for (int ib = 0; ib < BQ / 32; ++ib) {
+        u32x4 fq[D / 16];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        fq[s] = *reinterpret_cast<const LDS_AS u32x4*>(qs + 32 * ib * D + r_rd[s]);
-        fd[s] = *reinterpret_cast<const LDS_AS u32x4*>(ds + 32 * ib * D + r_rd[s]);
+        for (int s = 0; s < D / 16; ++s)
+          fq[s] = *reinterpret_cast<const LDS_AS u32x4*>(qs + 32 * ib * D + r_rd[s]);
+        f32x16 sc = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) sc = mfma_qk<BF16>(fq[s], kvf[s], sc);
+        float p[16];
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + 32 * ib + 8 * grp + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[4 * grp + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * grp + e], a.c, l4[e]));
+        }
+        // The mask only on blocks that cross the diagonal of the pair's keys
+        // (a wave-uniform branch).
+        if (CAUSAL && jw + 31 > i0 + 32 * ib + a.causal_off) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            p[r] = dq >= -(32 * ib + 8 * (r >> 2) + (r & 3)) ? p[r] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xch[(ib * 4 + q) * 64] = (f32x4){p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+        // Values r = 8 s2 + j go to operand s2, slot j (the forward's P
+        // layout): word w of keep holds values 2w, 2w+1.
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          keep[ib][w] = __uint_as_float(pack_in<BF16>(p[2 * w], p[2 * w + 1]));
       }
-      sc[ib] = dp[ib] = (f32x16){};
+    } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) sc[ib] = mfma_qk<BF16>(fq[s], ktf[s], sc[ib]);
+      for (int ib = 0; ib < BQ / 32; ++ib) {
+        u32x4 fd[D / 16];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) dp[ib] = mfma_qk<BF16>(fd[s], vtf[s], dp[ib]);
+        for (int s = 0; s < D / 16; ++s)
+          fd[s] = *reinterpret_cast<const LDS_AS u32x4*>(ds + 32 * ib * D + r_rd[s]);
+        keep[ib] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) keep[ib] = mfma_qk<BF16>(fd[s], kvf[s], keep[ib]);
+      }
     }
+  };
+  // After the barrier: dV^T += dO^T P (P-wave), or dS = P (dP - delta) and
+  // dK^T += Q^T dS (D-wave); contraction over the block's rows.
+  auto phase2 = [&](auto role_c, const LDS_AS uint16_t* qs, const LDS_AS uint16_t* ds,
+                    const LDS_AS float* rs) __attribute__((always_inline)) {
+    if constexpr (decltype(role_c)::value == 0) {
 #pragma unroll
-    for (int ib = 0; ib < BQ / 32; ++ib) {
-      // P and dS; lane value r is query row 8(r/4) + 4hi + r%4 of the block.
-      float p[16], t[16];
+      for (int ib = 0; ib < BQ / 32; ++ib)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int rloc = 32 * ib + 8 * grp + 4 * hi;  // first of 4 consecutive rows
-        const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + rloc);
-        const f32x4 t4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + BQ + rloc);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 td[D / 32];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[4 * grp + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ib][4 * grp + e], a.c, l4[e]));
-          t[4 * grp + e] = t4[e];
+          for (int db = 0; db < D / 32; ++db) td[db] = tr_frag(ds, (32 * ib + 16 * s2) * D, db);
+          const u32x4 pf = {__float_as_uint(keep[ib][4 * s2]), __float_as_uint(keep[ib][4 * s2 + 1]),
+                            __float_as_uint(keep[ib][4 * s2 + 2]), __float_as_uint(keep[ib][4 * s2 + 3])};
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) acc[db] = mfma_qk<BF16>(td[db], pf, acc[db]);
         }
-      }
-      // The mask only on blocks that cross the diagonal of this wave's keys
-      // (a wave-uniform branch; dq is exact whenever it is taken).
-      if (CAUSAL && jw + 31 > i0 + 32 * ib + a.causal_off) {
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[r] = dq >= -(32 * ib + 8 * (r >> 2) + (r & 3)) ? p[r] : 0.f;
-      }
-      // Values r = 8 s2 + j go to operand s2, slot j (the forward's P layout).
-      u32x4 pf[2], sf[2];
+      for (int ib = 0; ib < BQ / 32; ++ib) {
+        u32x4 sf[2];
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int r = 2 * w;
-        pf[w >> 2][w & 3] = pack_in<BF16>(p[r], p[r + 1]);
-        sf[w >> 2][w & 3] = pack_in<BF16>(p[r] * (dp[ib][r] - t[r]),
-                                          p[r + 1] * (dp[ib][r + 1] - t[r + 1]));
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the block's rows).
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 td[D / 32], tq[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          td[db] = tr_frag(ds, (32 * ib + 16 * s2) * D, db);
-          tq[db] = tr_frag(qs, (32 * ib + 16 * s2) * D, db);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 p4 = xch[(ib * 4 + q) * 64];
+          const f32x4 t4 = *reinterpret_cast<const LDS_AS f32x4*>(rs + BQ + 32 * ib + 8 * q + 4 * hi);
+          // values r = 4q .. 4q+3: operand q / 2, slots 4(q % 2) ..
+          sf[q >> 1][2 * (q & 1)] = pack_in<BF16>(p4[0] * (keep[ib][4 * q] - t4[0]),
+                                                   p4[1] * (keep[ib][4 * q + 1] - t4[1]));
+          sf[q >> 1][2 * (q & 1) + 1] = pack_in<BF16>(p4[2] * (keep[ib][4 * q + 2] - t4[2]),
+                                                       p4[3] * (keep[ib][4 * q + 3] - t4[3]));
         }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mfma_qk<BF16>(td[db], pf[s2], dv[db]);
-          dk[db] = mfma_qk<BF16>(tq[db], sf[s2], dk[db]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 tq[D / 32];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) tq[db] = tr_frag(qs, (32 * ib + 16 * s2) * D, db);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) acc[db] = mfma_qk<BF16>(tq[db], sf[s2], acc[db]);
         }
       }
     }
@@ -321,37 +363,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   LDS_AS uint16_t* const Qs[2] = {(LDS_AS uint16_t*)q_lds0, (LDS_AS uint16_t*)q_lds1};
   LDS_AS uint16_t* const Ds[2] = {(LDS_AS uint16_t*)do_lds0, (LDS_AS uint16_t*)do_lds1};
   LDS_AS float* const Rs[2] = {(LDS_AS float*)rs_lds0, (LDS_AS float*)rs_lds1};
-  Pos cur{hk * a.group, qt0};
-  Pos nxt = advance(cur);
-  if (steps > 0) issue(cur, Qs[0], Ds[0], Rs[0]);
-  auto iteration = [&](int u, auto par) __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (u + 1 < steps) issue(nxt, Qs[P ^ 1], Ds[P ^ 1], Rs[P ^ 1]);
-    const int i0 = cur.t * BQ;
-    // Skip a tile whose queries all precede this wave's keys.
-    if (!CAUSAL || i0 + BQ - 1 >= jw - a.causal_off) compute(i0, Qs[P], Ds[P], Rs[P]);
-    cur = nxt;
-    nxt = advance(nxt);
+  // Two barriers per tile: the first makes the tile's DMA visible and frees
+  // the other buffers (and the P exchange) from the previous tile; the
+  // second hands P from the P-waves to the D-waves.  Each role runs its own
+  // copy of the loop (same trip count, same barriers), so the registers of
+  // one role's work are not held across the other's.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    Pos cur{hk * a.group, qt0};
+    Pos nxt = advance(cur);
+    if (steps > 0) issue(cur, Qs[0], Ds[0], Rs[0]);
+    auto iteration = [&](int u, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (u + 1 < steps) issue(nxt, Qs[P ^ 1], Ds[P ^ 1], Rs[P ^ 1]);
+      const int i0 = cur.t * BQ;
+      // Skip a tile whose queries all precede the pair's keys (pair-uniform).
+      const bool active = !CAUSAL || i0 + BQ - 1 >= jw - a.causal_off;
+      if (active) phase1(role_c, i0, Qs[P], Ds[P], Rs[P]);
+      __syncthreads();
+      if (active) phase2(role_c, Qs[P], Ds[P], Rs[P]);
+      cur = nxt;
+      nxt = advance(nxt);
+    };
+    for (int u = 0; u < steps; u += 2) {
+      iteration(u, std::integral_constant<int, 0>{});
+      if (u + 1 < steps) iteration(u + 1, std::integral_constant<int, 1>{});
+    }
   };
-  for (int u = 0; u < steps; u += 2) {
-    iteration(u, std::integral_constant<int, 0>{});
-    if (u + 1 < steps) iteration(u + 1, std::integral_constant<int, 1>{});
-  }
+  if (role == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
-  // dK = scale dS^T Q, dV = P^T dO; lane holds row jl, d = 32db + 8g + 4hi .. +3.
+  // dV = P^T dO (P-wave), dK = scale dS^T Q (D-wave); lane holds row jl,
+  // d = 32db + 8g + 4hi .. +3.
   if (k_ok) {
     const int64_t row = kv_base + (int64_t)jl * a.k_ss;
+    void* const dst = role == 0 ? a.dv : a.dk;
+    const float f = role == 0 ? 1.f : a.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * hi;
-        store4<BF16, OF32>(a.dk, row + d0, reinterpret_cast<const float*>(&dk[db]) + 4 * g,
-                           a.scale);
-        store4<BF16, OF32>(a.dv, row + d0, reinterpret_cast<const float*>(&dv[db]) + 4 * g, 1.f);
-      }
+      for (int g = 0; g < 4; ++g)
+        store4<BF16, OF32>(dst, row + 32 * db + 8 * g + 4 * hi,
+                           reinterpret_cast<const float*>(&acc[db]) + 4 * g, f);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -553,7 +609,7 @@ hipError_t launch_t(BackwardArgs a, hipStream_t s) {
   ak.n_tiles = (a.Skv + 127) / 128;
   ak.total = a.B * a.H_kv * ak.n_tiles;
   if (ak.total > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, OF32>), dim3(ak.total), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, OF32>), dim3(ak.total), dim3(512), 0, s,
                        ak);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
