@@ -89,16 +89,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// One fp32 -> fp16/bf16 bits, round to nearest even (hardware conversions).
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_out(float f) {
-  if constexpr (BF16) return (uint16_t)bf16_bits(f);
+  if constexpr (BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
   else return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 

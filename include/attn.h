@@ -1,14 +1,16 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused-attention library.
  *
- * Two operations, both the plain scaled-dot-product attention
+ * Scaled-dot-product attention
  *
  *     O[b,h,i,:] = sum_j softmax_j(scale * <q_i, k_j> + M_ij) * v_j
  *
- * (flash-style prefill: "WAVE: A Symbolic Python DSL and Compiler for High
- * Performance Machine Learning (MLSys 2026)", core method, and its attention
- * experiments over BHSD and BSHD layouts; paged flash decoding: "Wave February
- * 2025 Release", FlashDecoding list).
+ * as a flash-style prefill ("WAVE: A Symbolic Python DSL and Compiler for
+ * High Performance Machine Learning (MLSys 2026)", core method, and its
+ * attention experiments over BHSD and BSHD layouts) and as paged flash
+ * decoding ("Wave February 2025 Release", FlashDecoding list), with grouped
+ * KV heads, extend attention after a paged prefix, fp8 inputs, and the
+ * backward pass of the prefill (roadmap items of the same release).
  *
  * Conventions for every entry point:
  *   - Every pointer is a device pointer owned by the caller.  The library never
@@ -38,7 +40,7 @@ enum {
   ATTN_OK = 0,
   ATTN_E_INVALID = 1,      /* null pointer, negative size, bad scale, misaligned pointer */
   ATTN_E_UNSUPPORTED = 2,  /* valid request this build does not implement (head dim, page size) */
-  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than attn_paged_decode_workspace_size */
+  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than the entry point's *_workspace_size */
   ATTN_E_HIP = 4           /* the HIP runtime reported an error at launch */
 };
 
