@@ -59,16 +59,18 @@ __device__ __forceinline__ float hi_f32(uint32_t w) {
   else return (float)__builtin_bit_cast(f16x2, w)[1];
 }
 
-// fp32 dot product of two packed 2-element vectors, accumulated into c.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 dot product of two packed 2-element vectors, accumulated into c
+// (v_dot2_f32_f16 / v_dot2_f32_bf16: exact products, fp32 sum).
 template <bool BF16>
 __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float c) {
-  if constexpr (BF16) {
-    c = __builtin_fmaf(lo_f32<true>(x), lo_f32<true>(y), c);
-    return __builtin_fmaf(hi_f32<true>(x), hi_f32<true>(y), c);
-  } else {
+  if constexpr (BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                           __builtin_bit_cast(bf16x2_t, y), c, false);
+  else
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), c,
                                   false);
-  }
 }
 
 template <int CTRL>
