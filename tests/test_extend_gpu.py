@@ -40,7 +40,7 @@ CASES = [  # (prefix_lens, extend_lens)
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("H,H_kv", [(8, 8), (8, 2), (6, 1)])
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (8, 2), (6, 1), (16, 2), (32, 1)])
 @pytest.mark.parametrize("D,dtype", [(128, "bf16"), (128, "f16"), (64, "f16"), (64, "bf16")])
 def test_extend_parity_nan_poisoned(gpu_lib, case, H, H_kv, D, dtype):
     pl, el = CASES[case]
