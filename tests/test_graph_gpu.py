@@ -53,3 +53,71 @@ def test_graph_capture_and_replay(gpu_lib):
         assert torch.equal(o_pre, ref_pre), f"prefill replay {i}"
         assert torch.equal(o_dec, ref_dec), f"decode replay {i}"
         _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_graph_capture_backward_extend_fp8(gpu_lib):
+    """The other entry points in one captured graph: forward with LSE,
+    backward, extend after a paged prefix, fp8 prefill and grouped-query
+    decode, replayed three times against the eager results."""
+    attn = gpu_lib
+    dev = torch.device("cuda")
+    q, k, v, do = (t.to(dev) for t in workloads.backward_inputs(1, 8, 200, 260, 128, "bf16",
+                                                                "BSHD", amp=0.5, seed=33,
+                                                                h_kv=2))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 8, 200), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(attn.attn_prefill_bwd_workspace_size(1, 8, 200), dtype=torch.uint8,
+                      device=dev)
+    e = workloads.extend_inputs(3, 8, 128, [5, 0, 40], [30, 17, 9], "f16", seed=34, h_kv=2)
+    ge = {n: getattr(e, n).to(dev) for n in ("q", "k", "v", "k_cache", "v_cache", "page_table",
+                                             "prefix_lens", "qo_start")}
+    o_ext = torch.empty_like(ge["q"])
+    q8, k8, v8, desc = workloads.prefill_inputs_fp8(1, 4, 130, 150, 128, seed=35, h_kv=1)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o8 = torch.empty(q8.shape, dtype=torch.float16, device=dev)
+    b = workloads.paged_decode_inputs(B=4, H=16, D=128, page_size=16, num_pages=256,
+                                      max_seq=700, seed=36, h_kv=4)
+    gd = {n: getattr(b, n).to(dev) for n in ("q", "k_cache", "v_cache", "page_table", "seq_lens")}
+    dws = torch.empty(attn.attn_paged_decode_gqa_workspace_size(4, 16, 4, 128, b.max_pages_per_seq,
+                                                                16),
+                      dtype=torch.uint8, device=dev)
+    o_dec = torch.empty_like(gd["q"])
+    outs = (o, lse, dq, dk, dv, o_ext, o8, o_dec)
+
+    def work(stream=None):
+        attn.prefill_with_lse(q, k, v, causal=True, layout="BSHD", out=o, lse=lse, stream=stream)
+        attn.prefill_backward(q, k, v, o, do, lse, causal=True, layout="BSHD", dq=dq, dk=dk,
+                              dv=dv, workspace=bws, stream=stream)
+        attn.extend(ge["q"], ge["k"], ge["v"], ge["k_cache"], ge["v_cache"], ge["page_table"],
+                    ge["prefix_lens"], ge["qo_start"], max_extend_len=e.max_extend_len,
+                    out=o_ext, stream=stream)
+        attn.prefill_fp8(q8, k8, v8, desc, causal=True, out=o8, stream=stream)
+        attn.paged_decode(gd["q"], gd["k_cache"], gd["v_cache"], gd["page_table"],
+                          gd["seq_lens"], out=o_dec, workspace=dws, stream=stream)
+
+    print("[case] graph capture of lse/backward/extend/fp8/gqa decode", flush=True)
+    work()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outs]
+
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in outs:
+            t.zero_()
+        with torch.cuda.graph(graph, stream=s):
+            work(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, (t, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(t, r), f"output {n}, replay {i}"
+        _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
