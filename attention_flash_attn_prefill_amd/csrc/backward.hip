@@ -8,21 +8,24 @@
 //   dQ = scale dS K,         dK = scale dS^T Q.
 //
 // Three kernels:
-//   * delta: rowsum(dO * O) in fp32 (one 16-byte load per lane per tensor).
-//   * dK/dV: one workgroup per (batch, KV head, 128 keys), four waves of 32
-//     keys.  A wave keeps its keys' K and V as MFMA operands and dK^T, dV^T as
-//     fp32 accumulators in registers for the whole pass; tiles of 64 queries of
-//     every query head that shares the KV head stream through LDS (Q, dO by
-//     DMA, double-buffered, plus their LSE and delta), so grouped heads sum
-//     into dK, dV without atomics.  S = Q K^T and dP = dO V^T come out with a
-//     lane per key and rows of queries, which is the B-operand layout of
+//   * delta: per query row, rowsum(dO * O) and -LSE log2(e) in fp32 (one
+//     16-byte load per lane per tensor).
+//   * dK/dV: one workgroup per (batch, KV head, 128 keys), four pairs of
+//     waves, a pair per 32 keys.  The pair keeps its keys' K (one wave) and V
+//     (the other) as MFMA operands and dV^T, dK^T as fp32 accumulators in
+//     registers for the whole pass; tiles of 64 queries of every query head
+//     that shares the KV head stream through LDS (Q, dO by DMA,
+//     double-buffered, plus their LSE and delta), so grouped heads sum into
+//     dK, dV without atomics.  S = Q K^T and dP = dO V^T come out with a lane
+//     per key and rows of queries, which is the B-operand layout of
 //     dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T) are read
-//     by transposing LDS reads.  The register file holds this (one wave per
-//     SIMD, up to 512 registers).
+//     by transposing LDS reads; P passes from one wave of the pair to the
+//     other through LDS.
 //   * dQ: one workgroup per (batch, head, 256 queries), eight waves of 32
 //     queries (the forward kernel's shape): Q and dO stay as operands, tiles
-//     of 32 keys stream through LDS, S^T = K Q^T and dP^T = V dO^T give a lane
-//     per query, and dQ^T += K^T dS^T with K^T by transposing reads.
+//     of 64 keys stream through LDS (used as two 32-key halves), S^T = K Q^T
+//     and dP^T = V dO^T give a lane per query, and dQ^T += K^T dS^T with K^T
+//     by transposing reads.
 // Recomputing S and dP in both kernels costs two extra products over the
 // five of the algorithm but needs no fp32 atomics: the gradients are
 // deterministic.  The operand layouts, swizzle and transposing-read offsets
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;           // queries per workgroup
-  constexpr int BN = 32;                // keys per streamed tile
+  constexpr int BN = 64;                // keys per streamed tile (two 32-key halves)
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / NT;
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly over the threads");
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
 
-  auto compute = [&](int t, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) __attribute__((always_inline)) {
+  auto compute_half = [&](int kv0, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) __attribute__((always_inline)) {
     // S^T = K Q^T and dP^T = V dO^T: 32 keys (rows) x 32 queries (lane).
     u32x4 fk[D / 16];
 #pragma unroll
@@ -528,9 +531,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
     f32x16 dp = (f32x16){};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) dp = mfma_qk<BF16>(fv[s], df[s], dp);
-    // dS^T = P^T (dP^T - delta); value r is key t BN + 8(r/4) + 4hi + r%4.
-    const int kv0 = t * BN;
-    const bool need_mask = (kv0 + BN > a.Skv) || (CAUSAL && kv0 + BN - 1 > q0 + a.causal_off);
+    // dS^T = P^T (dP^T - delta); value r is key kv0 + 8(r/4) + 4hi + r%4.
+    const bool need_mask = (kv0 + 32 > a.Skv) || (CAUSAL && kv0 + 31 > q0 + a.causal_off);
     const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
     u32x4 sf[2];
 #pragma unroll
@@ -565,6 +567,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma_qk<BF16>(tk[db], sf[s2], acc[db]);
     }
+  };
+  // A 64-key tile as two 32-key halves (one barrier per 64 keys); the second
+  // half only if the wave sees one of its keys (wave-uniform).
+  auto compute = [&](int t, const LDS_AS uint16_t* ks, const LDS_AS uint16_t* vs) __attribute__((always_inline)) {
+    compute_half(t * BN, ks, vs);
+    if (t * BN + 32 < wave_kv_end) compute_half(t * BN + 32, ks + 32 * D, vs + 32 * D);
   };
 
   LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
