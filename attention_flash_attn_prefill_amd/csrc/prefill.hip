@@ -97,6 +97,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[BN * D];
+  __shared__ int ext_seq;  // extend: the sequence this workgroup works on
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,7 +124,29 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   int mt = L % a.n_mtiles;
   L /= a.n_mtiles;
   if (CAUSAL) mt = a.n_mtiles - 1 - mt;  // heaviest query tiles first
-  const int hk = L % a.H_kv, b = L / a.H_kv;
+  const int hk = L % a.H_kv;
+  int b = L / a.H_kv;
+  if constexpr (EXT) {
+    // Longest prefix first: the work order takes sequences by rank of their
+    // prefix length (descending, ties by index), so the longest work items of
+    // a ragged batch start first instead of last.  Thread t ranks sequence t
+    // and the one whose rank is this workgroup's sequence slot publishes it.
+    // Only for small batches (B <= 64: at most 64 uniform loads per thread).
+    const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv);
+    if (nb > 1 && nb <= 64) {
+      if (tid < nb) {
+        const int pt = a.prefix_lens[tid];
+        int rank = 0;
+        for (int u = 0; u < nb; ++u) {
+          const int pu = a.prefix_lens[u];
+          rank += (pu > pt) || (pu == pt && u < tid);
+        }
+        if (rank == b) ext_seq = tid;
+      }
+      __syncthreads();
+      b = ext_seq;
+    }
+  }
   const int h = hk * a.group + gg * HPW + wave / WPH;  // wave-uniform
 
   // Sequence sizes.  Extend: Sq = the sequence's new tokens, Skv = prefix +
