@@ -74,6 +74,39 @@ SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
   return p;
 }
 
+// Grouped-query plan (group > 1, decode_gqa.hip): lines = B x H_kv x
+// ceil(group / 32), each holding its sequence's 32-token tiles; the tiles of
+// all lines are cut into W equal ranges on the device, W = min(ranges,
+// ceil(NT / min_tiles)) for the batch's actual tile count NT.  A range writes
+// one partial row per query of the chunk for every line it touches, so it
+// covers at least min(group, 32) / 2 tiles (partials <= ~6% of its K/V
+// bytes).  Slots = ranges + lines bound the (range, line) pairs.
+struct GqaPlan {
+  int ranges, min_tiles, rows_per_slot;
+  int64_t lines, slots;
+};
+GqaPlan plan_gqa(int B, int H, int H_kv, int max_pages, int page_size) {
+  GqaPlan p{0, 0, 0, 0, 0};
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || H == H_kv || max_pages <= 0 ||
+      page_size != kDecodePageSize)
+    return p;
+  const int group = H / H_kv;
+  p.rows_per_slot = group < 32 ? group : 32;
+  p.min_tiles = p.rows_per_slot > 1 ? p.rows_per_slot / 2 : 1;
+  p.lines = (int64_t)B * H_kv * ((group + 31) / 32);
+  const int64_t max_tiles = ((int64_t)max_pages * page_size + 31) / 32;
+  const int64_t nt_max = p.lines * max_tiles;
+  if (nt_max >= ((int64_t)1 << 31) || (int64_t)B * H >= ((int64_t)1 << 31) ||
+      (int64_t)max_pages * page_size >= ((int64_t)1 << 31))
+    return GqaPlan{};
+  const int64_t by_size = (nt_max + p.min_tiles - 1) / p.min_tiles;
+  p.ranges = (int)(by_size < kDecodeRanges ? by_size : kDecodeRanges);
+  p.slots = p.ranges + p.lines;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -351,6 +384,11 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
 
 int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
                                      int page_size, int* tokens_per_split) {
+  if (H_kv > 0 && H > H_kv) {
+    const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+    if (tokens_per_split) *tokens_per_split = g.min_tiles * 32;
+    return g.ranges;
+  }
   const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
   if (tokens_per_split) *tokens_per_split = p.tokens_per_split;
   return p.n_splits;
@@ -365,6 +403,15 @@ int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_s
 size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D, int max_pages_per_seq,
                                             int page_size) {
   if (D != 64 && D != 128) return 0;
+  if (H_kv > 0 && H > H_kv) {
+    // partial outputs [slots, rows, D], log-sum-exps [slots, rows], then the
+    // range metadata (B + 3 ints), each 256-B aligned
+    const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+    if (g.ranges == 0) return 0;
+    const size_t rows = (size_t)g.slots * g.rows_per_slot;
+    return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) +
+           ((size_t)B + 3) * sizeof(int);
+  }
   const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
   if (p.n_splits == 0) return 0;
   const size_t rows = (size_t)B * H * p.n_splits;
@@ -391,25 +438,29 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
   if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
   if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H == 0) return ATTN_OK;
+  if ((int64_t)max_pages_per_seq * page_size >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;  // token positions are 32-bit
   if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
   const int group = H / H_kv;
   const int qchunks = (group + 31) / 32;
-  if (group == 1 ? B > 65535 : (int64_t)B * H_kv * qchunks >= ((int64_t)1 << 31))
-    return ATTN_E_UNSUPPORTED;  // grid limits
+  if (group == 1 && B > 65535) return ATTN_E_UNSUPPORTED;  // grid limit
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return ATTN_E_INVALID;
   if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
 
-  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
-  if (p.n_splits == 0 || p.n_splits > 65535) return ATTN_E_UNSUPPORTED;
+  const SplitPlan p = group == 1 ? plan_splits(B, H, H_kv, max_pages_per_seq, page_size)
+                                 : SplitPlan{0, 0};
+  const GqaPlan g = group == 1 ? GqaPlan{} : plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+  if (group == 1 ? (p.n_splits == 0 || p.n_splits > 65535) : g.ranges == 0)
+    return ATTN_E_UNSUPPORTED;  // grid or index limits
   const size_t need =
       attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size);
   if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_E_INVALID;
 
-  const size_t rows = (size_t)B * H * p.n_splits;
-  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
+  const size_t rows = group == 1 ? (size_t)B * H * p.n_splits : (size_t)g.slots * g.rows_per_slot;
+  const size_t o_bytes = align256(rows * D * sizeof(float));
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -419,14 +470,18 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
   a.o = o;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  a.meta = reinterpret_cast<int*>(static_cast<char*>(workspace) + o_bytes +
+                                  align256(rows * sizeof(float)));
   a.B = B;
   a.H = H;
   a.H_kv = H_kv;
   a.group = group;
   a.qchunks = qchunks;
   a.max_pages = max_pages_per_seq;
-  a.n_splits = p.n_splits;
+  a.n_splits = group == 1 ? p.n_splits : g.ranges;
   a.tokens_per_split = p.tokens_per_split;
+  a.min_tiles = g.min_tiles;
+  a.rows_per_slot = g.rows_per_slot;
   a.num_pages = num_pages;
   a.c = exp2_multiplier(scale);
   hipError_t e = group == 1 ? launch_paged_decode(D, bf16, out_f32, a, stream)

@@ -36,6 +36,13 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// One fp32 -> fp16/bf16 bits, round to nearest even (hardware conversions).
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_out(float f) {
+  if constexpr (BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
+  else return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // Max / sum of a value with the same value in lane ^ 32.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -80,6 +80,10 @@ hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, i
 // split, chunk of up to 32 query heads of the group).
 constexpr int kDecodeHeadsPerWG = 4;
 constexpr int kDecodePageSize = 16;
+// Grouped-query decode: the batch's KV tiles are cut into at most this many
+// equal ranges, one wave each -- the waves one launch keeps resident on 256
+// CUs at eight per CU, so all of them start at once.
+constexpr int kDecodeRanges = 2048;
 
 struct DecodeArgs {
   const uint16_t* q;          // [B, H, D]
@@ -88,10 +92,16 @@ struct DecodeArgs {
   const int32_t* page_table;  // [B, max_pages]
   const int32_t* seq_lens;    // [B]
   void* o;                    // [B, H, D], dtype of q or fp32 (out_f32)
-  float* part_o;              // [B, H, n_splits, D]   (workspace)
-  float* part_lse;            // [B, H, n_splits]      (workspace; log2 domain)
-  int B, H, max_pages, n_splits, tokens_per_split;
+  // Partials (workspace).  group = 1: [B, H, n_splits, D] and [B, H, n_splits]
+  // (log2 domain).  group > 1: [slots, rows_per_slot, D] and [slots,
+  // rows_per_slot], slot = work range + line; meta = {NT, W, first tile of
+  // each sequence (B + 1 entries)}.
+  float* part_o;
+  float* part_lse;
+  int* meta;
+  int B, H, max_pages, n_splits, tokens_per_split;  // group > 1: n_splits = max work ranges
   int H_kv, group, qchunks;   // qchunks = ceil(group / 32)
+  int min_tiles, rows_per_slot;  // group > 1: tiles per range at least; min(group, 32)
   int num_pages;              // page ids outside [0, num_pages) are rejected on the device
   float c;                    // scale * log2(e)
 };

@@ -284,7 +284,11 @@ def bench_decode(attn, cfg, steps, warmup, clock):
     cfg_out = {"workload": batch.meta["name"], "B": B, "H": H, "H_kv": H_kv, "D": D,
                "dtype": batch.meta["dtype"],
                "page_size": batch.page_size, "num_pages": batch.num_pages,
-               "live_tokens": n_tok, "n_splits": n_splits, "tokens_per_split": tps}
+               "live_tokens": n_tok}
+    if H_kv == H:
+        cfg_out.update(n_splits=n_splits, tokens_per_split=tps)
+    else:  # tiles of the whole batch cut into equal ranges on the device
+        cfg_out.update(max_work_ranges=n_splits, min_tokens_per_range=tps)
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM, 4),
             "traffic": load_traffic(f"decode_split__{batch.meta['name']}", DECODE_SRC) if H_kv == H

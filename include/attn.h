@@ -262,6 +262,14 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
  * Arithmetic for H_kv < H: Q.K^T on MFMA in the input dtype with fp32
  * accumulation, softmax in fp32, P rounded to fp16 and P.V on fp16 MFMA
  * (bf16 V converted to fp16 on staging, as in attn_prefill).
+ * Work division for H_kv < H: instead of fixed per-sequence splits, the
+ * batch's 32-token tiles, taken sequence by sequence and KV head by KV head,
+ * are cut on the device into W equal contiguous ranges (W at most
+ * attn_paged_decode_gqa_num_splits, fewer for short batches), one wave each;
+ * a range that crosses sequences writes one partial per sequence and KV head
+ * it touches, and the log-sum-exp combine merges them (flash decoding with
+ * the KV split sized to fill the GPU, as above).  The workspace also holds
+ * the range metadata, rewritten by every call.
  */
 int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* page_table, const int32_t* seq_lens, void* o,
@@ -273,7 +281,11 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
 size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D,
                                             int max_pages_per_seq, int page_size);
 
-/* Split plan of attn_paged_decode_gqa (see attn_paged_decode_num_splits). */
+/* Work plan of attn_paged_decode_gqa.  H_kv = H: the multi-head split plan
+ * (see attn_paged_decode_num_splits).  H_kv < H: returns the largest number
+ * of work ranges W a call uses (0 on invalid sizes) and stores in
+ * tokens_per_split the fewest tokens a range covers unless the batch holds
+ * fewer: 16 per query head of the group, at most 512, at least 32. */
 int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
                                      int page_size, int* tokens_per_split);
 

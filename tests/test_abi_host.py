@@ -223,18 +223,23 @@ def test_gqa_split_plan_and_workspace():
         attn.attn_paged_decode_num_splits(64, 32, 512, 16)
     assert attn.attn_paged_decode_gqa_workspace_size(64, 32, 32, 128, 512, 16) == \
         attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
-    n, tps = attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16)
-    assert tps % 64 == 0 and tps >= 64 and n == math.ceil(512 * 16 / tps)
-    # one wave per (sequence, KV head, split): at least 8192 of them, or 64-token splits
-    assert 64 * 8 * n >= 8192 or tps == 64
-    ws = attn.attn_paged_decode_gqa_workspace_size(64, 32, 8, 128, 512, 16)
-    assert ws >= 64 * 32 * n * 129 * 4            # partials per query head
-    # 32 query heads per KV head: splits of at least 16 tokens per query head
-    # (512), so the per-head partial rows stay a few percent of the K/V bytes
-    assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (16, 512)
-    assert attn.attn_paged_decode_gqa_num_splits(1, 8, 1, 512, 16)[1] == 128
+    # H_kv < H: (work ranges, tokens per range at least).  The batch's tiles
+    # are cut into at most 2048 equal ranges (one resident wave each), each
+    # covering at least min(group, 32) / 2 tiles of 32 tokens, so a range's
+    # partial rows (one per query of the group) stay a few percent of its K/V
+    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16) == (2048, 64)
+    assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (2048, 512)
+    assert attn.attn_paged_decode_gqa_num_splits(1, 8, 1, 512, 16) == (64, 128)
+    assert attn.attn_paged_decode_gqa_num_splits(2, 64, 1, 100, 16) == (13, 512)
     assert attn.attn_paged_decode_gqa_num_splits(4, 6, 4, 8, 16) == (0, 0)
+    # partial rows for every (range, line) pair a call can touch: at most
+    # ranges + lines of them, min(group, 32) rows of D + 1 floats each
+    lines = 64 * 8
+    ws = attn.attn_paged_decode_gqa_workspace_size(64, 32, 8, 128, 512, 16)
+    assert ws >= (2048 + lines) * 4 * 129 * 4 + (64 + 3) * 4
     assert attn.attn_paged_decode_gqa_workspace_size(4, 8, 2, 96, 8, 16) == 0
+    # token positions must fit 32 bits
+    assert attn.attn_paged_decode_gqa_num_splits(1, 8, 1, 1 << 27, 16) == (0, 0)
 
 
 def _decode(**kw):

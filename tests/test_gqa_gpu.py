@@ -147,3 +147,92 @@ def test_decode_gqa_full_config(gpu_lib, cfg):
     ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
                               batch.seq_lens, scale=batch.meta["scale"], batch_indices=sel)
     assert_parity(_f64(o[sel]), ref, f"config {cfg} ({len(sel)} sequences, all heads)")
+
+
+# Grouped-query decode cuts the batch's 32-token tiles (line after line, a
+# line = one sequence's tiles for one KV head) into equal ranges, one wave
+# each; a range may end inside a line and run on into the next ones.  These
+# cases put range ends everywhere: inside lines, on line and sequence
+# boundaries, past empty sequences.
+
+def _lens_batch(lens, H, H_kv, seed, D=128, dtype="f16", **kw):
+    pages = sum(-(-max(n, 0) // 16) for n in lens)
+    return workloads.paged_decode_inputs(B=len(lens), H=H, D=D, dtype=dtype, page_size=16,
+                                         num_pages=pages + 64, seq_lens=lens, seed=seed,
+                                         h_kv=H_kv, **kw)
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (32, 1), (64, 1)])
+def test_decode_gqa_ranges_mixed_lengths(gpu_lib, H, H_kv):
+    """700 sequences (more than one pass of the length scan) mixing empty,
+    one-token, page-edge and long ones: every head against the oracle, and
+    O = 0 exactly for the empty sequences."""
+    rng = np.random.default_rng(H + H_kv)
+    lens = rng.choice([0, 1, 16, 17, 33, 100, 512, 513, 2000], size=700).tolist()
+    batch = _lens_batch(lens, H, H_kv, seed=75 + H)
+    print(f"[case] decode_gqa ranges H{H}/{H_kv} B700 mixed lengths", flush=True)
+    o = _decode(gpu_lib, batch)
+    live = [b for b, n in enumerate(lens) if n > 0]
+    empty = [b for b, n in enumerate(lens) if n == 0]
+    assert empty and torch.count_nonzero(o[empty]) == 0
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, batch_indices=live)
+    assert_parity(_f64(o[live]), ref, f"decode gqa ranges H{H}/{H_kv} mixed lengths")
+
+
+@pytest.mark.parametrize("lens,H,H_kv", [([60000], 32, 1), ([0, 37000, 0], 64, 1),
+                                         ([5, 30000], 16, 2)])
+def test_decode_gqa_ranges_long_sequences(gpu_lib, lens, H, H_kv):
+    """Few long sequences: one line spread over many ranges (up to a hundred
+    partials merged per head), two query chunks per KV head (group 64)."""
+    batch = _lens_batch(lens, H, H_kv, seed=76 + H, dtype="bf16")
+    print(f"[case] decode_gqa ranges H{H}/{H_kv} long {lens}", flush=True)
+    o = _decode(gpu_lib, batch)
+    live = [b for b, n in enumerate(lens) if n > 0]
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, batch_indices=live)
+    assert_parity(_f64(o[live]), ref, f"decode gqa ranges long {lens}")
+    assert torch.count_nonzero(o[[b for b, n in enumerate(lens) if n == 0]]) == 0
+
+
+def test_decode_gqa_ranges_workspace_reused(gpu_lib):
+    """The range metadata is rewritten by every call: a workspace used for a
+    batch of long sequences, then for the same sizes with mostly empty ones,
+    gives bitwise what a fresh workspace gives."""
+    attn = gpu_lib
+    long_b = _lens_batch([4000] * 24, 32, 4, seed=77)
+    short_lens = [0] * 24
+    short_lens[5], short_lens[17] = 70, 1
+    short_b = workloads.paged_decode_inputs(B=24, H=32, D=128, page_size=16,
+                                            num_pages=long_b.num_pages, seq_lens=short_lens,
+                                            max_pages_per_seq=long_b.max_pages_per_seq, seed=78,
+                                            h_kv=4)
+    need = attn.attn_paged_decode_gqa_workspace_size(24, 32, 4, 128, long_b.max_pages_per_seq, 16)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    print("[case] decode_gqa ranges workspace reuse", flush=True)
+    _decode(attn, long_b, workspace=ws)
+    again = _decode(attn, short_b, workspace=ws)
+    fresh = _decode(attn, short_b)
+    assert torch.equal(again, fresh)
+    ref = oracle.paged_decode(short_b.q, short_b.k_cache, short_b.v_cache, short_b.page_table,
+                              short_b.seq_lens, batch_indices=[5, 17])
+    assert_parity(_f64(fresh[[5, 17]]), ref, "decode gqa after workspace reuse")
+
+
+def test_decode_gqa_ranges_bad_page_in_long_sequence(gpu_lib):
+    """A bad page id deep inside a sequence that spans several ranges makes
+    every head of that sequence NaN and leaves the others exact."""
+    lens = [3000, 9000, 20, 5000]
+    batch = _lens_batch(lens, 32, 1, seed=79, max_pages_per_seq=600)
+    table = batch.page_table.clone()
+    table[1, 400] = batch.num_pages + 3
+    print("[case] decode_gqa ranges bad page in a long sequence", flush=True)
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k_cache", "v_cache", "seq_lens")}
+    o = gpu_lib.paged_decode(g["q"], g["k_cache"], g["v_cache"], table.cuda(),
+                             g["seq_lens"]).float().cpu()
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1]).all()
+    assert torch.isfinite(o[[0, 2, 3]]).all()
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, batch_indices=[0, 2, 3])
+    assert_parity(_f64(o[[0, 2, 3]]), ref, "gqa sequences around the bad one")
