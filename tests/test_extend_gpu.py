@@ -137,3 +137,51 @@ def test_extend_full_config9_sampled(gpu_lib):
     ref = _ref(batch, scale=batch.meta["scale"], seqs=seqs)
     rows = [r for b in seqs for r in range(int(batch.qo_start[b]), int(batch.qo_start[b + 1]))]
     assert_parity(o[rows].double().numpy(), ref[rows], f"config 9 ({len(rows)} rows of {seqs})")
+
+
+def _permuted(batch, perm):
+    """The same sequences in another batch order: new-token rows regrouped,
+    prefix lengths and page-table rows moved with them, the cache unchanged."""
+    s = batch.qo_start.tolist()
+    rows = [r for b in perm for r in range(s[b], s[b + 1])]
+    lens = [s[b + 1] - s[b] for b in perm]
+    starts = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    return workloads.ExtendBatch(q=batch.q[rows], k=batch.k[rows], v=batch.v[rows],
+                                 k_cache=batch.k_cache, v_cache=batch.v_cache,
+                                 page_table=batch.page_table[perm].contiguous(),
+                                 prefix_lens=batch.prefix_lens[perm].contiguous(),
+                                 qo_start=starts, page_size=batch.page_size, meta=batch.meta)
+
+
+@pytest.mark.parametrize("H,H_kv", [(32, 8), (8, 8)])
+def test_extend_sequence_order_independent_bitwise(gpu_lib, H, H_kv):
+    """Work is taken longest prefix first (ties by batch index) for batches of
+    up to 64 sequences: any batch order, with tied, empty and long prefixes
+    and sequences without new tokens, gives each sequence bitwise the same
+    rows, and those rows match the oracle."""
+    pl = [700, 0, 700, 65, 3000, 700, 1, 0, 1500, 64, 700, 2999]
+    el = [40, 300, 0, 129, 64, 1, 256, 17, 90, 200, 33, 5]
+    batch = workloads.extend_inputs(len(pl), H, 128, pl, el, "bf16", seed=95 + H, h_kv=H_kv)
+    perm = [4, 10, 1, 7, 2, 11, 0, 9, 5, 3, 8, 6]
+    o = _run(gpu_lib, batch)
+    o2 = _run(gpu_lib, _permuted(batch, perm))
+    s = batch.qo_start.tolist()
+    rows = [r for b in perm for r in range(s[b], s[b + 1])]
+    assert torch.equal(o2, o[rows])
+    assert_parity(o.double().numpy(), _ref(batch), f"extend ranked batch H{H}/{H_kv}")
+
+
+def test_extend_many_sequences(gpu_lib):
+    """More than 64 sequences (the plain work order) and 64 exactly (the
+    largest ranked batch), against the oracle on a spread of sequences."""
+    rng = np.random.default_rng(96)
+    for B in (64, 90):
+        pl = rng.integers(0, 600, B).tolist()
+        el = rng.integers(0, 70, B).tolist()
+        batch = workloads.extend_inputs(B, 8, 128, pl, el, "f16", seed=96 + B, h_kv=2)
+        o = _run(gpu_lib, batch)
+        seqs = list(range(0, B, 7)) + [B - 1]
+        ref = _ref(batch, seqs=seqs)
+        s = batch.qo_start.tolist()
+        rows = [r for b in seqs for r in range(s[b], s[b + 1])]
+        assert_parity(o[rows].double().numpy(), ref[rows], f"extend B{B} ({len(seqs)} sequences)")
