@@ -285,8 +285,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
 #pragma unroll
     for (int jj = 1; jj < PPT; ++jj) pg = j == jj ? pg_cur[jj] : pg;
     const uint16_t* base = live > 0 ? cache + (int64_t)pg * page_elems : cache;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
-                                             (int)(max(live, 0) * slot_bytes), kBufferConfig);
+    // The range is wave-uniform; keeping it in an SGPR keeps the compiler
+    // from wrapping every load in a waterfall loop over the lanes (it would
+    // otherwise clamp it with a vector instruction).
+    const int nbytes = __builtin_amdgcn_readfirstlane(max(live, 0) * (int)slot_bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferConfig);
   };
 
   // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
