@@ -532,20 +532,28 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) dp = mfma_qk<BF16>(fv[s], df[s], dp);
     // dS^T = P^T (dP^T - delta); value r is key kv0 + 8(r/4) + 4hi + r%4.
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.c, nl2));
+    // Keys past the end or (causal) above the diagonal, only in the halves
+    // that have any: a wave-uniform branch around the whole pass, so the
+    // other halves carry no per-element compares and selects (the fence has
+    // a side effect, which keeps the compiler from turning the branch into
+    // selects executed on every half).
     const bool need_mask = (kv0 + 32 > a.Skv) || (CAUSAL && kv0 + 31 > q0 + a.causal_off);
-    const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
+    if (need_mask) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int lim = CAUSAL ? min(a.Skv - 1, qi + a.causal_off) : a.Skv - 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv0 + 8 * (r >> 2) + 4 * hi + (r & 3) > lim) p[r] = 0.f;
+    }
     u32x4 sf[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       float d[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * s2 + j;
-        const int key = kv0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.c, nl2));
-        if (need_mask && key > lim) p = 0.f;
-        d[j] = p * (dp[r] - delta);
-      }
+      for (int j = 0; j < 8; ++j) d[j] = p[8 * s2 + j] * (dp[8 * s2 + j] - delta);
 #pragma unroll
       for (int w = 0; w < 4; ++w) sf[s2][w] = pack_in<BF16>(d[2 * w], d[2 * w + 1]);
     }
