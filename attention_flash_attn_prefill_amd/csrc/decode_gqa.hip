@@ -41,7 +41,10 @@ namespace {
 constexpr int PS = kDecodePageSize;  // tokens per page
 constexpr int T = 2 * PS;            // tokens per tile
 
-template <int D, bool BF16>
+// P16: the partial outputs are stored in fp16 (fp16 inputs and output only:
+// a partial is a convex combination of V rows, so it stays within fp16's
+// range, and the output is rounded to fp16 anyway); otherwise fp32.
+template <int D, bool BF16, bool P16>
 __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int CPR = D / 8;           // 16-byte chunks per token row
@@ -343,28 +346,23 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
     // log-sum-exp in base 2.  Lane (li, hi) holds d = 32db + 8(r/4) + 4hi + r%4.
     if (!q_ok) return;
     const int64_t row = (int64_t)slot * a.rows_per_slot + li;
-    float* po = a.part_o + row * D;
-    if (bad_page) {
-      const float nan = __builtin_nanf("");
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g + 4 * hi) = (f32x4){nan, nan, nan, nan};
-      if (hi == 0) a.part_lse[row] = nan;
-      return;
-    }
+    // A rejected page makes the partial NaN (the key set is unknown).
     const float l_tot = pair_sum(l_run);  // > 0: the segment holds a live token
-    const float inv = 1.f / l_tot;
+    const float inv = bad_page ? __builtin_nanf("") : 1.f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float* v4 = reinterpret_cast<const float*>(&acc[db]) + 4 * g;
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g + 4 * hi) =
-            (f32x4){v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
+        const int d0 = 32 * db + 8 * g + 4 * hi;
+        if constexpr (P16)
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.part_o) + row * D + d0) =
+              (u32x2){pack_f16(v4[0] * inv, v4[1] * inv), pack_f16(v4[2] * inv, v4[3] * inv)};
+        else
+          *reinterpret_cast<f32x4*>(a.part_o + row * D + d0) =
+              (f32x4){v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
       }
-    if (hi == 0) a.part_lse[row] = m_run + __log2f(l_tot);
+    if (hi == 0) a.part_lse[row] = bad_page ? __builtin_nanf("") : m_run + __log2f(l_tot);
   };
 
   // ---- walk the range: a segment per line it touches.
@@ -392,7 +390,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
 // whose range holds one of its tiles, found from NT, W and the sequence's
 // first tile as the split kernel cut them).  A NaN partial (rejected page
 // id) makes the output NaN; a sequence without tokens gets O = 0.
-template <int D, bool BF16, bool OF32>
+template <int D, bool BF16, bool OF32, bool P16>
 __global__ __launch_bounds__(64) void decode_gqa_combine_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;  // output elements per lane
   const int bh = blockIdx.x;
@@ -431,8 +429,11 @@ __global__ __launch_bounds__(64) void decode_gqa_combine_kernel(DecodeArgs a) {
       const float w = __builtin_amdgcn_exp2f(a.part_lse[row] - mx);
       wsum += w;
 #pragma unroll
-      for (int e = 0; e < PER; ++e)
-        acc[e] = __builtin_fmaf(w, a.part_o[row * D + lane + 64 * e], acc[e]);
+      for (int e = 0; e < PER; ++e) {
+        const int64_t i = row * D + lane + 64 * e;
+        const float po = P16 ? (float)reinterpret_cast<const _Float16*>(a.part_o)[i] : a.part_o[i];
+        acc[e] = __builtin_fmaf(w, po, acc[e]);
+      }
     }
   }
   const float inv = poisoned ? __builtin_nanf("") : (wsum > 0.f ? 1.f / wsum : 0.f);
@@ -446,15 +447,21 @@ __global__ __launch_bounds__(64) void decode_gqa_combine_kernel(DecodeArgs a) {
 
 template <int D, bool BF16>
 hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16>), dim3(a.n_splits), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (out_f32)
-    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, true>), dim3(a.B * a.H), dim3(64), 0,
+  hipError_t e;
+  if (out_f32) {
+    hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16, false>), dim3(a.n_splits), dim3(64), 0,
                        s, a);
-  else
-    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, false>), dim3(a.B * a.H), dim3(64),
-                       0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, true, false>), dim3(a.B * a.H),
+                       dim3(64), 0, s, a);
+  } else {
+    constexpr bool P16 = !BF16;
+    hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16, P16>), dim3(a.n_splits), dim3(64), 0, s,
+                       a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, false, P16>), dim3(a.B * a.H),
+                       dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
