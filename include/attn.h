@@ -269,7 +269,9 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
  * a range that crosses sequences writes one partial per sequence and KV head
  * it touches, and the log-sum-exp combine merges them (flash decoding with
  * the KV split sized to fill the GPU, as above).  The workspace also holds
- * the range metadata, rewritten by every call.
+ * the range metadata, rewritten by every call.  With fp16 inputs and fp16
+ * output the partial outputs (normalised, so within fp16 range) are kept in
+ * fp16; otherwise in fp32.
  */
 int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* page_table, const int32_t* seq_lens, void* o,
