@@ -48,9 +48,8 @@ struct SplitPlan {
 // per split and query head: about 0.5% of the KV bytes at 512 tokens.  The
 // plan depends only on host-side sizes (never on seq_lens).
 //
-// Work items per split: group = 1 (decode.hip): B x ceil(H / 4) workgroups of
-// four waves; group > 1 (decode_gqa.hip): B x H_kv x ceil(group / 32)
-// one-wave workgroups.
+// Work items per split (group = 1, decode.hip): B x ceil(H / 4) workgroups
+// of four waves.  Grouped heads (decode_gqa.hip) use plan_gqa below instead.
 SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
   SplitPlan p{0, 0};
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || max_pages <= 0 ||

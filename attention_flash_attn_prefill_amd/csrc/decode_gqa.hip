@@ -7,7 +7,13 @@
 // February 2025 Release", FlashDecoding list; splits sized to fill the GPU:
 // "[FlyDSL] FP8 MQA logits improvements for gfx950", Changes / Host side).
 //
-// One wave per (sequence, KV head, split, 32-query chunk of the group):
+// Work: a line is one (sequence, KV head, 32-query chunk of the group) and
+// holds its sequence's 32-token tiles; the batch's tiles, line after line,
+// are cut on the device into W equal contiguous ranges, one wave each, so
+// every wave streams the same number of tiles whatever the length mix (W at
+// most the resident wave count, so all ranges start at once).  A range
+// writes one partial per line it touches; the combine kernel below merges a
+// line's partials.  Within a range, per line:
 //   * Tiles of 32 tokens (two 16-token pages).  K and V rows of a tile are
 //     gathered through the page table into registers with 16-byte
 //     non-temporal buffer loads (16 lanes per 256-byte row); tile t+1's loads
@@ -16,16 +22,16 @@
 //     which the MFMA operands are read.  The bytes in flight per CU, not the
 //     arithmetic, bound this kernel: staging through registers instead of
 //     LDS-only double buffering lets more waves (and bytes) be resident.
-//   * Each page gets its own buffer resource whose range ends at the split's
-//     last live token, so slots past it read as zero and a page past the end
-//     is never touched.
+//   * Each page gets its own buffer resource whose range ends at the
+//     segment's last live token, so slots past it read as zero and a page
+//     past the end is never touched.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (K rows are the M dimension, the
 //     group's queries the N dimension, zero-padded to 32), the online softmax
 //     per query column in fp32 (base 2, lazy rescale), P rounded to fp16 and
 //     O^T += V^T P^T on fp16 MFMA with V read by transposing LDS reads -- the
 //     operand layouts and swizzle of the prefill kernel.
 //   * Page ids are checked before any load through them: an id outside
-//     [0, num_pages) poisons the split's partial result with NaN.
+//     [0, num_pages) poisons the segment's partial result with NaN.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
       f32x16 sc = (f32x16){};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) sc = mfma_qk<BF16>(kf[s], qf[s], sc);
-      // Tokens past the split's end.
+      // Tokens past the segment's end.
       if (tb + T > t_end) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
