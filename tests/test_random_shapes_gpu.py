@@ -1,0 +1,104 @@
+"""A seeded sweep of random shapes through prefill (with and without the LSE
+output), grouped-query decode and extend, each against the fp64 oracle at the
+standard bar.  The draws mix batch, head counts and grouping, lengths on and
+off tile boundaries (including Sq > Skv under the bottom-right causal mask),
+head size, dtype, layout and scale, so that combinations the hand-picked
+cases do not name are still exercised.  Sizes stay small enough for the
+oracle to finish in seconds."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw_prefill(i):
+    r = np.random.default_rng(1000 + i)
+    H_kv = int(r.choice([1, 2, 4]))
+    H = H_kv * int(r.choice([1, 2, 3, 4]))
+    return dict(B=int(r.integers(1, 3)), H=H, H_kv=H_kv, Sq=int(r.integers(1, 600)),
+                Skv=int(r.integers(1, 700)), D=int(r.choice([64, 128])),
+                dtype=str(r.choice(["f16", "bf16"])), layout=str(r.choice(["BHSD", "BSHD"])),
+                causal=bool(r.integers(0, 2)), scale=float(r.uniform(0.02, 0.3)),
+                lse=bool(r.integers(0, 2)))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_prefill_random(gpu_lib, i):
+    c = _draw_prefill(i)
+    print(f"[case] prefill random {i}: {c}", flush=True)
+    q, k, v = workloads.prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                       c["layout"], seed=2000 + i, h_kv=c["H_kv"])
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    if c["lse"]:
+        o, lse = gpu_lib.prefill_with_lse(qg, kg, vg, causal=c["causal"], scale=c["scale"],
+                                          layout=c["layout"])
+    else:
+        o = gpu_lib.prefill(qg, kg, vg, causal=c["causal"], scale=c["scale"], layout=c["layout"])
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, causal=c["causal"], scale=c["scale"], layout=c["layout"])
+    assert_parity(o.double().cpu().numpy(), ref, f"prefill random {i}")
+    if c["lse"]:
+        want = oracle.lse_rows(q, k, causal=c["causal"], scale=c["scale"], layout=c["layout"])
+        got = lse.double().cpu().numpy()
+        fin = np.isfinite(want)
+        assert np.array_equal(fin, np.isfinite(got))
+        assert np.all(np.abs(got[fin] - want[fin]) <= 1e-3 + 1e-6 * np.abs(want[fin]))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_decode_random(gpu_lib, i):
+    r = np.random.default_rng(3000 + i)
+    H_kv = int(r.choice([1, 2, 4, 8]))
+    H = H_kv * int(r.choice([1, 2, 4, 8, 16]))
+    B = int(r.integers(1, 40))
+    lens = r.integers(0, 3000, B).tolist()
+    lens[int(r.integers(0, B))] = int(r.integers(1, 5000))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["f16", "bf16"]))
+    scale = float(r.uniform(0.02, 0.3))
+    pages = sum(-(-n // 16) for n in lens)
+    print(f"[case] decode random {i}: B{B} H{H}/{H_kv} D{D} {dtype} max_len {max(lens)}",
+          flush=True)
+    batch = workloads.paged_decode_inputs(B=B, H=H, D=D, dtype=dtype, page_size=16,
+                                          num_pages=pages + 32, seq_lens=lens, seed=4000 + i,
+                                          h_kv=H_kv)
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k_cache", "v_cache", "page_table",
+                                              "seq_lens")}
+    o = gpu_lib.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"],
+                             scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, scale=scale)
+    assert_parity(o.double().cpu().numpy(), ref, f"decode random {i}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_extend_random(gpu_lib, i):
+    r = np.random.default_rng(5000 + i)
+    H_kv = int(r.choice([1, 2, 4]))
+    H = H_kv * int(r.choice([1, 2, 4]))
+    B = int(r.integers(1, 6))
+    pl = r.integers(0, 900, B).tolist()
+    el = r.integers(0, 300, B).tolist()
+    el[int(r.integers(0, B))] = int(r.integers(1, 300))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["f16", "bf16"]))
+    scale = float(r.uniform(0.02, 0.3))
+    print(f"[case] extend random {i}: B{B} H{H}/{H_kv} D{D} {dtype} prefix {pl} new {el}",
+          flush=True)
+    batch = workloads.extend_inputs(B, H, D, pl, el, dtype, seed=6000 + i, h_kv=H_kv)
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k", "v", "k_cache", "v_cache",
+                                              "page_table", "prefix_lens", "qo_start")}
+    o = gpu_lib.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                       g["prefix_lens"], g["qo_start"], scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        batch.page_table, batch.prefix_lens, batch.qo_start, scale=scale)
+    assert_parity(o.double().cpu().numpy(), ref, f"extend random {i}")
