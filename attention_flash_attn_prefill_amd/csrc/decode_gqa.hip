@@ -391,17 +391,33 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// One wave per (sequence, query head): merge, by log-sum-exp, the partials
-// of the ranges that cover the head's line (slots w + line for the waves w
-// whose range holds one of its tiles, found from NT, W and the sequence's
-// first tile as the split kernel cut them).  A NaN partial (rejected page
-// id) makes the output NaN; a sequence without tokens gets O = 0.
+// Merge, by log-sum-exp, the partials of the ranges that cover a (sequence,
+// query head) row's line (slots w + line for the waves w whose range holds
+// one of its tiles, found from NT, W and the sequence's first tile as the
+// split kernel cut them).  A NaN partial (rejected page id) makes the output
+// NaN; a sequence without tokens gets O = 0.
+//
+// Eight rows per 64-lane workgroup, eight lanes per row, each lane D/8
+// consecutive outputs: a row's partial is read as 16-byte loads, the eight
+// lanes of a row covering it contiguously, and up to U partials per lane are
+// in flight at once (the merge is bound by load latency, not bytes).  Lanes
+// first take the row's maximum log-sum-exp over the partials (each lane a
+// stride-8 share, reduced over the row's lanes), then accumulate the
+// partials in slot order with the same operations as a one-lane-per-output
+// loop, so the result does not depend on this layout.
 template <int D, bool BF16, bool OF32, bool P16>
 __global__ __launch_bounds__(64) void decode_gqa_combine_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;  // output elements per lane
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh % a.H;
+  constexpr int E = D / 8;                      // outputs per lane
+  constexpr int EB = P16 ? 2 : 4;               // bytes per partial element
+  constexpr int NV = E * EB / 16;               // 16-byte loads per lane per partial
+  constexpr int U = P16 ? 16 : 8;               // partials loaded per batch
+  constexpr int EPV = 16 / EB;                  // elements per 16-byte load
+  static_assert(NV * 16 == E * EB, "a lane's share is whole 16-byte chunks");
   const int lane = threadIdx.x;
+  const int k = lane & 7;                       // the lane's chunk of its row
+  const int bh = blockIdx.x * 8 + (lane >> 3);  // the lane's (sequence, head) row
+  if (bh >= a.B * a.H) return;                  // whole 8-lane groups leave together
+  const int b = bh / a.H, h = bh % a.H;
   const int hk = h / a.group, qn = h % a.group;
   const int lines = a.H_kv * a.qchunks;
   const int j = hk * a.qchunks + qn / 32;  // line of sequence b
@@ -409,45 +425,89 @@ __global__ __launch_bounds__(64) void decode_gqa_combine_kernel(DecodeArgs a) {
   const int pb = a.meta[2 + b];
   const int ntb = (a.meta[3 + b] - pb) / lines;
 
-  float wsum = 0.f;
-  bool poisoned = false;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  int np = 0;             // partials of the line
+  int64_t row0 = 0;       // partial row of the first of them
+  const int64_t stride = a.rows_per_slot;  // row of the next slot
   if (ntb > 0) {
-    const int A = pb + j * ntb, E = A + ntb;  // the line's tiles [A, E)
+    const int A = pb + j * ntb, Ee = A + ntb;  // the line's tiles [A, Ee)
     const int w_lo = (int)(((int64_t)(A + 1) * W - 1) / NT);
-    const int w_hi = (int)(((int64_t)E * W - 1) / NT);
-    const int np = w_hi - w_lo + 1;
-    const int64_t row0 = (int64_t)(w_lo + b * lines + j) * a.rows_per_slot + qn % 32;
-    const int64_t stride = a.rows_per_slot;  // row of the next slot
-    float mx = kNegInf;
-    for (int s = lane; s < np; s += 64) {
-      const float l = a.part_lse[row0 + s * stride];
-      mx = fmaxf(mx, l);
-      poisoned |= __builtin_isnan(l);
+    const int w_hi = (int)(((int64_t)Ee * W - 1) / NT);
+    np = w_hi - w_lo + 1;
+    row0 = (int64_t)(w_lo + b * lines + j) * a.rows_per_slot + qn % 32;
+  }
+
+  // Row maximum of the partials' log-sum-exps, and whether any is NaN.
+  float mx = kNegInf;
+  int poisoned = 0;
+  for (int s = k; s < np; s += 8) {
+    const float l = a.part_lse[row0 + s * stride];
+    mx = fmaxf(mx, l);
+    poisoned |= __builtin_isnan(l) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    poisoned |= __shfl_xor(poisoned, off);
+  }
+
+  float wsum = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const char* po_base = reinterpret_cast<const char*>(a.part_o) + (int64_t)k * E * EB;
+  for (int s0 = 0; s0 < np; s0 += U) {
+    // Loads of the batch (indices past the end repeat the last partial and
+    // are not accumulated).
+    float l[U];
+    u32x4 p[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = row0 + min(s0 + u, np - 1) * stride;
+      l[u] = a.part_lse[row];
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        p[u][v] = *reinterpret_cast<const u32x4*>(po_base + row * D * EB + 16 * v);
     }
-    poisoned = __any(poisoned);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    for (int s = 0; s < np; ++s) {
-      const int64_t row = row0 + s * stride;
-      const float w = __builtin_amdgcn_exp2f(a.part_lse[row] - mx);
-      wsum += w;
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < np) {
+        const float w = __builtin_amdgcn_exp2f(l[u] - mx);
+        wsum += w;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int64_t i = row * D + lane + 64 * e;
-        const float po = P16 ? (float)reinterpret_cast<const _Float16*>(a.part_o)[i] : a.part_o[i];
-        acc[e] = __builtin_fmaf(w, po, acc[e]);
+        for (int v = 0; v < NV; ++v) {
+          if constexpr (P16) {
+            const f16x8 hv = __builtin_bit_cast(f16x8, p[u][v]);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i)
+              acc[v * EPV + i] = __builtin_fmaf(w, (float)hv[i], acc[v * EPV + i]);
+          } else {
+            const f32x4 fv = __builtin_bit_cast(f32x4, p[u][v]);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i)
+              acc[v * EPV + i] = __builtin_fmaf(w, fv[i], acc[v * EPV + i]);
+          }
+        }
       }
     }
   }
   const float inv = poisoned ? __builtin_nanf("") : (wsum > 0.f ? 1.f / wsum : 0.f);
+  const int64_t o0 = (int64_t)bh * D + k * E;
+  if constexpr (OF32) {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t i = (int64_t)bh * D + lane + 64 * e;
-    if constexpr (OF32) static_cast<float*>(a.o)[i] = acc[e] * inv;
-    else static_cast<uint16_t*>(a.o)[i] = to_out<BF16>(acc[e] * inv);
+    for (int v = 0; v < E / 4; ++v)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + o0 + 4 * v) =
+          (f32x4){acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
+                  acc[4 * v + 3] * inv};
+  } else {
+#pragma unroll
+    for (int v = 0; v < E / 8; ++v) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)to_out<BF16>(acc[8 * v + 2 * i] * inv) |
+               ((uint32_t)to_out<BF16>(acc[8 * v + 2 * i + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + o0 + 8 * v) = w;
+    }
   }
 }
 
@@ -458,15 +518,15 @@ hipError_t launch_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16, false>), dim3(a.n_splits), dim3(64), 0,
                        s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, true, false>), dim3(a.B * a.H),
-                       dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, true, false>),
+                       dim3((a.B * a.H + 7) / 8), dim3(64), 0, s, a);
   } else {
     constexpr bool P16 = !BF16;
     hipLaunchKernelGGL((decode_gqa_split_kernel<D, BF16, P16>), dim3(a.n_splits), dim3(64), 0, s,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, false, P16>), dim3(a.B * a.H),
-                       dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D, BF16, false, P16>),
+                       dim3((a.B * a.H + 7) / 8), dim3(64), 0, s, a);
   }
   return hipGetLastError();
 }
