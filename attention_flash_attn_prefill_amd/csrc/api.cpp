@@ -77,9 +77,14 @@ SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
 // ceil(group / 32), each holding its sequence's 32-token tiles; the tiles of
 // all lines are cut into W equal ranges on the device, W = min(ranges,
 // ceil(NT / min_tiles)) for the batch's actual tile count NT.  A range writes
-// one partial row per query of the chunk for every line it touches, so it
-// covers at least min(group, 32) / 2 tiles (partials <= ~6% of its K/V
-// bytes).  Slots = ranges + lines bound the (range, line) pairs.
+// one partial row per query of the chunk for every line it touches, which the
+// combine reads back, so it covers at least min(group, 32) / 2 tiles, at most
+// 8 (more ranges keep small batches' loads in flight).  Groups of 16 or more
+// query heads take at most half the ranges (4 resident waves per CU instead
+// of 8): their partials are 16-32 rows per range, and halving the ranges ran
+// 7-9% faster at group sizes 16 and 32 on batches of 64-256 sequences of up
+// to 8k tokens, no faster at 4 and 8.  Slots = ranges + lines bound the
+// (range, line) pairs.
 struct GqaPlan {
   int ranges, min_tiles, rows_per_slot;
   int64_t lines, slots;
@@ -91,7 +96,7 @@ GqaPlan plan_gqa(int B, int H, int H_kv, int max_pages, int page_size) {
     return p;
   const int group = H / H_kv;
   p.rows_per_slot = group < 32 ? group : 32;
-  p.min_tiles = p.rows_per_slot > 1 ? p.rows_per_slot / 2 : 1;
+  p.min_tiles = p.rows_per_slot / 2 < 8 ? (p.rows_per_slot > 1 ? p.rows_per_slot / 2 : 1) : 8;
   p.lines = (int64_t)B * H_kv * ((group + 31) / 32);
   const int64_t max_tiles = ((int64_t)max_pages * page_size + 31) / 32;
   const int64_t nt_max = p.lines * max_tiles;
@@ -99,7 +104,8 @@ GqaPlan plan_gqa(int B, int H, int H_kv, int max_pages, int page_size) {
       (int64_t)max_pages * page_size >= ((int64_t)1 << 31))
     return GqaPlan{};
   const int64_t by_size = (nt_max + p.min_tiles - 1) / p.min_tiles;
-  p.ranges = (int)(by_size < kDecodeRanges ? by_size : kDecodeRanges);
+  const int64_t cap = p.rows_per_slot >= 16 ? kDecodeRanges / 2 : kDecodeRanges;
+  p.ranges = (int)(by_size < cap ? by_size : cap);
   p.slots = p.ranges + p.lines;
   return p;
 }

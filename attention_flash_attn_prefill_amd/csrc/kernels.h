@@ -81,8 +81,9 @@ hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, i
 constexpr int kDecodeHeadsPerWG = 4;
 constexpr int kDecodePageSize = 16;
 // Grouped-query decode: the batch's KV tiles are cut into at most this many
-// equal ranges, one wave each -- the waves one launch keeps resident on 256
-// CUs at eight per CU, so all of them start at once.
+// equal ranges (half as many for groups of 16 or more query heads), one wave
+// each -- the waves one launch keeps resident on 256 CUs at eight per CU, so
+// all of them start at once.
 constexpr int kDecodeRanges = 2048;
 
 struct DecodeArgs {

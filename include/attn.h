@@ -287,7 +287,8 @@ size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D,
  * (see attn_paged_decode_num_splits).  H_kv < H: returns the largest number
  * of work ranges W a call uses (0 on invalid sizes) and stores in
  * tokens_per_split the fewest tokens a range covers unless the batch holds
- * fewer: 16 per query head of the group, at most 512, at least 32. */
+ * fewer: 16 per query head of the group, at most 256, at least 32.  W is
+ * at most 2048, or 1024 for groups of 16 or more query heads. */
 int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
                                      int page_size, int* tokens_per_split);
 

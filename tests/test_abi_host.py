@@ -224,13 +224,17 @@ def test_gqa_split_plan_and_workspace():
     assert attn.attn_paged_decode_gqa_workspace_size(64, 32, 32, 128, 512, 16) == \
         attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
     # H_kv < H: (work ranges, tokens per range at least).  The batch's tiles
-    # are cut into at most 2048 equal ranges (one resident wave each), each
-    # covering at least min(group, 32) / 2 tiles of 32 tokens, so a range's
-    # partial rows (one per query of the group) stay a few percent of its K/V
+    # are cut into at most 2048 equal ranges (one resident wave each; 1024
+    # for groups of 16 or more query heads, whose partials are larger), each
+    # covering at least min(min(group, 32) / 2, 8) tiles of 32 tokens, so a
+    # range's partial rows (one per query of the group) stay a small share of
+    # its K/V
     assert attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16) == (2048, 64)
-    assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (2048, 512)
+    assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (1024, 256)
+    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 2, 512, 16) == (1024, 256)
+    assert attn.attn_paged_decode_gqa_num_splits(64, 64, 8, 512, 16) == (2048, 128)
     assert attn.attn_paged_decode_gqa_num_splits(1, 8, 1, 512, 16) == (64, 128)
-    assert attn.attn_paged_decode_gqa_num_splits(2, 64, 1, 100, 16) == (13, 512)
+    assert attn.attn_paged_decode_gqa_num_splits(2, 64, 1, 100, 16) == (25, 256)
     assert attn.attn_paged_decode_gqa_num_splits(4, 6, 4, 8, 16) == (0, 0)
     # partial rows for every (range, line) pair a call can touch: at most
     # ranges + lines of them, min(group, 32) rows of D + 1 floats each
