@@ -235,10 +235,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
                                              (int)(rows * row_bytes), kBufferConfig);
   };
 
-  // Extend prefix tiles: load i of a wave covers 64 / CPR rows of one page
-  // (rows are 16-aligned within the tile, pages hold 16 tokens).  Its buffer
-  // spans the page's slots below P, so rows past the prefix read as zero.
+  // Extend prefix tiles: the loads of a wave cover its WAVE_ROWS rows of the
+  // tile, which lie in one page (page wpage of the tile; pages hold 16
+  // tokens), so one buffer per tile and cache serves them all.  It spans the
+  // page's slots below P, so rows past the prefix read as zero.
   constexpr int ROWS_PER_LOAD = 64 / CPR;
+  constexpr int WAVE_ROWS = LOADS * ROWS_PER_LOAD;
+  static_assert(!EXT || kDecodePageSize % WAVE_ROWS == 0, "a wave's rows of a tile in one page");
+  const int wpage = (wave * WAVE_ROWS) / kDecodePageSize;  // wave-uniform
   const int64_t page_elems = (int64_t)kDecodePageSize * a.H_kv * D;
   const uint32_t slot_bytes = (uint32_t)a.H_kv * D * 2u;
   const int32_t* ptab = EXT ? a.page_table + (int64_t)b * a.max_pages : nullptr;
@@ -252,44 +256,39 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     }
   }
   bool bad_page = false;  // workgroup-uniform: a prefix page id outside the pool
-  // Page ids of the next prefix tile to load (-1: no live token there),
-  // fetched a tile ahead by a vector load -- lane j & 3 reads page j of the
-  // tile -- so the read is waited for with the tile loads (vmcnt) at the next
-  // barrier; a scalar load would share its counter with the LDS operand reads
-  // and stall the compute in between.
+  // Page ids of the next prefix tile to load (0 where the tile holds no live
+  // token: such a page is never read), fetched a tile ahead by a vector load
+  // -- lane j & 3 reads page j of the tile -- so the read is waited for with
+  // the tile loads (vmcnt) at the next barrier; a scalar load would share its
+  // counter with the LDS operand reads and stall the compute in between.
   constexpr int PPT = BN / kDecodePageSize;  // pages per tile
-  static_assert(PPT == 4, "page ids of a tile are kept in one 4-vector");
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  int pgv_next = -1;
+  static_assert(PPT == 4, "page ids of a tile are held by lanes j & 3");
+  int pgv_next = 0;
   auto fetch_pages = [&](int t) {
     const int tok = t * BN + (lane & 3) * kDecodePageSize;
-    pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : -1;
+    pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : 0;
   };
-  auto next_pages = [&]() {
-    return (i32x4){__builtin_amdgcn_readlane(pgv_next, 0), __builtin_amdgcn_readlane(pgv_next, 1),
-                   __builtin_amdgcn_readlane(pgv_next, 2), __builtin_amdgcn_readlane(pgv_next, 3)};
+  // Every wave checks every page of the tile (as unsigned, so negative ids
+  // are rejected too), so all waves agree.
+  auto pages_ok = [&]() {
+    return __builtin_amdgcn_ballot_w64((uint32_t)pgv_next >= (uint32_t)a.num_pages) == 0;
   };
-  // Every wave checks every live page of the tile, so all waves agree.
-  auto pages_ok = [&](i32x4 pg) {
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) ok &= pg[j] < a.num_pages;  // -1 (no page) passes
-    return ok;
-  };
-  i32x4 pg_cur = {-1, -1, -1, -1};  // page ids of the tile being loaded
-  auto page_rsrc = [&](const uint16_t* cache, int t, int i) {
-    const int row0 = (wave * LOADS + i) * ROWS_PER_LOAD;  // first row of load i
-    const int j = row0 / kDecodePageSize;
-    const int live = min(kDecodePageSize, P - (t * BN + j * kDecodePageSize));
-    int pg = pg_cur[0];
-#pragma unroll
-    for (int jj = 1; jj < PPT; ++jj) pg = j == jj ? pg_cur[jj] : pg;
-    const uint16_t* base = live > 0 ? cache + (int64_t)pg * page_elems : cache;
-    // The range is wave-uniform; keeping it in an SGPR keeps the compiler
-    // from wrapping every load in a waterfall loop over the lanes (it would
-    // otherwise clamp it with a vector instruction).
+  // Buffers of this wave's page of the tile being loaded, in the K and the V
+  // cache.  The range is wave-uniform; keeping it in an SGPR keeps the
+  // compiler from wrapping every load in a waterfall loop over the lanes (it
+  // would otherwise clamp it with a vector instruction).
+  __amdgpu_buffer_rsrc_t pk_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.k_cache, (short)0, 0, kBufferConfig);
+  __amdgpu_buffer_rsrc_t pv_rsrc = pk_rsrc;
+  auto set_page_rsrc = [&](int t) {
+    const int live = min(kDecodePageSize, P - (t * BN + wpage * kDecodePageSize));
+    const int64_t off = live > 0 ? (int64_t)__builtin_amdgcn_readlane(pgv_next, wpage) * page_elems
+                                 : 0;
     const int nbytes = __builtin_amdgcn_readfirstlane(max(live, 0) * (int)slot_bytes);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferConfig);
+    pk_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_cache + off), (short)0, nbytes,
+                                                kBufferConfig);
+    pv_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_cache + off), (short)0, nbytes,
+                                                kBufferConfig);
   };
 
   // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     if (is_pre(t)) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(a.k_cache, t, i),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pk_rsrc,
                                                  (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
                                                  16, pg_off[i], 0, 0, 0);
       return;
@@ -315,7 +314,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     const auto rv = tile_rsrc(vp, pre ? 0 : tile_key0(t) - P);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const auto r = pre ? page_rsrc(a.v_cache, t, i) : rv;
+      const auto r = pre ? pv_rsrc : rv;
       const int off = pre ? pg_off[i] : g_off[i];
       if constexpr (BF16 || FP8)
         vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -530,11 +529,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
 
   // A tile is loaded only when its pages check out (dense tiles always do);
-  // its page ids move to pg_cur and the following tile's are fetched.
+  // its page buffers are set up and the following tile's ids are fetched.
   auto load_ok = [&](int t) {
     if constexpr (EXT) {
-      pg_cur = next_pages();
-      if (is_pre(t) && !pages_ok(pg_cur)) bad_page = true;
+      if (is_pre(t)) {
+        if (!pages_ok()) bad_page = true;
+        else set_page_rsrc(t);
+      }
       fetch_pages(t + 1);
     }
     return !bad_page;

@@ -115,6 +115,34 @@ def test_extend_bad_page_id_gives_nan(gpu_lib):
     assert_parity(o[good].double().numpy(), ref[good], "extend sequences with valid pages")
 
 
+def test_extend_negative_page_id_gives_nan(gpu_lib):
+    # A negative page id is outside [0, num_pages) too.  The pool sits one page
+    # into a padded allocation, so an id of -1 stays inside it even if it were
+    # dereferenced; the most negative id runs only once -1 is rejected.
+    batch = workloads.extend_inputs(3, 4, 128, [40, 100, 20], [30, 20, 10], "f16", seed=95,
+                                    num_pages=64)
+    P = batch.k_cache.shape[0]
+    pad = (P + 2,) + tuple(batch.k_cache.shape[1:])
+    k_pad = torch.zeros(pad, dtype=batch.k_cache.dtype, device="cuda")
+    v_pad = torch.zeros(pad, dtype=batch.v_cache.dtype, device="cuda")
+    k_pad[1:P + 1].copy_(batch.k_cache)
+    v_pad[1:P + 1].copy_(batch.v_cache)
+    g = _gpu(batch)
+    s = batch.qo_start.tolist()
+    good = list(range(s[0], s[1])) + list(range(s[2], s[3]))
+    ref = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        batch.page_table, batch.prefix_lens, batch.qo_start, seqs=[0, 2])
+    for bad in (-1, -(1 << 31)):
+        table = batch.page_table.clone()
+        table[1, 2] = bad      # a live prefix page of sequence 1
+        print(f"[case] extend page id {bad}", flush=True)
+        o = gpu_lib.extend(g["q"], g["k"], g["v"], k_pad[1:P + 1], v_pad[1:P + 1],
+                           table.cuda(), g["prefix_lens"], g["qo_start"]).float().cpu()
+        torch.cuda.synchronize()
+        assert torch.isnan(o[s[1]:s[2]]).all(), f"page id {bad} was not rejected"
+        assert_parity(o[good].double().numpy(), ref[good], "extend sequences with valid pages")
+
+
 def test_extend_rows_past_max_extend_len_untouched(gpu_lib):
     batch = workloads.extend_inputs(2, 4, 64, [10, 20], [40, 100], "f16", seed=94)
     g = _gpu(batch)
