@@ -231,55 +231,104 @@ __global__ __launch_bounds__(64 * kDecodeHeadsPerWG) void decode_split_kernel(De
   }
 }
 
-// One wave per (sequence, head): merge the live splits by log-sum-exp.  A
-// NaN partial (rejected page id) makes the output NaN.  OF32: O in fp32.
+// Merge a (sequence, head) row's live splits by log-sum-exp.  A NaN partial
+// (rejected page id) makes the output NaN.  OF32: O in fp32.
+//
+// Eight rows per 64-lane workgroup, eight lanes per row, each lane D/8
+// consecutive outputs: a partial row is read as 16-byte loads, the eight
+// lanes of a row covering it contiguously, and up to U partials per lane are
+// in flight at once (the merge is bound by load latency, not bytes).  Lanes
+// first take the row's maximum log-sum-exp over its splits (each lane a
+// stride-8 share, reduced over the row's lanes), then accumulate the splits
+// in order with the same operations as a one-lane-per-output loop, so the
+// result does not depend on this layout.
 template <int D, bool BF16, bool OF32>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;  // output elements per lane
-  const int bh = blockIdx.x;
-  const int b = bh / a.H;
+  constexpr int E = D / 8;   // outputs per lane
+  constexpr int NV = E / 4;  // 16-byte loads per lane per partial (fp32)
+  constexpr int U = 8;       // partials loaded per batch
   const int lane = threadIdx.x;
+  const int k = lane & 7;                       // the lane's chunk of its row
+  const int bh = blockIdx.x * 8 + (lane >> 3);  // the lane's (sequence, head) row
+  if (bh >= a.B * a.H) return;                  // whole 8-lane groups leave together
+  const int b = bh / a.H;
   const int n = max(0, min(a.seq_lens[b], a.max_pages * PS));
   const int ns = min(a.n_splits, (n + a.tokens_per_split - 1) / a.tokens_per_split);
   const float* lse = a.part_lse + (int64_t)bh * a.n_splits;
-  const float* po = a.part_o + (int64_t)bh * a.n_splits * D;
+  const float* po = a.part_o + (int64_t)bh * a.n_splits * D + k * E;
 
   float mx = kNegInf;
-  bool poisoned = false;
-  for (int s = lane; s < ns; s += 64) {
-    mx = fmaxf(mx, lse[s]);
-    poisoned |= __builtin_isnan(lse[s]);
+  int poisoned = 0;
+  for (int s = k; s < ns; s += 8) {
+    const float l = lse[s];
+    mx = fmaxf(mx, l);
+    poisoned |= __builtin_isnan(l) ? 1 : 0;
   }
-  poisoned = __any(poisoned);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  for (int off = 1; off < 8; off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    poisoned |= __shfl_xor(poisoned, off);
+  }
 
   float wsum = 0.f;
-  float acc[PER];
+  float acc[E];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(lse[s] - mx);
-    wsum += w;
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    // Loads of the batch (indices past the last split repeat it and are not
+    // accumulated).
+    float l[U];
+    float4 p[U][NV];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(w, po[s * D + lane + 64 * e], acc[e]);
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + u, ns - 1);
+      l[u] = lse[sp];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) p[u][v] = *reinterpret_cast<const float4*>(po + sp * D + 4 * v);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < ns) {
+        const float w = __builtin_amdgcn_exp2f(l[u] - mx);
+        wsum += w;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          acc[4 * v] = __builtin_fmaf(w, p[u][v].x, acc[4 * v]);
+          acc[4 * v + 1] = __builtin_fmaf(w, p[u][v].y, acc[4 * v + 1]);
+          acc[4 * v + 2] = __builtin_fmaf(w, p[u][v].z, acc[4 * v + 2]);
+          acc[4 * v + 3] = __builtin_fmaf(w, p[u][v].w, acc[4 * v + 3]);
+        }
+      }
+    }
   }
   const float inv = poisoned ? __builtin_nanf("") : (wsum > 0.f ? 1.f / wsum : 0.f);
+  const int64_t o0 = (int64_t)bh * D + k * E;
+  if constexpr (OF32) {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t i = (int64_t)bh * D + lane + 64 * e;
-    if constexpr (OF32) static_cast<float*>(a.o)[i] = acc[e] * inv;
-    else static_cast<uint16_t*>(a.o)[i] = to_out<BF16>(acc[e] * inv);
+    for (int v = 0; v < NV; ++v)
+      *reinterpret_cast<float4*>(static_cast<float*>(a.o) + o0 + 4 * v) =
+          make_float4(acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
+                      acc[4 * v + 3] * inv);
+  } else {
+#pragma unroll
+    for (int v = 0; v < E / 8; ++v) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)to_out<BF16>(acc[8 * v + 2 * i] * inv) |
+               ((uint32_t)to_out<BF16>(acc[8 * v + 2 * i + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + o0 + 8 * v) = w;
+    }
   }
 }
 
 template <int D, bool BF16>
 hipError_t launch_combine_t(bool out_f32, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((a.B * a.H + 7) / 8);
   if (out_f32)
-    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, true>), dim3(a.B * a.H), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, true>), grid, dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, false>), dim3(a.B * a.H), dim3(64), 0, s,
-                       a);
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, false>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
