@@ -111,7 +111,8 @@ hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs&
                                hipStream_t s);
 hipError_t launch_paged_decode_gqa(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                    hipStream_t s);
-// The log-sum-exp merge of the per-split partials (one wave per (b, h)).
+// The log-sum-exp merge of the per-split partials (eight (b, h) rows per
+// 64-lane workgroup).
 hipError_t launch_decode_combine(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                  hipStream_t s);
 
