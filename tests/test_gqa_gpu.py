@@ -195,6 +195,24 @@ def test_decode_gqa_ranges_long_sequences(gpu_lib, lens, H, H_kv):
     assert torch.count_nonzero(o[[b for b, n in enumerate(lens) if n == 0]]) == 0
 
 
+@pytest.mark.parametrize("lens,H,H_kv,dtype", [([9000, 3, 40000], 3, 1, "f16"),
+                                               ([9000, 3, 40000], 6, 2, "bf16"),
+                                               ([5000, 100, 8192, 1, 17], 3, 3, "f16")])
+def test_decode_combine_row_groups(gpu_lib, lens, H, H_kv, dtype):
+    """The combines merge eight (sequence, head) rows per workgroup: B*H not a
+    multiple of eight leaves the last workgroup part empty, and long
+    sequences give a row more partials than one batch of loads holds (fp16
+    partials 16 at a time, fp32 ones 8; the multi-head case has up to 16
+    splits)."""
+    assert (len(lens) * H) % 8 != 0
+    batch = _lens_batch(lens, H, H_kv, seed=81 + H, dtype=dtype)
+    print(f"[case] decode combine rows B{len(lens)} H{H}/{H_kv} {dtype} {lens}", flush=True)
+    o = _decode(gpu_lib, batch)
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens)
+    assert_parity(_f64(o), ref, f"decode combine rows B{len(lens)} H{H}/{H_kv} {dtype}")
+
+
 def test_decode_gqa_ranges_workspace_reused(gpu_lib):
     """The range metadata is rewritten by every call: a workspace used for a
     batch of long sequences, then for the same sizes with mostly empty ones,
