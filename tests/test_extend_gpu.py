@@ -164,7 +164,7 @@ def test_extend_full_config9_sampled(gpu_lib):
     seqs = [0, 3, 7]
     ref = _ref(batch, scale=batch.meta["scale"], seqs=seqs)
     rows = [r for b in seqs for r in range(int(batch.qo_start[b]), int(batch.qo_start[b + 1]))]
-    assert_parity(o[rows].double().numpy(), ref[rows], f"config 9 ({len(rows)} rows of {seqs})")
+    assert_parity(o[rows].double().numpy(), ref[rows], f"{batch.meta['name']} ({len(rows)} rows of sequences {seqs})")
 
 
 def _permuted(batch, perm):

@@ -51,7 +51,7 @@ def test_prefill_gqa_equals_repeated_kv_bitwise(gpu_lib):
 
 def test_prefill_gqa_full_config6_sampled(gpu_lib):
     q, k, v, m = workloads.prefill_config(6)
-    print(f"[case] prefill config 6 {m['name']}", flush=True)
+    print(f"[case] prefill {m['name']}", flush=True)
     o = gpu_lib.prefill(q.cuda(), k.cuda(), v.cuda(), causal=m["causal"], scale=m["scale"],
                         layout=m["layout"]).cpu()
     torch.cuda.synchronize()
@@ -62,7 +62,7 @@ def test_prefill_gqa_full_config6_sampled(gpu_lib):
              for _ in range(64)]
     ref = oracle.sdpa_rows(q, k, v, rows, causal=m["causal"], scale=m["scale"], layout=m["layout"])
     got = np.stack([o[b, i, h].double().numpy() for b, h, i in rows])
-    assert_parity(got, ref, f"config 6 ({len(rows)} sampled rows)")
+    assert_parity(got, ref, f"{m['name']} ({len(rows)} sampled rows)")
 
 
 # ------------------------------------------------------------------- decode
