@@ -155,11 +155,11 @@ def test_backward_writes_every_row(gpu_lib):
 
 @pytest.mark.parametrize("cfg", [11, 12])
 def test_backward_full_config_sampled(gpu_lib, cfg):
-    """The 8k causal BSHD backward at full size (config 11; config 12 with
+    """The 8k causal BSHD backward at full size (32 query heads; and with
     four query heads per KV head), in the bench's launch configuration: dq at
     sampled query rows, dk and dv at sampled keys."""
     q, k, v, do, m = workloads.backward_config(cfg)
-    print(f"[case] backward config {cfg} {m['name']}", flush=True)
+    print(f"[case] backward {m['name']}", flush=True)
     _, _, (dq, dk, dv) = _run(gpu_lib, q, k, v, do, m["causal"], m["layout"], scale=m["scale"])
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     rng = np.random.default_rng(cfg)

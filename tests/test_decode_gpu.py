@@ -102,7 +102,7 @@ def test_decode_full_config4(gpu_lib):
     batch = workloads.decode_config(4)
     o = _run(gpu_lib, batch, scale=batch.meta["scale"])
     ref = _ref(batch, scale=batch.meta["scale"])
-    assert_parity(o.double().numpy(), ref, "config 4 (all sequences and heads)")
+    assert_parity(o.double().numpy(), ref, f"{batch.meta['name']} (all sequences and heads)")
 
 
 @pytest.mark.parametrize("dtype,amp", [("f16", 6.0), ("bf16", 8.0)])

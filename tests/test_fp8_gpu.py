@@ -71,4 +71,4 @@ def test_prefill_fp8_full_config10_sampled(gpu_lib):
     q, k, v = _deq(q8, k8, v8, m["descales"])
     ref = oracle.sdpa_rows(q, k, v, rows, causal=m["causal"], scale=m["scale"], layout=m["layout"])
     got = np.stack([o[b, h, i].double().numpy() for b, h, i in rows])
-    assert_parity(got, ref, f"config 10 ({len(rows)} sampled rows)")
+    assert_parity(got, ref, f"{m['name']} ({len(rows)} sampled rows)")

@@ -61,7 +61,7 @@ def test_prefill_config1_full(gpu_lib):
     q, k, v, m = workloads.prefill_config(1)
     o = _run(gpu_lib, q, k, v, m["causal"], m["scale"], m["layout"])
     ref = oracle.sdpa(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"])
-    assert_parity(_f64(o), ref, "config 1 (full tensor)")
+    assert_parity(_f64(o), ref, f"{m['name']} (full tensor)")
 
 
 @pytest.mark.parametrize("Sq,Skv,causal", [(1, 1, False), (1, 1000, True), (1000, 1, True),
