@@ -131,9 +131,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     // prefix length (descending, ties by index), so the longest work items of
     // a ragged batch start first instead of last.  Thread t ranks sequence t
     // and the one whose rank is this workgroup's sequence slot publishes it.
-    // Only for small batches (B <= 64: at most 64 uniform loads per thread).
+    // Only for small batches (B <= 64: at most 64 uniform loads per thread),
+    // and only when there can be a prefix: with max_pages = 0 prefix_lens may
+    // be null and every prefix is empty, so index order is already the rank.
     const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv);
-    if (nb > 1 && nb <= 64) {
+    if (a.max_pages > 0 && nb > 1 && nb <= 64) {
       if (tid < nb) {
         const int pt = a.prefix_lens[tid];
         int rank = 0;

@@ -24,3 +24,13 @@ def gpu_lib():
     import attention_flash_attn_prefill_amd as attn
     attn.load_library()  # raises if the shared library was not built
     return attn
+
+
+@pytest.fixture
+def progress(capsys):
+    """A function that prints a progress line past pytest's output capture,
+    for tests whose CPU-side oracle work runs for minutes."""
+    def say(msg):
+        with capsys.disabled():
+            print(msg, flush=True)
+    return say

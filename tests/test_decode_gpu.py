@@ -24,7 +24,7 @@ def _to_gpu(batch):
                                                  "seq_lens")}
 
 
-def _run(attn, batch, scale=None, page_table=None):
+def _run(attn, batch, scale=None, page_table=None, out=None):
     print(f"[case] decode B{batch.q.shape[0]} H{batch.q.shape[1]} D{batch.q.shape[2]} "
           f"{batch.q.dtype} pages{batch.num_pages} lens={batch.seq_lens.tolist()[:8]}...",
           flush=True)
@@ -32,7 +32,7 @@ def _run(attn, batch, scale=None, page_table=None):
     if page_table is not None:
         g["page_table"] = page_table.cuda()
     o = attn.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"],
-                          scale=scale)
+                          scale=scale, out=out)
     torch.cuda.synchronize()
     return o.cpu()
 
@@ -99,8 +99,11 @@ def test_decode_scale(gpu_lib):
 
 
 def test_decode_full_config4(gpu_lib):
+    """Every (sequence, head) of the paged-decode workload, written into a
+    NaN-prefilled output."""
     batch = workloads.decode_config(4)
-    o = _run(gpu_lib, batch, scale=batch.meta["scale"])
+    out = torch.full(tuple(batch.q.shape), float("nan"), dtype=batch.q.dtype, device="cuda")
+    o = _run(gpu_lib, batch, scale=batch.meta["scale"], out=out)
     ref = _ref(batch, scale=batch.meta["scale"])
     assert_parity(o.double().numpy(), ref, f"{batch.meta['name']} (all sequences and heads)")
 

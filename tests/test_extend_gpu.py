@@ -6,7 +6,8 @@ import torch
 
 import oracle
 import workloads
-from parity import assert_parity
+import whole_tensor as whole
+from parity import MAX_ABS_TOL, REL_FRO_TOL, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -158,13 +159,19 @@ def test_extend_rows_past_max_extend_len_untouched(gpu_lib):
     assert torch.all(o[104:140] == 7.0)
 
 
-def test_extend_full_config9_sampled(gpu_lib):
+@pytest.mark.timeout(600)
+def test_extend_full_config9_whole(gpu_lib, progress):
+    """The ragged extend batch at full size: NaN-prefilled output, every
+    sequence's rows against the oracle."""
     batch = workloads.extend_config(9)
-    o = _run(gpu_lib, batch, scale=batch.meta["scale"])
-    seqs = [0, 3, 7]
-    ref = _ref(batch, scale=batch.meta["scale"], seqs=seqs)
-    rows = [r for b in seqs for r in range(int(batch.qo_start[b]), int(batch.qo_start[b + 1]))]
-    assert_parity(o[rows].double().numpy(), ref[rows], f"{batch.meta['name']} ({len(rows)} rows of sequences {seqs})")
+    scale = batch.meta["scale"]
+    out = whole.nan_like(batch.q)
+    o = _run(gpu_lib, batch, scale=scale, out=out)
+    st = whole.compare(whole.extend_units(batch, ["o"], scale=scale), {"o": o},
+                       progress=progress)["o"]
+    print(f"[parity] {batch.meta['name']} (whole tensor): {st}", flush=True)
+    assert st.nonfinite == 0, f"{st.nonfinite} elements not written (or not finite)"
+    assert st.max_abs <= MAX_ABS_TOL and st.rel_fro <= REL_FRO_TOL, f"{batch.meta['name']}: {st}"
 
 
 def _permuted(batch, perm):
@@ -213,3 +220,36 @@ def test_extend_many_sequences(gpu_lib):
         s = batch.qo_start.tolist()
         rows = [r for b in seqs for r in range(s[b], s[b + 1])]
         assert_parity(o[rows].double().numpy(), ref[rows], f"extend B{B} ({len(seqs)} sequences)")
+
+
+@pytest.mark.parametrize("B", [2, 64])
+def test_extend_no_cache_null_pointers_equals_causal_prefill_bitwise(gpu_lib, B):
+    """max_pages_per_seq = 0 with k_cache, v_cache, page_table and prefix_lens
+    all NULL (the header allows it when there is no prefix): every sequence's
+    rows are bitwise those of causal prefill over its new tokens.  B = 2 and
+    B = 64 are batch sizes for which the kernel would rank sequences by prefix
+    length if a prefix could exist."""
+    attn = gpu_lib
+    rng = np.random.default_rng(97 + B)
+    el = [300, 77] if B == 2 else rng.integers(0, 90, B).tolist()
+    batch = workloads.extend_inputs(B, 8, 128, [0] * B, el, "bf16", seed=97 + B, h_kv=2)
+    T, H, D = batch.q.shape
+    H_kv = batch.k.shape[1]
+    q, k, v = batch.q.cuda(), batch.k.cuda(), batch.v.cuda()
+    starts = batch.qo_start.cuda()
+    o = torch.full_like(q, float("nan"))
+    print(f"[case] extend B{B} no cache (NULL pointers, max_pages_per_seq 0)", flush=True)
+    st = attn.attn_extend(q, k, v, None, None, None, None, starts, o, B, H, H_kv, D, T,
+                          max(el), 16, 0, 0, attn.ATTN_BF16, 1 / np.sqrt(D))
+    assert st == attn.ATTN_OK, attn.attn_status_string(st)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert torch.isfinite(o.float()).all(), "rows left unwritten"
+    s = batch.qo_start.tolist()
+    for b in range(B):
+        if s[b + 1] == s[b]:
+            continue
+        ref = attn.prefill(q[None, s[b]:s[b + 1]].contiguous(), k[None, s[b]:s[b + 1]].contiguous(),
+                           v[None, s[b]:s[b + 1]].contiguous(), causal=True, layout="BSHD")
+        torch.cuda.synchronize()
+        assert torch.equal(o[s[b]:s[b + 1]], ref[0].cpu()), f"sequence {b}"

@@ -1,20 +1,21 @@
 """GPU parity of attn_prefill (through the C ABI) against the fp64 oracle.
 
 Bar: max-abs error <= 1e-2 and relative Frobenius error <= 2e-3, over the
-whole output for shapes the oracle finishes in seconds, and over sampled rows
-(computed one by one by the oracle) at the full workload sizes, in the same
-launch configuration the bench times.
+whole output: for shapes the oracle finishes in seconds, and at the full
+workload sizes in the launch configuration the bench times (written into
+NaN-prefilled buffers; the oracle runs per head and row block on a thread
+pool, see whole_tensor.py).
 """
 import math
 import zlib
 
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from parity import assert_parity
+import whole_tensor as whole
+from parity import MAX_ABS_TOL, REL_FRO_TOL, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -127,29 +128,41 @@ def test_prefill_deterministic(gpu_lib):
 
 # ------------------------------------------------------ full workload sizes
 
-def _sample_rows(B, H, Sq, n_random, seed):
-    g = np.random.default_rng(seed)
-    rows = set()
-    for b, h in ((0, 0), (B - 1, H - 1)):
-        for i in (0, 1, 127, 128, Sq // 2, Sq - 129, Sq - 128, Sq - 1):
-            rows.add((b, h, i))
-    for _ in range(n_random):
-        rows.add((int(g.integers(B)), int(g.integers(H)), int(g.integers(Sq))))
-    return sorted(rows)
+# Output buffers start as NaN, so a row the kernel never writes is caught, and
+# the whole output is compared with the oracle (tests/whole_tensor.py).  For
+# the long-context workload the fp32 output is graded too, against the
+# four-times tighter fp32 bar, so the pass does not rest on how the bf16
+# rounding of O (up to 2^-8 |O|, and |O| reaches ~4 in its early causal rows)
+# happens to fall.
+F32_MAX_ABS_FULL, F32_REL_FRO_FULL = 3e-3, 5e-4
 
 
-@pytest.mark.parametrize("cfg,n_random", [(2, 384), (3, 384), (5, 256)])
-def test_prefill_full_config_sampled(gpu_lib, cfg, n_random):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_prefill_full_config_whole(gpu_lib, cfg, progress):
+    attn = gpu_lib
     q, k, v, m = workloads.prefill_config(cfg)
-    o = _run(gpu_lib, q, k, v, m["causal"], m["scale"], m["layout"])
-    rows = _sample_rows(m["B"], m["H"], m["Sq"], n_random, seed=cfg)
-    ref = oracle.sdpa_rows(q, k, v, rows, causal=m["causal"], scale=m["scale"], layout=m["layout"])
-    if m["layout"] == "BHSD":
-        got = torch.stack([o[b, h, i] for b, h, i in rows])
-    else:
-        got = torch.stack([o[b, i, h] for b, h, i in rows])
-    assert torch.isfinite(o.float()).all()
-    assert_parity(_f64(got), ref, f"config {cfg} ({len(rows)} sampled rows)")
+    print(f"[case] prefill {m['name']} whole tensor", flush=True)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    kw = dict(causal=m["causal"], scale=m["scale"], layout=m["layout"])
+    outs = {"o": attn.prefill(qg, kg, vg, out=whole.nan_like(qg), **kw)}
+    if cfg == 5:
+        outs["o_f32"] = attn.prefill(qg, kg, vg, out=whole.nan_like(qg, torch.float32), **kw)
+    torch.cuda.synchronize()
+    outs = {n: t.cpu() for n, t in outs.items()}
+    del qg, kg, vg
+    stats = whole.compare(whole.prefill_units(q, k, v, list(outs), **kw), outs,
+                          progress=progress)
+    for n, st in stats.items():
+        print(f"[parity] {m['name']} {n} (whole tensor): {st}", flush=True)
+        assert st.nonfinite == 0, f"{n}: {st.nonfinite} elements not written (or not finite)"
+    st = stats["o"]
+    assert st.max_abs <= MAX_ABS_TOL and st.rel_fro <= REL_FRO_TOL, f"{m['name']}: {st}"
+    if "o_f32" in stats:
+        st = stats["o_f32"]
+        assert st.max_abs <= F32_MAX_ABS_FULL and st.rel_fro <= F32_REL_FRO_FULL, \
+            f"{m['name']} fp32 output: {st}"
+        assert torch.equal(outs["o_f32"].to(outs["o"].dtype), outs["o"])
 
 
 # ------------------------------------------------------------ stress cases
