@@ -22,8 +22,14 @@ reported too).  Alongside, per workload: a cold-cache pass (a 512 MiB write,
 twice the 256 MiB last-level cache, before every timed step and outside its
 events), the GFX clock sampled over a ~1.5 s sustained window of the same
 step, and for the tiny 128x128 workload the median over 20 replays of a HIP
-graph of 50 launches (launch overhead removed).  The CPU baseline is the fp64
-oracle timed on a bounded sample of the same workload.  Prints ONE JSON line.
+graph of 50 launches (launch overhead removed).  Also sampled over that
+window: socket power, the power cap, the share of the window the firmware
+spent limiting for package power or temperature, and the throttle status.
+Every workload also carries a CPU baseline: the fp64 oracle timed on a
+bounded sample of the same inputs (whole heads, sequences or KV-head groups
+in order; ~15 s for the headline, ~3 s for the others), after the GPU timing,
+with the host described (CPU model, CPU count, BLAS threads).  Prints ONE
+JSON line.
 """
 from __future__ import annotations
 
@@ -122,25 +128,67 @@ class ClockProbe:
         return float(self.amdsmi.amdsmi_get_clock_info(self.handle,
                                                        self.amdsmi.AmdSmiClkType.GFX)["clk"])
 
-    def sustained_mhz(self, fn, seconds=1.5, settle=1.0):
-        """Mean GFX clock over XCDs, median of the samples taken after `settle`
-        seconds of back-to-back fn() calls."""
-        if self.handle is None:
+    def read_power_w(self):
+        """Socket power now, in W (gpu metrics; the power-info call as a fallback)."""
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        for key in ("current_socket_power", "average_socket_power"):
+            val = m.get(key)
+            if isinstance(val, (int, float)) and 0 < val < 100000:
+                return float(val)
+        info = self.amdsmi.amdsmi_get_power_info(self.handle)
+        val = info.get("current_socket_power")
+        return float(val) if isinstance(val, (int, float)) else None
+
+    def power_cap_w(self):
+        try:
+            cap = self.amdsmi.amdsmi_get_power_cap_info(self.handle).get("power_cap")
+            return round(cap / 1e6, 1) if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:
             return None
+
+    def violations(self):
+        """Accumulated throttle-violation counters (package power, socket
+        thermal) and their sample counter; None if unavailable."""
+        try:
+            v = self.amdsmi.amdsmi_get_violation_status(self.handle)
+            vals = {k: v.get(k) for k in ("acc_counter", "acc_ppt_pwr", "acc_socket_thrm",
+                                          "acc_prochot_thrm", "acc_hbm_thrm")}
+            if not all(isinstance(x, int) for x in vals.values()):
+                return None
+            vals["per_ppt_pwr"] = v.get("per_ppt_pwr")  # the library's own percentage
+            return vals
+        except Exception:
+            return None
+
+    def sustained(self, fn, seconds=1.5, settle=1.0):
+        """GFX clock (mean over XCDs) and socket power, medians of the samples
+        taken after `settle` seconds of back-to-back fn() calls, with the
+        power cap, the fraction of that window the firmware spent limiting
+        for package power or temperature (violation counters read before and
+        after it), and the throttle status at its end."""
+        if self.handle is None:
+            return {}
         import threading
         import torch
-        samples, stop = [], threading.Event()
+        clocks, powers, stop = [], [], threading.Event()
         t0 = time.perf_counter()
 
         def sample():
             while not stop.is_set():
                 if time.perf_counter() - t0 >= settle:
                     try:
-                        samples.append(self.read_mhz())
+                        clocks.append(self.read_mhz())
                     except Exception:
                         return
+                    try:
+                        p = self.read_power_w()
+                        if p is not None:
+                            powers.append(p)
+                    except Exception:
+                        pass
                 time.sleep(0.02)
 
+        v0 = self.violations()
         th = threading.Thread(target=sample)
         th.start()
         while time.perf_counter() - t0 < seconds:
@@ -149,10 +197,23 @@ class ClockProbe:
             torch.cuda.synchronize()
         stop.set()
         th.join()
-        if not samples:
-            return None
-        samples.sort()
-        return round(samples[len(samples) // 2], 1)
+        v1 = self.violations()
+        med = lambda xs: round(sorted(xs)[len(xs) // 2], 1) if xs else None
+        out = {"clock_mhz": med(clocks), "power_w": med(powers), "power_cap_w": self.power_cap_w()}
+        if v0 and v1 and v1["acc_counter"] > v0["acc_counter"]:
+            n = v1["acc_counter"] - v0["acc_counter"]
+            out["limit_frac"] = {
+                "package_power": round((v1["acc_ppt_pwr"] - v0["acc_ppt_pwr"]) / n, 3),
+                "socket_thermal": round((v1["acc_socket_thrm"] - v0["acc_socket_thrm"]) / n, 3),
+                "hbm_thermal": round((v1["acc_hbm_thrm"] - v0["acc_hbm_thrm"]) / n, 3),
+                "samples": n, "package_power_pct_reported": v1.get("per_ppt_pwr")}
+        try:
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            out["throttle_status"] = m.get("throttle_status")
+            out["indep_throttle_status"] = m.get("indep_throttle_status")
+        except Exception:
+            pass
+        return out
 
 
 def cache_flusher(mib=512):
@@ -181,7 +242,7 @@ def measure(fn, steps, warmup, stream, clock):
         del buf
         t["cold_mean_ms"] = cold["mean_ms"]
         t["cold_median_ms"] = cold["median_ms"]
-    t["clock_mhz"] = clock.sustained_mhz(fn) if clock is not None else None
+    t["sustained"] = clock.sustained(fn) if clock is not None else {}
     return t
 
 
@@ -211,11 +272,11 @@ def graph_replay_us(fn, stream, launches=50, samples=20):
     return per[len(per) // 2]
 
 
-def bench_prefill(attn, cfg, steps, warmup, clock):
+def bench_prefill(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     import torch
     import workloads
-    q, k, v, m = workloads.prefill_config(cfg)
-    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    qc, kc, vc, m = workloads.prefill_config(cfg)
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
     stream = torch.cuda.current_stream()
     if m["dtype"] == "fp8":
         o = torch.empty(q.shape, dtype=torch.float16, device="cuda")
@@ -252,11 +313,12 @@ def bench_prefill(attn, cfg, steps, warmup, clock):
             "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
     del q, k, v, o
     torch.cuda.empty_cache()
+    cpu = cpu_baseline_prefill(qc, kc, vc, m, cpu_budget) if cpu_budget > 0 else None
     return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof,
-                inputs=(None))
+                cpu_baseline=cpu)
 
 
-def bench_decode(attn, cfg, steps, warmup, clock):
+def bench_decode(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     import torch
     import workloads
     batch = workloads.decode_config(cfg)
@@ -295,7 +357,9 @@ def bench_decode(attn, cfg, steps, warmup, clock):
             else load_traffic(f"decode_gqa_split__{batch.meta['name']}", DECODE_GQA_SRC)}
     del g, ws, o
     torch.cuda.empty_cache()
-    return dict(config=cfg_out, timing=t, bytes_per_step=nbytes, gbs=gbs, roofline=roof)
+    cpu = cpu_baseline_decode(batch, cpu_budget) if cpu_budget > 0 else None
+    return dict(config=cfg_out, timing=t, bytes_per_step=nbytes, gbs=gbs, roofline=roof,
+                cpu_baseline=cpu)
 
 
 def extend_flops(batch):
@@ -310,7 +374,7 @@ def extend_flops(batch):
     return 4.0 * H * D * total
 
 
-def bench_extend(attn, cfg, steps, warmup, clock):
+def bench_extend(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     import torch
     import workloads
     batch = workloads.extend_config(cfg)
@@ -337,7 +401,9 @@ def bench_extend(attn, cfg, steps, warmup, clock):
             "traffic": load_traffic(f"prefill_fwd__{batch.meta['name']}", PREFILL_SRC)}
     del g, o
     torch.cuda.empty_cache()
-    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof)
+    cpu = cpu_baseline_extend(batch, cpu_budget) if cpu_budget > 0 else None
+    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof,
+                cpu_baseline=cpu)
 
 
 def backward_flops(m):
@@ -346,13 +412,13 @@ def backward_flops(m):
     return 2.5 * prefill_flops(m)
 
 
-def bench_backward(attn, cfg, steps, warmup, clock):
+def bench_backward(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     """One step: one attn_prefill_bwd call (delta, dK/dV and dQ kernels) on
     the forward's O and LSE, which are computed once before timing."""
     import torch
     import workloads
-    q, k, v, do, m = workloads.backward_config(cfg)
-    q, k, v, do = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    qc, kc, vc, doc, m = workloads.backward_config(cfg)
+    q, k, v, do = qc.cuda(), kc.cuda(), vc.cuda(), doc.cuda()
     stream = torch.cuda.current_stream()
     o, lse = attn.prefill_with_lse(q, k, v, causal=m["causal"], scale=m["scale"],
                                    layout=m["layout"], stream=stream)
@@ -377,7 +443,9 @@ def bench_backward(attn, cfg, steps, warmup, clock):
             "traffic": load_traffic(f"prefill_bwd__{m['name']}", BACKWARD_SRC)}
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof)
+    cpu = cpu_baseline_backward(qc, kc, vc, doc, m, cpu_budget) if cpu_budget > 0 else None
+    return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof,
+                cpu_baseline=cpu)
 
 
 def copy_calibration(mib):
@@ -420,47 +488,158 @@ def vendor_gemm_reference(n=16384, dtype_name="f16"):
             "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3)}
 
 
-def cpu_baseline_prefill(cfg, budget_s=15.0):
-    """The fp64 oracle as it stands, on whole heads of the same workload,
-    until about budget_s seconds of CPU work; scaled to TFLOP/s."""
-    import workloads
-    import oracle
-    q, k, v, m = workloads.prefill_config(cfg)
-    B, H = m["B"], m["H"]
-    heads = 0
-    t0 = time.perf_counter()
-    for b in range(B):
-        for h in range(H):
-            sl = (slice(b, b + 1), slice(h, h + 1)) if m["layout"] == "BHSD" else None
-            if m["layout"] == "BHSD":
-                oracle.sdpa(q[sl], k[sl], v[sl], causal=m["causal"], scale=m["scale"])
-            else:
-                oracle.sdpa(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1],
-                            causal=m["causal"], scale=m["scale"], layout="BSHD")
-            heads += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        else:
-            continue
-        break
-    dt = time.perf_counter() - t0
-    per_head = prefill_flops(m) / (B * H)
-    threads = None
+def host_info():
+    """The host the CPU baseline runs on: logical CPUs, the CPUs this process
+    may run on, the CPU model, and the BLAS threads numpy's matrix products use
+    (its elementwise loops run on one thread)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+        blas = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
     except Exception:
         pass
-    return {"value": round(per_head * heads / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": f"{heads} of {B * H} heads of the same workload, fp64 oracle, "
-                      f"{dt:.1f} s"}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model,
+            "blas_threads": blas, "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _timed_units(units, budget_s):
+    """Run (work, callable) units in order until about budget_s seconds have
+    passed (at least one); returns (work done, seconds, units run)."""
+    done, n = 0.0, 0
+    t0 = time.perf_counter()
+    for work, fn in units:
+        fn()
+        done += work
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return done, time.perf_counter() - t0, n
+
+
+def _cpu_record(value, unit, sample):
+    h = host_info()
+    return {"value": value, "unit": unit, "cores": h["blas_threads"] or h["affinity_cpus"],
+            "kind": "oracle", "sample": sample}
+
+
+def cpu_baseline_prefill(q, k, v, m, budget_s):
+    """The fp64 oracle as it stands (oracle.sdpa; for fp8 inputs
+    oracle.dequantize_fp8 first), on whole heads of the same workload in
+    order, until about budget_s seconds of CPU work; scaled to TFLOP/s."""
+    import oracle
+    B, H, H_kv = m["B"], m["H"], m["H_kv"]
+    bhsd = m["layout"] == "BHSD"
+    per_head = prefill_flops(m) / (B * H)
+
+    def head(b, h):
+        g = oracle.kv_head(h, H, H_kv)
+        if bhsd:
+            qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1]
+        else:
+            qs, ks, vs = q[b:b + 1, :, h:h + 1], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1]
+        if m["dtype"] == "fp8":
+            qd, kd, vd = m["descales"]
+            qs, ks, vs = (oracle.dequantize_fp8(qs, qd), oracle.dequantize_fp8(ks, kd),
+                          oracle.dequantize_fp8(vs, vd))
+        oracle.sdpa(qs, ks, vs, causal=m["causal"], scale=m["scale"], layout=m["layout"])
+
+    units = [(per_head, lambda b=b, h=h: head(b, h)) for b in range(B) for h in range(H)]
+    flops, dt, n = _timed_units(units, budget_s)
+    return _cpu_record(round(flops / dt / 1e12, 6), "TFLOP/s",
+                       f"{n} of {B * H} heads of the same workload, fp64 oracle, {dt:.1f} s")
+
+
+def cpu_baseline_decode(batch, budget_s):
+    """oracle.paged_decode on the batch's sequences in order until about
+    budget_s seconds; GB/s of the algorithmic K/V bytes of those sequences."""
+    import oracle
+    B, H, D = batch.q.shape
+    H_kv = batch.k_cache.shape[2]
+    lens = batch.seq_lens.tolist()
+    units = [(lens[b] * H_kv * D * 2 * 2,
+              lambda b=b: oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache,
+                                              batch.page_table, batch.seq_lens,
+                                              scale=batch.meta["scale"], batch_indices=[b]))
+             for b in range(B)]
+    nbytes, dt, n = _timed_units(units, budget_s)
+    return _cpu_record(round(nbytes / dt / 1e9, 4), "GB/s",
+                       f"{n} of {B} sequences of the same batch (page-table gather included), "
+                       f"fp64 oracle, {dt:.1f} s")
+
+
+def cpu_baseline_extend(batch, budget_s):
+    """oracle.extend one sequence at a time, in order, until about budget_s
+    seconds; TFLOP/s of those sequences' flops."""
+    import oracle
+    H, D = batch.q.shape[1], batch.q.shape[2]
+    starts = batch.qo_start.tolist()
+    plen = batch.prefix_lens.tolist()
+    B = len(plen)
+
+    def flops(b):
+        E = starts[b + 1] - starts[b]
+        return 4.0 * H * D * (E * plen[b] + E * (E + 1) // 2)
+
+    units = [(flops(b), lambda b=b: oracle.extend(batch.q, batch.k, batch.v, batch.k_cache,
+                                                  batch.v_cache, batch.page_table,
+                                                  batch.prefix_lens, batch.qo_start,
+                                                  scale=batch.meta["scale"], seqs=[b]))
+             for b in range(B)]
+    fl, dt, n = _timed_units(units, budget_s)
+    return _cpu_record(round(fl / dt / 1e12, 6), "TFLOP/s",
+                       f"{n} of {B} sequences of the same batch, fp64 oracle, {dt:.1f} s")
+
+
+def cpu_baseline_backward(q, k, v, do, m, budget_s):
+    """oracle.sdpa_backward on one (batch, KV head) -- its query heads -- at a
+    time, in order, until about budget_s seconds; TFLOP/s of the backward's
+    five products for those heads."""
+    import oracle
+    B, H, H_kv = m["B"], m["H"], m["H_kv"]
+    group = H // H_kv
+    per_head = backward_flops(m) / (B * H)
+    bhsd = m["layout"] == "BHSD"
+
+    def unit(b, g):
+        hs = slice(g * group, (g + 1) * group)
+        if bhsd:
+            sq, sk = (slice(b, b + 1), hs), (slice(b, b + 1), slice(g, g + 1))
+        else:
+            sq = (slice(b, b + 1), slice(None), hs)
+            sk = (slice(b, b + 1), slice(None), slice(g, g + 1))
+        oracle.sdpa_backward(q[sq], k[sk], v[sk], do[sq], causal=m["causal"], scale=m["scale"],
+                             layout=m["layout"])
+
+    units = [(per_head * group, lambda b=b, g=g: unit(b, g)) for b in range(B)
+             for g in range(H_kv)]
+    fl, dt, n = _timed_units(units, budget_s)
+    return _cpu_record(round(fl / dt / 1e12, 6), "TFLOP/s",
+                       f"{n * group} of {B * H} heads ({n} KV-head groups) of the same workload, "
+                       f"fp64 oracle, {dt:.1f} s")
 
 
 def side_measurements(t):
     r4 = lambda x: None if x is None else round(x, 4)
+    sus = t.get("sustained") or {}
     out = {"cold_cache_ms": r4(t["cold_mean_ms"]), "cold_cache_median_ms": r4(t["cold_median_ms"]),
-           "clock_mhz": t["clock_mhz"]}
+           "clock_mhz": sus.get("clock_mhz")}
+    power = {k: sus[k] for k in ("power_w", "power_cap_w", "limit_frac", "throttle_status",
+                                 "indep_throttle_status") if k in sus}
+    if power:
+        out["power"] = power
     if "graph_us_per_launch" in t:
         out["graph_replay_us_per_launch"] = round(t["graph_us_per_launch"], 2)
     return out
@@ -476,7 +655,10 @@ def main():
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of fp64-oracle CPU work for the headline workload's baseline")
+    ap.add_argument("--cpu-budget-extra", type=float, default=3.0,
+                    help="seconds of oracle CPU work for each other workload's baseline")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip timing the vendor GEMM reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -513,18 +695,26 @@ def main():
     results = {}
     for c in cfgs:
         print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
+        # The oracle's CPU baseline runs after the GPU timing of the same
+        # inputs, never alongside it.
+        budget = 0.0 if args.no_cpu_baseline else (
+            args.cpu_budget if c == head_cfg else args.cpu_budget_extra)
         if c in workloads.DECODE_CONFIGS:
-            results[c] = bench_decode(attn, c, args.steps, args.warmup, clock)
+            results[c] = bench_decode(attn, c, args.steps, args.warmup, clock, budget)
         elif c in workloads.EXTEND_CONFIGS:
-            results[c] = bench_extend(attn, c, args.steps, args.warmup, clock)
+            results[c] = bench_extend(attn, c, args.steps, args.warmup, clock, budget)
         elif c in workloads.BACKWARD_CONFIGS:
-            results[c] = bench_backward(attn, c, args.steps, args.warmup, clock)
+            results[c] = bench_backward(attn, c, args.steps, args.warmup, clock, budget)
         else:
-            results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock)
+            results[c] = bench_prefill(attn, c, args.steps, args.warmup, clock, budget)
         r = results[c]
+        cpu_msg = ""
+        if r.get("cpu_baseline"):
+            cpu_msg = f"; cpu oracle {r['cpu_baseline']['value']} {r['cpu_baseline']['unit']}"
         print(f"[bench] config {c}: {r['timing']['mean_ms']:.4f} ms "
               f"{r['roofline']['achieved']} {r['roofline']['unit']} "
-              f"({100 * r['roofline']['frac']:.1f}% of peak)", file=sys.stderr, flush=True)
+              f"({100 * r['roofline']['frac']:.1f}% of peak){cpu_msg}", file=sys.stderr,
+              flush=True)
 
     head = results[head_cfg]
     gemm_ref = None
@@ -533,10 +723,7 @@ def main():
         gemm_ref = vendor_gemm_reference()
         print(f"[bench] vendor GEMM reference: {gemm_ref['tflops']} TFLOP/s", file=sys.stderr,
               flush=True)
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (fp64 oracle) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_prefill(head_cfg, args.cpu_budget)
+    cpu = head.get("cpu_baseline")
 
     extra = {}
     for c, r in results.items():
@@ -545,6 +732,7 @@ def main():
         e = {"config": r["config"], "ms_per_step": round(r["timing"]["mean_ms"], 4),
              "median_ms": round(r["timing"]["median_ms"], 4), "roofline": r["roofline"]}
         e.update(side_measurements(r["timing"]))
+        e["cpu_baseline"] = r.get("cpu_baseline")
         extra[f"config{c}"] = e
 
     line = {
@@ -566,6 +754,7 @@ def main():
         "roofline": head["roofline"],
         **side_measurements(head["timing"]),
         "cpu_baseline": cpu,
+        "cpu_host": None if args.no_cpu_baseline else host_info(),
         "extra": extra,
         "mfma_context": gemm_ref,
     }
