@@ -26,6 +26,7 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = rang
 ATTN_BHSD, ATTN_BSHD = 0, 1
 ATTN_F16, ATTN_BF16 = 0, 1
 ATTN_OUT_F32 = 0x100
+ATTN_DECODE_SCRATCH_BYTES = 32 << 20  # the no-allocation decode's device array per GPU
 LAYOUTS = {"BHSD": ATTN_BHSD, "BSHD": ATTN_BSHD}
 
 # Every symbol include/attn.h declares, with its ctypes signature.
@@ -41,6 +42,8 @@ SIGNATURES = {
     "attn_paged_decode_gqa": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I,
                                    _F, _VP, _SZ, _VP]),
     "attn_paged_decode_gqa_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "attn_paged_decode_gqa_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
+                                           _I, _I, _F, _VP]),
     "attn_paged_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
     "attn_prefill_fp8": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _F,
                               _F, _VP]),
@@ -171,6 +174,16 @@ def attn_paged_decode_gqa(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H,
         H_kv, D, page_size, num_pages, max_pages_per_seq, dtype, float(scale), _ptr(workspace),
         int(workspace_bytes), _stream(stream))
+
+
+def attn_paged_decode_gqa_noalloc(q, k_cache, v_cache, page_table, seq_lens, o, B, H, H_kv, D,
+                                  page_size, num_pages, max_pages_per_seq, dtype, scale,
+                                  stream=None) -> int:
+    """Direct call of the C entry point (no workspace: the library's own
+    device array of ATTN_DECODE_SCRATCH_BYTES); returns its status code."""
+    return load_library().attn_paged_decode_gqa_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(o), B, H,
+        H_kv, D, page_size, num_pages, max_pages_per_seq, dtype, float(scale), _stream(stream))
 
 
 def attn_prefill_fp8(q, k, v, o, B, H, H_kv, Sq, Skv, D, layout, out_dtype, causal, scale,

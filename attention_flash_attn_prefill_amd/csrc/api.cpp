@@ -114,6 +114,45 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+namespace mi355_attn {
+
+// Every check of attn_paged_decode_gqa short of the workspace, before any HIP
+// call.  ATTN_OK with *need = 0: nothing to launch (B * H = 0).  ATTN_OK with
+// *need > 0: a launch needs that many workspace bytes.
+int check_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, const int32_t* seq_lens, const void* o, int B,
+                       int H, int H_kv, int D, int page_size, int num_pages,
+                       int max_pages_per_seq, int dtype, float scale, size_t* need) {
+  *need = 0;
+  if (B < 0 || H < 0 || H_kv < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return ATTN_OK;
+  if ((int64_t)max_pages_per_seq * page_size >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;  // token positions are 32-bit
+  if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
+  const int group = H / H_kv;
+  if (group == 1 && B > 65535) return ATTN_E_UNSUPPORTED;  // grid limit
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return ATTN_E_INVALID;
+  if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
+
+  const SplitPlan p = group == 1 ? plan_splits(B, H, H_kv, max_pages_per_seq, page_size)
+                                 : SplitPlan{0, 0};
+  const GqaPlan g = group == 1 ? GqaPlan{} : plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+  if (group == 1 ? (p.n_splits == 0 || p.n_splits > 65535) : g.ranges == 0)
+    return ATTN_E_UNSUPPORTED;  // grid or index limits
+  *need = attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size);
+  return *need > 0 ? ATTN_OK : ATTN_E_UNSUPPORTED;
+}
+
+}  // namespace mi355_attn
+
 extern "C" {
 
 const char* attn_status_string(int status) {
@@ -435,34 +474,20 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
                           int H, int H_kv, int D, int page_size, int num_pages,
                           int max_pages_per_seq, int dtype, float scale, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || H < 0 || H_kv < 0 || num_pages < 0 || max_pages_per_seq < 0) return ATTN_E_INVALID;
-  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  size_t need = 0;
+  const int st = mi355_attn::check_paged_decode(q, k_cache, v_cache, page_table, seq_lens, o, B,
+                                                H, H_kv, D, page_size, num_pages,
+                                                max_pages_per_seq, dtype, scale, &need);
+  if (st != ATTN_OK || need == 0) return st;
+  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_E_INVALID;
   bool bf16, out_f32;
-  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
-  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
-  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
-  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
-  if ((int64_t)B * H == 0) return ATTN_OK;
-  if ((int64_t)max_pages_per_seq * page_size >= ((int64_t)1 << 31))
-    return ATTN_E_UNSUPPORTED;  // token positions are 32-bit
-  if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
+  parse_dtype(dtype, &bf16, &out_f32);
   const int group = H / H_kv;
   const int qchunks = (group + 31) / 32;
-  if (group == 1 && B > 65535) return ATTN_E_UNSUPPORTED;  // grid limit
-  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return ATTN_E_INVALID;
-  if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
-
   const SplitPlan p = group == 1 ? plan_splits(B, H, H_kv, max_pages_per_seq, page_size)
                                  : SplitPlan{0, 0};
   const GqaPlan g = group == 1 ? GqaPlan{} : plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
-  if (group == 1 ? (p.n_splits == 0 || p.n_splits > 65535) : g.ranges == 0)
-    return ATTN_E_UNSUPPORTED;  // grid or index limits
-  const size_t need =
-      attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size);
-  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_E_INVALID;
 
   const size_t rows = group == 1 ? (size_t)B * H * p.n_splits : (size_t)g.slots * g.rows_per_slot;
   const size_t o_bytes = align256(rows * D * sizeof(float));

@@ -116,4 +116,11 @@ hipError_t launch_paged_decode_gqa(int D, bool bf16, bool out_f32, const DecodeA
 hipError_t launch_decode_combine(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                  hipStream_t s);
 
+// Argument checks of paged decode (api.cpp), shared by the entry point that
+// takes a workspace and the one that uses the library's own array.
+int check_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, const int32_t* seq_lens, const void* o, int B,
+                       int H, int H_kv, int D, int page_size, int num_pages,
+                       int max_pages_per_seq, int dtype, float scale, size_t* need);
+
 }  // namespace mi355_attn

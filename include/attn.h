@@ -279,6 +279,35 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
                           int max_pages_per_seq, int dtype, float scale,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): paged
+ * decode as attn_paged_decode_gqa -- same arguments without the workspace,
+ * same kernels, bitwise the same results and device-side checks -- with the
+ * partial results kept in a device array the library owns:
+ * ATTN_DECODE_SCRATCH_BYTES (32 MiB) on each GPU the library runs on,
+ * reserved when the library's device code is loaded there and held until the
+ * process ends.  Nothing is allocated, freed or synchronised by the call.
+ *
+ *   - Sizes whose attn_paged_decode_gqa_workspace_size exceeds
+ *     ATTN_DECODE_SCRATCH_BYTES are refused with ATTN_E_WORKSPACE, after the
+ *     other argument checks and before any HIP call.
+ *   - The array needs no initialisation: every call writes each partial and
+ *     the metadata it reads back.  It keeps the last call's contents.
+ *   - Every call on one GPU uses that GPU's single array: calls that may
+ *     overlap on one GPU (other streams, other host threads) race on it, and
+ *     the caller must order them (for example, one stream per GPU).
+ *   - The first call on a device looks the array's address up on the device
+ *     current at that call (hipGetSymbolAddress, no allocation), which must be
+ *     the device of `stream`; ATTN_E_HIP if the runtime cannot give it.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_paged_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* page_table, const int32_t* seq_lens, void* o,
+                                  int B, int H, int H_kv, int D, int page_size, int num_pages,
+                                  int max_pages_per_seq, int dtype, float scale,
+                                  hipStream_t stream);
+
 /* Workspace bytes of attn_paged_decode_gqa (0 for invalid sizes). */
 size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D,
                                             int max_pages_per_seq, int page_size);

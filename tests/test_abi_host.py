@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                             "attn_paged_decode_gqa_workspace_size",
                             "attn_paged_decode_gqa_num_splits", "attn_extend",
                             "attn_prefill_fp8", "attn_prefill_lse", "attn_prefill_bwd",
-                            "attn_prefill_bwd_workspace_size"])
+                            "attn_prefill_bwd_workspace_size",
+                            "attn_paged_decode_gqa_noalloc"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -355,3 +356,38 @@ def test_prefill_fp8_validation(kw, status):
 
 def test_prefill_fp8_empty_is_a_noop():
     assert _prefill_fp8(Sq=0, q=None, o=None) == attn.ATTN_OK
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, seq_lens=FAKE, o=FAKE, B=4,
+             H=32, H_kv=8, D=128, page_size=16, num_pages=64, max_pages_per_seq=8, dtype=0,
+             scale=0.1, stream=0)
+    a.update(kw)
+    return attn.attn_paged_decode_gqa_noalloc(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=5), attn.ATTN_E_INVALID),
+    (dict(page_size=32), attn.ATTN_E_UNSUPPORTED),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(q=None), attn.ATTN_E_INVALID),
+    (dict(o=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(scale=float("nan")), attn.ATTN_E_INVALID),
+    (dict(B=0), attn.ATTN_OK),
+    # partials beyond the library's 32 MiB array: refused before any HIP call
+    (dict(B=4096, H=32, H_kv=32, max_pages_per_seq=512), attn.ATTN_E_WORKSPACE),
+    (dict(B=64, H=32, H_kv=32, max_pages_per_seq=8192), attn.ATTN_E_WORKSPACE),
+])
+def test_decode_noalloc_validation(kw, status):
+    assert _decode_noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_workspace_size():
+    """The sizes the no-allocation decode accepts are exactly those whose
+    workspace fits ATTN_DECODE_SCRATCH_BYTES; the bench's decode workloads fit."""
+    cap = attn.ATTN_DECODE_SCRATCH_BYTES
+    assert cap == 32 << 20
+    for B, H, H_kv, mp in [(64, 32, 32, 512), (64, 32, 8, 512), (256, 32, 1, 512)]:
+        assert 0 < attn.attn_paged_decode_gqa_workspace_size(B, H, H_kv, 128, mp, 16) <= cap
+    big = attn.attn_paged_decode_gqa_workspace_size(4096, 32, 32, 128, 512, 16)
+    assert big > cap
