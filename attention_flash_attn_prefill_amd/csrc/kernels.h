@@ -15,7 +15,7 @@ struct PrefillArgs {
   int H, Sq, Skv;       // H query heads
   int H_kv, group;     // KV heads and query heads per KV head (H = H_kv * group)
   int n_mtiles;        // ceil(Sq / BM), set by launch_prefill
-  int total_tiles;     // B * H * n_mtiles  (= grid size), set by launch_prefill
+  int total_tiles;     // grid size (work items), set by launch_prefill
   int64_t q_sb, q_sh;  // element strides of q and o between batches / heads
   int q_ss;            // element stride between query rows
   int64_t k_sb, k_sh;  // element strides of k and v (per batch, per KV head)

@@ -109,21 +109,28 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // head w; every K/V tile staged in LDS then serves the HPW heads, and a
   // partial or causal query tile is RPW rows rather than BM.
   constexpr int RPW = BM / HPW, WPH = NW / HPW;
-  // Work item L = ((b * H_kv + kv_head) * n_mtiles + mt) * (group / HPW) + gg:
+  // Work item L = ((b * H_kv + kv_head) * n_items + item) * (group / HPW) + gg:
   // the query heads that share a KV head are adjacent, so they run the same
   // query tile at the same time on one XCD and read the same K/V tiles
-  // through its L2 (group = 1 is plain (b, h, mt) order).  Extend batches are
-  // ragged, so there the (sequence, KV head) blocks are interleaved over the
-  // XCDs instead of given out in contiguous ranges.
+  // through its L2 (group = 1 is plain (b, h, item) order).  Extend batches
+  // are ragged, so there the (sequence, KV head) blocks are interleaved over
+  // the XCDs instead of given out in contiguous ranges.
+  //
+  // Causal prefill pairs the query tiles of a head: item p runs query tile
+  // n - 1 - p (the heaviest left) and then tile p (the lightest), so every
+  // workgroup walks about n + 1 tiles' worth of keys and the grid has no
+  // tail of short workgroups (n = n_mtiles; the middle tile of an odd n runs
+  // alone).  Other work has one query tile per item.
+  constexpr bool PAIRS = CAUSAL && !EXT;
   const int hgroups = a.group / HPW;
+  const int n_items = PAIRS ? (a.n_mtiles + 1) >> 1 : a.n_mtiles;
   int L = EXT ? xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * hgroups),
                                a.n_mtiles * hgroups)
               : xcd_remap(blockIdx.x, a.total_tiles);
   const int gg = L % hgroups;
   L /= hgroups;
-  int mt = L % a.n_mtiles;
-  L /= a.n_mtiles;
-  if (CAUSAL) mt = a.n_mtiles - 1 - mt;  // heaviest query tiles first
+  const int item = L % n_items;
+  L /= n_items;
   const int hk = L % a.H_kv;
   int b = L / a.H_kv;
   if constexpr (EXT) {
@@ -150,467 +157,476 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     }
   }
   const int h = hk * a.group + gg * HPW + wave / WPH;  // wave-uniform
+  const int n_parts = (PAIRS && a.n_mtiles - 1 - item != item) ? 2 : 1;
 
-  // Sequence sizes.  Extend: Sq = the sequence's new tokens, Skv = prefix +
-  // new, bottom-right causal (offset = prefix length); the first n_pre tiles
-  // hold prefix keys [0, P) from the cache, the rest new keys from k, v.
-  int Sq = a.Sq, Skv = a.Skv, coff = a.causal_off, P = 0, n_pre = 0;
-  int64_t q_base = b * a.q_sb + h * a.q_sh;   // o shares q's element strides
-  int64_t kv_base = b * a.k_sb + hk * a.k_sh;
-  if constexpr (EXT) {
-    const int r0 = a.qo_start[b], r1 = a.qo_start[b + 1];
-    if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // invalid range: not computed
-    Sq = min(r1 - r0, a.Sq);                                // a.Sq = max_extend_len
-    P = a.max_pages > 0 ? max(0, min(a.prefix_lens[b], a.max_pages * kDecodePageSize)) : 0;
-    Skv = P + Sq;
-    coff = P;
-    n_pre = (P + BN - 1) / BN;
-    q_base = (int64_t)r0 * a.q_ss + h * a.q_sh;
-    kv_base = (int64_t)r0 * a.k_ss + hk * a.k_sh;
-  }
-  const char* __restrict__ qp = reinterpret_cast<const char*>(a.q) + q_base * EB;
-  const int64_t o_base = q_base;
-  const char* __restrict__ kp = reinterpret_cast<const char*>(a.k) + kv_base * EB;
-  const char* __restrict__ vp = reinterpret_cast<const char*>(a.v) + kv_base * EB;
+  for (int part = 0; part < n_parts; ++part) {
+    // Query tile of this part: extend in order; causal heaviest first.
+    const int mt = !CAUSAL ? item : (PAIRS && part == 1 ? item : a.n_mtiles - 1 - item);
+    // The second part refills the LDS stages: every wave must be done with
+    // the first part's last tile.
+    if (part > 0) __syncthreads();
 
-  const int m0 = mt * RPW;
-  if (EXT && m0 >= Sq) return;  // past this sequence's new tokens (workgroup-uniform)
-  const int q0 = m0 + (wave % WPH) * 32;
-  const int qi = q0 + li;
-  const bool q_ok = qi < Sq;
-
-  // Q^T fragments (B operand): lane holds Q[qi][16s + 8hi .. +7] (16-bit), or
-  // Q[qi][64s + 32hi .. +31] (fp8).
-  constexpr int QF = FP8 ? 1 : D / 16;
-  constexpr int QF8 = FP8 ? D / 64 : 1;
-  u32x4 qf[QF];
-  i32x8 qf8[QF8];
-  const char* qrow = qp + (int64_t)qi * a.q_ss * EB;
-  if constexpr (FP8) {
-#pragma unroll
-    for (int s = 0; s < QF8; ++s) {
-      const u32x4 lo = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi)
-                            : (u32x4){0u, 0u, 0u, 0u};
-      const u32x4 up = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi + 16)
-                            : (u32x4){0u, 0u, 0u, 0u};
-      qf8[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+    // Sequence sizes.  Extend: Sq = the sequence's new tokens, Skv = prefix +
+    // new, bottom-right causal (offset = prefix length); the first n_pre tiles
+    // hold prefix keys [0, P) from the cache, the rest new keys from k, v.
+    int Sq = a.Sq, Skv = a.Skv, coff = a.causal_off, P = 0, n_pre = 0;
+    int64_t q_base = b * a.q_sb + h * a.q_sh;   // o shares q's element strides
+    int64_t kv_base = b * a.k_sb + hk * a.k_sh;
+    if constexpr (EXT) {
+      const int r0 = a.qo_start[b], r1 = a.qo_start[b + 1];
+      if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // invalid range: not computed
+      Sq = min(r1 - r0, a.Sq);                                // a.Sq = max_extend_len
+      P = a.max_pages > 0 ? max(0, min(a.prefix_lens[b], a.max_pages * kDecodePageSize)) : 0;
+      Skv = P + Sq;
+      coff = P;
+      n_pre = (P + BN - 1) / BN;
+      q_base = (int64_t)r0 * a.q_ss + h * a.q_sh;
+      kv_base = (int64_t)r0 * a.k_ss + hk * a.k_sh;
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < QF; ++s)
-      qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 2 * (16 * s + 8 * hi))
-                   : (u32x4){0u, 0u, 0u, 0u};
-  }
+    const char* __restrict__ qp = reinterpret_cast<const char*>(a.q) + q_base * EB;
+    const int64_t o_base = q_base;
+    const char* __restrict__ kp = reinterpret_cast<const char*>(a.k) + kv_base * EB;
+    const char* __restrict__ vp = reinterpret_cast<const char*>(a.v) + kv_base * EB;
 
-  // Keys this workgroup needs: [0, kv_end).
-  int kv_end = Skv;
-  if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + RPW, Sq) + coff));
-  const int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
-  // Keys this wave needs: [0, wave_kv_end).
-  const bool wave_active = q0 < Sq;
-  const int wave_kv_end = CAUSAL ? min(Skv, min(q0 + 32, Sq) + coff) : Skv;
-  // First key (in the whole key sequence) of tile t, and whether it is a
-  // prefix tile (extend only).
-  auto is_pre = [&](int t) { return EXT && t < n_pre; };
-  auto tile_key0 = [&](int t) { return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : t * BN; };
+    const int m0 = mt * RPW;
+    if (EXT && m0 >= Sq) return;  // past this sequence's new tokens (workgroup-uniform)
+    const int q0 = m0 + (wave % WPH) * 32;
+    const int qi = q0 + li;
+    const bool q_ok = qi < Sq;
 
-  // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
-  // LDS chunk P = (wave * LOADS + i) * 64 + lane of the tile: row P / CPR,
-  // position P % CPR, holding logical chunk position ^ swz(row).
-  int g_off[LOADS];  // byte offset of the chunk within the tile's rows
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int chunk = (wave * LOADS + i) * 64 + lane;
-    const int row = chunk / CPR, pos = chunk % CPR;
-    if constexpr (FP8)
-      g_off[i] = row * a.k_ss + (pos ^ swz_fp8<D>(row)) * 16;
-    else
-      g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
-  }
-  const uint32_t row_bytes = (uint32_t)a.k_ss * EB;
-  const int n_rows = EXT ? Sq : Skv;  // rows of k, v (the new tokens, for extend)
+    // Q^T fragments (B operand): lane holds Q[qi][16s + 8hi .. +7] (16-bit), or
+    // Q[qi][64s + 32hi .. +31] (fp8).
+    constexpr int QF = FP8 ? 1 : D / 16;
+    constexpr int QF8 = FP8 ? D / 64 : 1;
+    u32x4 qf[QF];
+    i32x8 qf8[QF8];
+    const char* qrow = qp + (int64_t)qi * a.q_ss * EB;
+    if constexpr (FP8) {
+  #pragma unroll
+      for (int s = 0; s < QF8; ++s) {
+        const u32x4 lo = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi)
+                              : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 up = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hi + 16)
+                              : (u32x4){0u, 0u, 0u, 0u};
+        qf8[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+      }
+    } else {
+  #pragma unroll
+      for (int s = 0; s < QF; ++s)
+        qf[s] = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 2 * (16 * s + 8 * hi))
+                     : (u32x4){0u, 0u, 0u, 0u};
+    }
 
-  auto tile_rsrc = [&](const char* base, int kv0) {
-    const uint32_t rows = (uint32_t)max(0, n_rows - kv0);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss * EB), (short)0,
-                                             (int)(rows * row_bytes), kBufferConfig);
-  };
+    // Keys this workgroup needs: [0, kv_end).
+    int kv_end = Skv;
+    if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + RPW, Sq) + coff));
+    const int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
+    // Keys this wave needs: [0, wave_kv_end).
+    const bool wave_active = q0 < Sq;
+    const int wave_kv_end = CAUSAL ? min(Skv, min(q0 + 32, Sq) + coff) : Skv;
+    // First key (in the whole key sequence) of tile t, and whether it is a
+    // prefix tile (extend only).
+    auto is_pre = [&](int t) { return EXT && t < n_pre; };
+    auto tile_key0 = [&](int t) { return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : t * BN; };
 
-  // Extend prefix tiles: the loads of a wave cover its WAVE_ROWS rows of the
-  // tile, which lie in one page (page wpage of the tile; pages hold 16
-  // tokens), so one buffer per tile and cache serves them all.  It spans the
-  // page's slots below P, so rows past the prefix read as zero.
-  constexpr int ROWS_PER_LOAD = 64 / CPR;
-  constexpr int WAVE_ROWS = LOADS * ROWS_PER_LOAD;
-  static_assert(!EXT || kDecodePageSize % WAVE_ROWS == 0, "a wave's rows of a tile in one page");
-  const int wpage = (wave * WAVE_ROWS) / kDecodePageSize;  // wave-uniform
-  const int64_t page_elems = (int64_t)kDecodePageSize * a.H_kv * D;
-  const uint32_t slot_bytes = (uint32_t)a.H_kv * D * 2u;
-  const int32_t* ptab = EXT ? a.page_table + (int64_t)b * a.max_pages : nullptr;
-  int pg_off[LOADS];  // byte offset of the chunk within its page
-  if constexpr (EXT) {
-#pragma unroll
+    // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
+    // LDS chunk P = (wave * LOADS + i) * 64 + lane of the tile: row P / CPR,
+    // position P % CPR, holding logical chunk position ^ swz(row).
+    int g_off[LOADS];  // byte offset of the chunk within the tile's rows
+  #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int chunk = (wave * LOADS + i) * 64 + lane;
       const int row = chunk / CPR, pos = chunk % CPR;
-      pg_off[i] = ((row % kDecodePageSize) * a.H_kv * D + hk * D + ((pos ^ swz<D>(row)) * 8)) * 2;
-    }
-  }
-  bool bad_page = false;  // workgroup-uniform: a prefix page id outside the pool
-  // Page ids of the next prefix tile to load (0 where the tile holds no live
-  // token: such a page is never read), fetched a tile ahead by a vector load
-  // -- lane j & 3 reads page j of the tile -- so the read is waited for with
-  // the tile loads (vmcnt) at the next barrier; a scalar load would share its
-  // counter with the LDS operand reads and stall the compute in between.
-  constexpr int PPT = BN / kDecodePageSize;  // pages per tile
-  static_assert(PPT == 4, "page ids of a tile are held by lanes j & 3");
-  int pgv_next = 0;
-  auto fetch_pages = [&](int t) {
-    const int tok = t * BN + (lane & 3) * kDecodePageSize;
-    pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : 0;
-  };
-  // Every wave checks every page of the tile (as unsigned, so negative ids
-  // are rejected too), so all waves agree.
-  auto pages_ok = [&]() {
-    return __builtin_amdgcn_ballot_w64((uint32_t)pgv_next >= (uint32_t)a.num_pages) == 0;
-  };
-  // Buffers of this wave's page of the tile being loaded, in the K and the V
-  // cache.  The range is wave-uniform; keeping it in an SGPR keeps the
-  // compiler from wrapping every load in a waterfall loop over the lanes (it
-  // would otherwise clamp it with a vector instruction).
-  __amdgpu_buffer_rsrc_t pk_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.k_cache, (short)0, 0, kBufferConfig);
-  __amdgpu_buffer_rsrc_t pv_rsrc = pk_rsrc;
-  auto set_page_rsrc = [&](int t) {
-    const int live = min(kDecodePageSize, P - (t * BN + wpage * kDecodePageSize));
-    const int64_t off = live > 0 ? (int64_t)__builtin_amdgcn_readlane(pgv_next, wpage) * page_elems
-                                 : 0;
-    const int nbytes = __builtin_amdgcn_readfirstlane(max(live, 0) * (int)slot_bytes);
-    pk_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_cache + off), (short)0, nbytes,
-                                                kBufferConfig);
-    pv_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_cache + off), (short)0, nbytes,
-                                                kBufferConfig);
-  };
-
-  // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
-  // first for the fp16 conversion; store_v writes it to LDS).
-  u32x4 vreg[LOADS];
-  auto issue_k = [&](int t, LDS_AS uint16_t* k_dst) {
-    if (is_pre(t)) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(pk_rsrc,
-                                                 (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
-                                                 16, pg_off[i], 0, 0, 0);
-      return;
-    }
-    const auto rk = tile_rsrc(kp, tile_key0(t) - P);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
-                                               16, g_off[i], 0, 0, 0);
-  };
-  auto issue_v = [&](int t, LDS_AS uint16_t* v_dst) {
-    const bool pre = is_pre(t);
-    const auto rv = tile_rsrc(vp, pre ? 0 : tile_key0(t) - P);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const auto r = pre ? pv_rsrc : rv;
-      const int off = pre ? pg_off[i] : g_off[i];
-      if constexpr (BF16 || FP8)
-        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      if constexpr (FP8)
+        g_off[i] = row * a.k_ss + (pos ^ swz_fp8<D>(row)) * 16;
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
-                                                 16, off, 0, 0, 0);
+        g_off[i] = (row * a.k_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
     }
-  };
-  // fp8: widen the staged V chunk (16 e4m3fn values of row r, logical chunk
-  // c) to fp16 and write its two fp16 chunks 2c, 2c+1 of row r to LDS.
-  // bf16: convert the staged V chunks to fp16 and write them to LDS.
-  auto store_v = [&](LDS_AS uint16_t* v_dst) {
-    if constexpr (FP8) {
-#pragma unroll
+    const uint32_t row_bytes = (uint32_t)a.k_ss * EB;
+    const int n_rows = EXT ? Sq : Skv;  // rows of k, v (the new tokens, for extend)
+
+    auto tile_rsrc = [&](const char* base, int kv0) {
+      const uint32_t rows = (uint32_t)max(0, n_rows - kv0);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * a.k_ss * EB), (short)0,
+                                               (int)(rows * row_bytes), kBufferConfig);
+    };
+
+    // Extend prefix tiles: the loads of a wave cover its WAVE_ROWS rows of the
+    // tile, which lie in one page (page wpage of the tile; pages hold 16
+    // tokens), so one buffer per tile and cache serves them all.  It spans the
+    // page's slots below P, so rows past the prefix read as zero.
+    constexpr int ROWS_PER_LOAD = 64 / CPR;
+    constexpr int WAVE_ROWS = LOADS * ROWS_PER_LOAD;
+    static_assert(!EXT || kDecodePageSize % WAVE_ROWS == 0, "a wave's rows of a tile in one page");
+    const int wpage = (wave * WAVE_ROWS) / kDecodePageSize;  // wave-uniform
+    const int64_t page_elems = (int64_t)kDecodePageSize * a.H_kv * D;
+    const uint32_t slot_bytes = (uint32_t)a.H_kv * D * 2u;
+    const int32_t* ptab = EXT ? a.page_table + (int64_t)b * a.max_pages : nullptr;
+    int pg_off[LOADS];  // byte offset of the chunk within its page
+    if constexpr (EXT) {
+  #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int chunk = (wave * LOADS + i) * 64 + lane;
-        const int row = chunk / CPR, c = (chunk % CPR) ^ swz_fp8<D>(row);
-        u32x4 w[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2 h = fp8x4_to_f16x4(vreg[i][j]);
-          w[j >> 1][2 * (j & 1)] = h[0];
-          w[j >> 1][2 * (j & 1) + 1] = h[1];
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          *reinterpret_cast<LDS_AS u32x4*>(v_dst + row * D + (((2 * c + u) ^ swz<D>(row)) * 8)) =
-              w[u];
+        const int row = chunk / CPR, pos = chunk % CPR;
+        pg_off[i] = ((row % kDecodePageSize) * a.H_kv * D + hk * D + ((pos ^ swz<D>(row)) * 8)) * 2;
       }
-    } else if constexpr (BF16) {
-#pragma unroll
+    }
+    bool bad_page = false;  // workgroup-uniform: a prefix page id outside the pool
+    // Page ids of the next prefix tile to load (0 where the tile holds no live
+    // token: such a page is never read), fetched a tile ahead by a vector load
+    // -- lane j & 3 reads page j of the tile -- so the read is waited for with
+    // the tile loads (vmcnt) at the next barrier; a scalar load would share its
+    // counter with the LDS operand reads and stall the compute in between.
+    constexpr int PPT = BN / kDecodePageSize;  // pages per tile
+    static_assert(PPT == 4, "page ids of a tile are held by lanes j & 3");
+    int pgv_next = 0;
+    auto fetch_pages = [&](int t) {
+      const int tok = t * BN + (lane & 3) * kDecodePageSize;
+      pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : 0;
+    };
+    // Every wave checks every page of the tile (as unsigned, so negative ids
+    // are rejected too), so all waves agree.
+    auto pages_ok = [&]() {
+      return __builtin_amdgcn_ballot_w64((uint32_t)pgv_next >= (uint32_t)a.num_pages) == 0;
+    };
+    // Buffers of this wave's page of the tile being loaded, in the K and the V
+    // cache.  The range is wave-uniform; keeping it in an SGPR keeps the
+    // compiler from wrapping every load in a waterfall loop over the lanes (it
+    // would otherwise clamp it with a vector instruction).
+    __amdgpu_buffer_rsrc_t pk_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.k_cache, (short)0, 0, kBufferConfig);
+    __amdgpu_buffer_rsrc_t pv_rsrc = pk_rsrc;
+    auto set_page_rsrc = [&](int t) {
+      const int live = min(kDecodePageSize, P - (t * BN + wpage * kDecodePageSize));
+      const int64_t off = live > 0 ? (int64_t)__builtin_amdgcn_readlane(pgv_next, wpage) * page_elems
+                                   : 0;
+      const int nbytes = __builtin_amdgcn_readfirstlane(max(live, 0) * (int)slot_bytes);
+      pk_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_cache + off), (short)0, nbytes,
+                                                  kBufferConfig);
+      pv_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_cache + off), (short)0, nbytes,
+                                                  kBufferConfig);
+    };
+
+    // DMA loads of one K tile, and of one V tile (for bf16, V goes to registers
+    // first for the fp16 conversion; store_v writes it to LDS).
+    u32x4 vreg[LOADS];
+    auto issue_k = [&](int t, LDS_AS uint16_t* k_dst) {
+      if (is_pre(t)) {
+  #pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(pk_rsrc,
+                                                   (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
+                                                   16, pg_off[i], 0, 0, 0);
+        return;
+      }
+      const auto rk = tile_rsrc(kp, tile_key0(t) - P);
+  #pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(k_dst + (wave * LOADS + i) * 512),
+                                                 16, g_off[i], 0, 0, 0);
+    };
+    auto issue_v = [&](int t, LDS_AS uint16_t* v_dst) {
+      const bool pre = is_pre(t);
+      const auto rv = tile_rsrc(vp, pre ? 0 : tile_key0(t) - P);
+  #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int base = (wave * LOADS + i) * 64 * 8 + lane * 8;
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(vreg[i][j]);
-        *reinterpret_cast<LDS_AS u32x4*>(v_dst + base) = w;
+        const auto r = pre ? pv_rsrc : rv;
+        const int off = pre ? pg_off[i] : g_off[i];
+        if constexpr (BF16 || FP8)
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(v_dst + (wave * LOADS + i) * 512),
+                                                   16, off, 0, 0, 0);
+      }
+    };
+    // fp8: widen the staged V chunk (16 e4m3fn values of row r, logical chunk
+    // c) to fp16 and write its two fp16 chunks 2c, 2c+1 of row r to LDS.
+    // bf16: convert the staged V chunks to fp16 and write them to LDS.
+    auto store_v = [&](LDS_AS uint16_t* v_dst) {
+      if constexpr (FP8) {
+  #pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int chunk = (wave * LOADS + i) * 64 + lane;
+          const int row = chunk / CPR, c = (chunk % CPR) ^ swz_fp8<D>(row);
+          u32x4 w[2];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 h = fp8x4_to_f16x4(vreg[i][j]);
+            w[j >> 1][2 * (j & 1)] = h[0];
+            w[j >> 1][2 * (j & 1) + 1] = h[1];
+          }
+  #pragma unroll
+          for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<LDS_AS u32x4*>(v_dst + row * D + (((2 * c + u) ^ swz<D>(row)) * 8)) =
+                w[u];
+        }
+      } else if constexpr (BF16) {
+  #pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int base = (wave * LOADS + i) * 64 * 8 + lane * 8;
+          u32x4 w;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(vreg[i][j]);
+          *reinterpret_cast<LDS_AS u32x4*>(v_dst + base) = w;
+        }
+      }
+    };
+
+    // ---- LDS read offsets (halves, loop invariant).
+    // K (A operand of S^T): lane reads row 32jb + li, logical chunk 2s + hi.
+    // fp8: lane reads row 32jb + li, logical chunks 4s + 2hi and +1 (halves
+    // offsets into rows of D bytes).
+    int k_rd[FP8 ? 2 * (D / 64) : D / 16];
+    if constexpr (FP8) {
+  #pragma unroll
+      for (int s = 0; s < D / 64; ++s)
+  #pragma unroll
+        for (int u = 0; u < 2; ++u)
+          k_rd[2 * s + u] = (li * D + (((4 * s + 2 * hi + u) ^ swz_fp8<D>(li)) * 16)) / 2;
+    } else {
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
+    }
+    // V (transposing reads): lane (group g = lane/16, r, c) names 4 halves of
+    // key 16s + 8half + 4hi + r at d = 32db + 16(g & 1) + 4c.
+    const int g16 = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
+    int v_rd[2][D / 32];
+  #pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int key = 8 * half + 4 * hi + tr_r;  // key within its 16-key step (key & 15)
+  #pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int chunk = 4 * db + 2 * (g16 & 1) + (tr_c >> 1);
+        v_rd[half][db] = key * D + ((chunk ^ swz<D>(key)) * 8) + (tr_c & 1) * 4;
       }
     }
-  };
 
-  // ---- LDS read offsets (halves, loop invariant).
-  // K (A operand of S^T): lane reads row 32jb + li, logical chunk 2s + hi.
-  // fp8: lane reads row 32jb + li, logical chunks 4s + 2hi and +1 (halves
-  // offsets into rows of D bytes).
-  int k_rd[FP8 ? 2 * (D / 64) : D / 16];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int s = 0; s < D / 64; ++s)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        k_rd[2 * s + u] = (li * D + (((4 * s + 2 * hi + u) ^ swz_fp8<D>(li)) * 16)) / 2;
-  } else {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) k_rd[s] = li * D + (((2 * s + hi) ^ swz<D>(li)) * 8);
-  }
-  // V (transposing reads): lane (group g = lane/16, r, c) names 4 halves of
-  // key 16s + 8half + 4hi + r at d = 32db + 16(g & 1) + 4c.
-  const int g16 = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
-  int v_rd[2][D / 32];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int key = 8 * half + 4 * hi + tr_r;  // key within its 16-key step (key & 15)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int chunk = 4 * db + 2 * (g16 & 1) + (tr_c >> 1);
-      v_rd[half][db] = key * D + ((chunk ^ swz<D>(key)) * 8) + (tr_c & 1) * 4;
-    }
-  }
+    f32x16 acc[D / 32];
+  #pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+    float m_run = kNegInf;  // reference max (log2 units) used in the exponent
+    float l_run = 0.f;      // this lane's share of the row sum
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
-  float m_run = kNegInf;  // reference max (log2 units) used in the exponent
-  float l_run = 0.f;      // this lane's share of the row sum
+    // ---- per-tile pieces.
 
-  // ---- per-tile pieces.
+    // S^T = K Q^T for one tile: one 32-key accumulator chain per 32 keys,
+    // interleaved.
+    auto qk = [&](const LDS_AS uint16_t* ks, f32x16 (&sc)[BN / 32]) {
+      if constexpr (FP8) {
+        // Rows of D bytes: block jb starts at byte 32 jb D.
+        i32x8 kf8[D / 64][BN / 32];
+  #pragma unroll
+        for (int s = 0; s < D / 64; ++s)
+  #pragma unroll
+          for (int jb = 0; jb < BN / 32; ++jb) {
+            const u32x4 lo = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s]);
+            const u32x4 up = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s + 1]);
+            kf8[s][jb] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+          }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
+  #pragma unroll
+        for (int s = 0; s < D / 64; ++s)
+  #pragma unroll
+          for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk_fp8(kf8[s][jb], qf8[s], sc[jb]);
+        return;
+      }
+      // All K fragments are read before the first MFMA (the fence keeps the
+      // scheduler from recycling two registers and exposing an LDS round trip
+      // per MFMA pair).
+      u32x4 kf[D / 16][BN / 32];
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+  #pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb)
+          kf[s][jb] = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+  #pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk<BF16>(kf[s][jb], qf[s], sc[jb]);
+    };
 
-  // S^T = K Q^T for one tile: one 32-key accumulator chain per 32 keys,
-  // interleaved.
-  auto qk = [&](const LDS_AS uint16_t* ks, f32x16 (&sc)[BN / 32]) {
-    if constexpr (FP8) {
-      // Rows of D bytes: block jb starts at byte 32 jb D.
-      i32x8 kf8[D / 64][BN / 32];
-#pragma unroll
-      for (int s = 0; s < D / 64; ++s)
-#pragma unroll
-        for (int jb = 0; jb < BN / 32; ++jb) {
-          const u32x4 lo = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s]);
-          const u32x4 up = *reinterpret_cast<const LDS_AS u32x4*>(ks + 16 * jb * D + k_rd[2 * s + 1]);
-          kf8[s][jb] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                               (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+    // Mask keys past the sequence end and (causal) above the diagonal; in an
+    // extend prefix tile, the rows past the prefix.
+    auto mask_tile = [&](int t, f32x16 (&sc)[BN / 32]) {
+      const int kv0 = tile_key0(t);
+      const bool pre = is_pre(t);
+      const bool need_mask = pre ? kv0 + BN > P
+                                 : (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0 + coff);
+      if (need_mask) {
+        const int lim = pre ? P - 1 : (CAUSAL ? min(Skv - 1, qi + coff) : Skv - 1);
+  #pragma unroll
+        for (int jb = 0; jb < BN / 32; ++jb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * jb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > lim) sc[jb][r] = kNegInf;
+          }
+      }
+    };
+
+    // Row max over the tile's keys and the lazy rescale; returns the
+    // reference max used in this tile's exponent.
+    auto max_rescale = [&](const f32x16 (&sc)[BN / 32]) {
+      float mx = kNegInf;
+  #pragma unroll
+      for (int jb = 0; jb < BN / 32; ++jb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
+      mx = pair_max(mx) * a.c;
+      // Move the reference max only when some row's max grew by more than 8.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+  #pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        m_run = m_new;
+      }
+      return (m_run == kNegInf) ? 0.f : m_run;
+    };
+
+    // P^T = exp2(S^T * c - base) rounded to fp16 (the B operand of P.V), and
+    // the row sum of exactly those rounded values.
+    auto exp_tile = [&](const f32x16 (&sc)[BN / 32], float base, u32x4 (&pf)[BN / 16]) {
+  #pragma unroll
+      for (int s = 0; s < BN / 16; ++s) {
+        float e[8];
+  #pragma unroll
+        for (int j = 0; j < 8; ++j)
+          e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s >> 1][8 * (s & 1) + j], a.c, -base));
+        // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
+        // ext-vector *element* (pf[s][j]) as a read of element 0.
+        f16x2 hp[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          hp[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
+        pf[s] = (u32x4){__builtin_bit_cast(uint32_t, hp[0]), __builtin_bit_cast(uint32_t, hp[1]),
+                        __builtin_bit_cast(uint32_t, hp[2]), __builtin_bit_cast(uint32_t, hp[3])};
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          l_run = __builtin_amdgcn_fdot2(hp[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
+                                         false);
+      }
+    };
+
+    // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
+    // of the lane half's 16-key step).
+    auto pv = [&](const u32x4 (&pf)[BN / 16], const LDS_AS uint16_t* vs) {
+      // All V^T fragments are read before the first MFMA (see qk).
+      u32x4 vf[BN / 16][D / 32];
+  #pragma unroll
+      for (int s = 0; s < BN / 16; ++s)
+  #pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[0][db]));
+          const fp16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[1][db]));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
+          vf[s][db] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
         }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
-#pragma unroll
-      for (int s = 0; s < D / 64; ++s)
-#pragma unroll
-        for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk_fp8(kf8[s][jb], qf8[s], sc[jb]);
-      return;
-    }
-    // All K fragments are read before the first MFMA (the fence keeps the
-    // scheduler from recycling two registers and exposing an LDS round trip
-    // per MFMA pair).
-    u32x4 kf[D / 16][BN / 32];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-      for (int jb = 0; jb < BN / 32; ++jb)
-        kf[s][jb] = *reinterpret_cast<const LDS_AS u32x4*>(ks + 32 * jb * D + k_rd[s]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = (f32x16){};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-      for (int jb = 0; jb < BN / 32; ++jb) sc[jb] = mfma_qk<BF16>(kf[s][jb], qf[s], sc[jb]);
-  };
+  #pragma unroll
+      for (int s = 0; s < BN / 16; ++s)
+  #pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma_pv(vf[s][db], pf[s], acc[db]);
+    };
 
-  // Mask keys past the sequence end and (causal) above the diagonal; in an
-  // extend prefix tile, the rows past the prefix.
-  auto mask_tile = [&](int t, f32x16 (&sc)[BN / 32]) {
-    const int kv0 = tile_key0(t);
-    const bool pre = is_pre(t);
-    const bool need_mask = pre ? kv0 + BN > P
-                               : (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0 + coff);
-    if (need_mask) {
-      const int lim = pre ? P - 1 : (CAUSAL ? min(Skv - 1, qi + coff) : Skv - 1);
-#pragma unroll
-      for (int jb = 0; jb < BN / 32; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * jb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key > lim) sc[jb][r] = kNegInf;
+    // ---- main loop: two LDS stages; tile t+1 streams in while tile t
+    // computes; one barrier per tile.
+    LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
+    LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
+
+    // A tile is loaded only when its pages check out (dense tiles always do);
+    // its page buffers are set up and the following tile's ids are fetched.
+    auto load_ok = [&](int t) {
+      if constexpr (EXT) {
+        if (is_pre(t)) {
+          if (!pages_ok()) bad_page = true;
+          else set_page_rsrc(t);
         }
-    }
-  };
-
-  // Row max over the tile's keys and the lazy rescale; returns the
-  // reference max used in this tile's exponent.
-  auto max_rescale = [&](const f32x16 (&sc)[BN / 32]) {
-    float mx = kNegInf;
-#pragma unroll
-    for (int jb = 0; jb < BN / 32; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
-    mx = pair_max(mx) * a.c;
-    // Move the reference max only when some row's max grew by more than 8.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-      m_run = m_new;
-    }
-    return (m_run == kNegInf) ? 0.f : m_run;
-  };
-
-  // P^T = exp2(S^T * c - base) rounded to fp16 (the B operand of P.V), and
-  // the row sum of exactly those rounded values.
-  auto exp_tile = [&](const f32x16 (&sc)[BN / 32], float base, u32x4 (&pf)[BN / 16]) {
-#pragma unroll
-    for (int s = 0; s < BN / 16; ++s) {
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s >> 1][8 * (s & 1) + j], a.c, -base));
-      // Keep the pairs as f16x2 values: clang lowers a bit-cast of an
-      // ext-vector *element* (pf[s][j]) as a read of element 0.
-      f16x2 hp[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        hp[j] = __builtin_convertvector((f32x2){e[2 * j], e[2 * j + 1]}, f16x2);
-      pf[s] = (u32x4){__builtin_bit_cast(uint32_t, hp[0]), __builtin_bit_cast(uint32_t, hp[1]),
-                      __builtin_bit_cast(uint32_t, hp[2]), __builtin_bit_cast(uint32_t, hp[3])};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        l_run = __builtin_amdgcn_fdot2(hp[j], (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l_run,
-                                       false);
-    }
-  };
-
-  // O^T += V^T P^T ; V^T operand = two transposing reads (keys +0..3, +8..11
-  // of the lane half's 16-key step).
-  auto pv = [&](const u32x4 (&pf)[BN / 16], const LDS_AS uint16_t* vs) {
-    // All V^T fragments are read before the first MFMA (see qk).
-    u32x4 vf[BN / 16][D / 32];
-#pragma unroll
-    for (int s = 0; s < BN / 16; ++s)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[0][db]));
-        const fp16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (LDS_AS fp16x4_t*)(vs + 16 * s * D + v_rd[1][db]));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi4);
-        vf[s][db] = (u32x4){l2[0], l2[1], h2[0], h2[1]};
+        fetch_pages(t + 1);
       }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < BN / 16; ++s)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_pv(vf[s][db], pf[s], acc[db]);
-  };
-
-  // ---- main loop: two LDS stages; tile t+1 streams in while tile t
-  // computes; one barrier per tile.
-  LDS_AS uint16_t* const Ks[2] = {(LDS_AS uint16_t*)k_lds0, (LDS_AS uint16_t*)k_lds1};
-  LDS_AS uint16_t* const Vs[2] = {(LDS_AS uint16_t*)v_lds0, (LDS_AS uint16_t*)v_lds1};
-
-  // A tile is loaded only when its pages check out (dense tiles always do);
-  // its page buffers are set up and the following tile's ids are fetched.
-  auto load_ok = [&](int t) {
-    if constexpr (EXT) {
-      if (is_pre(t)) {
-        if (!pages_ok()) bad_page = true;
-        else set_page_rsrc(t);
+      return !bad_page;
+    };
+    if constexpr (EXT) fetch_pages(0);
+    if (n_tiles > 0 && load_ok(0)) {
+      issue_v(0, Vs[0]);
+      issue_k(0, Ks[0]);
+      store_v(Vs[0]);
+    }
+    auto iteration = [&](int t, auto par) {
+      constexpr int S = decltype(par)::value;  // t % 2
+      // Tile t has landed for this wave; after the barrier for every wave, and
+      // every wave is done with tile t-1, whose stages are refilled next.
+      wait_vmcnt<0>();
+      __syncthreads();
+      const bool more = t + 1 < n_tiles && load_ok(t + 1);
+      if (more) {
+        issue_v(t + 1, Vs[S ^ 1]);
+        issue_k(t + 1, Ks[S ^ 1]);
       }
-      fetch_pages(t + 1);
+      if (wave_active && (is_pre(t) || tile_key0(t) < wave_kv_end)) {
+        f32x16 sc[BN / 32];
+        qk(Ks[S], sc);
+        mask_tile(t, sc);
+        const float base = max_rescale(sc);
+        u32x4 pf[BN / 16];
+        exp_tile(sc, base, pf);
+        pv(pf, Vs[S]);
+      }
+      if (more) store_v(Vs[S ^ 1]);
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{});
     }
-    return !bad_page;
-  };
-  if constexpr (EXT) fetch_pages(0);
-  if (n_tiles > 0 && load_ok(0)) {
-    issue_v(0, Vs[0]);
-    issue_k(0, Ks[0]);
-    store_v(Vs[0]);
-  }
-  auto iteration = [&](int t, auto par) {
-    constexpr int S = decltype(par)::value;  // t % 2
-    // Tile t has landed for this wave; after the barrier for every wave, and
-    // every wave is done with tile t-1, whose stages are refilled next.
-    wait_vmcnt<0>();
-    __syncthreads();
-    const bool more = t + 1 < n_tiles && load_ok(t + 1);
-    if (more) {
-      issue_v(t + 1, Vs[S ^ 1]);
-      issue_k(t + 1, Ks[S ^ 1]);
-    }
-    if (wave_active && (is_pre(t) || tile_key0(t) < wave_kv_end)) {
-      f32x16 sc[BN / 32];
-      qk(Ks[S], sc);
-      mask_tile(t, sc);
-      const float base = max_rescale(sc);
-      u32x4 pf[BN / 16];
-      exp_tile(sc, base, pf);
-      pv(pf, Vs[S]);
-    }
-    if (more) store_v(Vs[S ^ 1]);
-  };
-  for (int t = 0; t < n_tiles; t += 2) {
-    iteration(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{});
-  }
 
-  // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
-  // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
-  const float l_tot = pair_sum(l_run);
-  if (a.lse != nullptr && q_ok && hi == 0) {
-    // log2-sum-exp of s c is m_run + log2(l); the natural one of s scale is
-    // that times ln 2.
-    const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
-    a.lse[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
-  }
-  // A rejected prefix page makes the rows NaN (the key set is unknown).
-  const float inv =
-      bad_page ? __builtin_nanf("") : (l_tot > 0.f ? a.o_scale / l_tot : 0.f);
-  if (q_ok) {
-    const int64_t row = o_base + (int64_t)qi * a.q_ss;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float* v4 = reinterpret_cast<const float*>(&acc[db]) + 4 * g;
-        const int d0 = 32 * db + 8 * g + 4 * hi;
-        if constexpr (OF32) {
-          const f32x4 out = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + row + d0) = out;
-        } else {
-          u32x2 out;
-          if constexpr (BF16) {
-            out[0] = pack_bf16(v4[0] * inv, v4[1] * inv);
-            out[1] = pack_bf16(v4[2] * inv, v4[3] * inv);
+    // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
+    // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
+    const float l_tot = pair_sum(l_run);
+    if (a.lse != nullptr && q_ok && hi == 0) {
+      // log2-sum-exp of s c is m_run + log2(l); the natural one of s scale is
+      // that times ln 2.
+      const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+      a.lse[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
+    }
+    // A rejected prefix page makes the rows NaN (the key set is unknown).
+    const float inv =
+        bad_page ? __builtin_nanf("") : (l_tot > 0.f ? a.o_scale / l_tot : 0.f);
+    if (q_ok) {
+      const int64_t row = o_base + (int64_t)qi * a.q_ss;
+  #pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float* v4 = reinterpret_cast<const float*>(&acc[db]) + 4 * g;
+          const int d0 = 32 * db + 8 * g + 4 * hi;
+          if constexpr (OF32) {
+            const f32x4 out = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + row + d0) = out;
           } else {
-            out[0] = pack_f16(v4[0] * inv, v4[1] * inv);
-            out[1] = pack_f16(v4[2] * inv, v4[3] * inv);
+            u32x2 out;
+            if constexpr (BF16) {
+              out[0] = pack_bf16(v4[0] * inv, v4[1] * inv);
+              out[1] = pack_bf16(v4[2] * inv, v4[3] * inv);
+            } else {
+              out[0] = pack_f16(v4[0] * inv, v4[1] * inv);
+              out[1] = pack_f16(v4[2] * inv, v4[3] * inv);
+            }
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + row + d0) = out;
           }
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + row + d0) = out;
         }
-      }
-  }
+    }
+  }  // part
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -619,7 +635,9 @@ template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = f
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
   constexpr int RPW = 32 * NW / HPW;  // query rows per head in a workgroup
   const int64_t n_mtiles = (a.Sq + RPW - 1) / RPW;
-  const int64_t total = (int64_t)B * (a.H / HPW) * n_mtiles;
+  // causal prefill: one workgroup per pair of query tiles (see the kernel)
+  const int64_t n_items = (CAUSAL && !EXT) ? (n_mtiles + 1) / 2 : n_mtiles;
+  const int64_t total = (int64_t)B * (a.H / HPW) * n_items;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;
   a.total_tiles = (int)total;
