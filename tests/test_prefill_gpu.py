@@ -243,3 +243,24 @@ def test_prefill_out_f32(gpu_lib, dtype, D, causal):
                   max_abs_tol=F32_MAX_ABS, rel_fro_tol=F32_REL_FRO)
     # The default output is the fp32 result rounded to nearest even.
     assert torch.equal(o32.to(o16.dtype), o16)
+
+
+# ---------------------------------------------------- causal query-tile pairs
+
+@pytest.mark.parametrize("Sq", [1, 63, 64, 65, 255, 256, 257, 511, 767, 1024, 1280])
+@pytest.mark.parametrize("D,H,H_kv", [(128, 2, 2), (64, 2, 2), (128, 8, 2)])
+def test_prefill_causal_tile_pairs(gpu_lib, Sq, D, H, H_kv):
+    """Causal prefill gives each workgroup a pair of query tiles (the
+    heaviest left, then the lightest; the middle one alone when the count is
+    odd): 1 to 10 tiles of 256 (D = 128), 128 (D = 64) or, with four query
+    heads per workgroup, 64 rows, with Skv = Sq + 37 so the diagonal is
+    offset, into a NaN-filled output."""
+    Skv = Sq + 37
+    q, k, v = workloads.prefill_inputs(1, H, Sq, Skv, D, "bf16", "BHSD", seed=Sq + D + H_kv,
+                                       h_kv=H_kv)
+    print(f"[case] causal pairs Sq{Sq} Skv{Skv} D{D} H{H}/{H_kv}", flush=True)
+    qg = q.cuda()
+    o = gpu_lib.prefill(qg, k.cuda(), v.cuda(), causal=True, out=whole.nan_like(qg))
+    torch.cuda.synchronize()
+    assert_parity(_f64(o.cpu()), oracle.sdpa(q, k, v, causal=True),
+                  f"causal pairs Sq{Sq} D{D} H{H}/{H_kv}")
