@@ -28,10 +28,17 @@ std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
 
 // Device address of `scratch` on the current device (looked up on the first
-// call for that device); ATTN_E_HIP if the runtime cannot give it.
-int scratch_address(void** out) {
+// call for that device); ATTN_E_HIP if the runtime cannot give it, and
+// ATTN_E_INVALID if `stream` belongs to another device (the address would
+// not be valid there).
+int scratch_address(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return ATTN_E_HIP;
+    if (sdev != dev) return ATTN_E_INVALID;
+  }
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (g_scratch_ptr[dev] == nullptr) {
     void* p = nullptr;
@@ -59,7 +66,7 @@ extern "C" int attn_paged_decode_gqa_noalloc(const void* q, const void* k_cache,
   if (st != ATTN_OK || need == 0) return st;
   if (need > ATTN_DECODE_SCRATCH_BYTES) return ATTN_E_WORKSPACE;
   void* ws = nullptr;
-  const int sa = scratch_address(&ws);
+  const int sa = scratch_address(stream, &ws);
   if (sa != ATTN_OK) return sa;
   // The kernels of the workspace form, with the array as the workspace: they
   // write every partial and the metadata they later read, so nothing needs

@@ -298,8 +298,9 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
  *     overlap on one GPU (other streams, other host threads) race on it, and
  *     the caller must order them (for example, one stream per GPU).
  *   - The first call on a device looks the array's address up on the device
- *     current at that call (hipGetSymbolAddress, no allocation), which must be
- *     the device of `stream`; ATTN_E_HIP if the runtime cannot give it.
+ *     current at that call (hipGetSymbolAddress, no allocation); ATTN_E_HIP if
+ *     the runtime cannot give it.  `stream` must belong to the current device
+ *     (else ATTN_E_INVALID).
  */
 #define ATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
 int attn_paged_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,

@@ -51,6 +51,29 @@ def test_decode_noalloc_matches_workspace_form_twice(gpu_lib):
     assert_parity(o_na.double().numpy(), ref, "noalloc decode, second (smaller) call")
 
 
+def test_decode_noalloc_on_a_side_stream(gpu_lib):
+    """A non-default stream of the current device is accepted; the result is
+    bitwise the workspace form's."""
+    attn = gpu_lib
+    b = workloads.paged_decode_inputs(B=3, H=8, D=64, dtype="f16", page_size=16, num_pages=64,
+                                      seq_lens=[5, 300, 17], seed=10, h_kv=2)
+    g = {n: getattr(b, n).cuda() for n in ("q", "k_cache", "v_cache", "page_table", "seq_lens")}
+    ref = attn.paged_decode(g["q"], g["k_cache"], g["v_cache"], g["page_table"], g["seq_lens"],
+                            scale=0.125)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o = torch.full_like(g["q"], float("nan"))
+    print("[case] decode noalloc on a side stream", flush=True)
+    with torch.cuda.stream(side):
+        st = attn.attn_paged_decode_gqa_noalloc(g["q"], g["k_cache"], g["v_cache"],
+                                                g["page_table"], g["seq_lens"], o, 3, 8, 2, 64,
+                                                16, 64, b.max_pages_per_seq, attn.ATTN_F16, 0.125,
+                                                stream=side)
+    assert st == attn.ATTN_OK, attn.attn_status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+
+
 def test_decode_noalloc_refuses_oversized(gpu_lib):
     attn = gpu_lib
     q = torch.zeros((4096, 32, 128), dtype=torch.float16, device="cuda")
