@@ -464,10 +464,12 @@ def copy_calibration(mib):
     torch.cuda.empty_cache()
 
 
-def vendor_gemm_reference(n=16384, dtype_name="f16"):
+def vendor_gemm_reference(n=16384, dtype_name="f16", clock=None):
     """Throughput of the vendor's tuned dense GEMM (torch.matmul -> hipBLASLt)
     on this GPU, as context for the MFMA roofline: sustained matrix-core load
-    runs the chip below its 2.4 GHz peak clock."""
+    runs the chip below its 2.4 GHz peak clock.  With a clock probe, also the
+    clock, socket power and limiter share over a sustained window of the
+    same product, and the energy per flop they imply."""
     import torch
     dt = torch.float16 if dtype_name == "f16" else torch.bfloat16
     a = torch.randn(n, n, device="cuda", dtype=dt)
@@ -482,10 +484,18 @@ def vendor_gemm_reference(n=16384, dtype_name="f16"):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 5
+    sus = clock.sustained(lambda: a @ b, seconds=2.5, settle=1.5) if clock is not None else {}
     del a, b
     torch.cuda.empty_cache()
-    return {"what": f"torch.matmul {dtype_name} {n}x{n}x{n} (hipBLASLt)",
-            "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3)}
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    out = {"what": f"torch.matmul {dtype_name} {n}x{n}x{n} (hipBLASLt)",
+           "tflops": round(tflops, 1), "ms": round(ms, 3)}
+    if sus:
+        out["clock_mhz"] = sus.get("clock_mhz")
+        out["power"] = {k: sus[k] for k in ("power_w", "power_cap_w", "limit_frac") if k in sus}
+        if sus.get("power_w"):
+            out["pj_per_flop"] = round(sus["power_w"] / (tflops * 1e12) * 1e12, 3)
+    return out
 
 
 def host_info():
@@ -631,7 +641,9 @@ def cpu_baseline_backward(q, k, v, do, m, budget_s):
                        f"fp64 oracle, {dt:.1f} s")
 
 
-def side_measurements(t):
+def side_measurements(t, work=None, unit=None):
+    """Cold-cache time, clock, power (and, for a flop count, the energy per
+    flop at the sustained power and the warm time) of one workload."""
     r4 = lambda x: None if x is None else round(x, 4)
     sus = t.get("sustained") or {}
     out = {"cold_cache_ms": r4(t["cold_mean_ms"]), "cold_cache_median_ms": r4(t["cold_median_ms"]),
@@ -639,6 +651,8 @@ def side_measurements(t):
     power = {k: sus[k] for k in ("power_w", "power_cap_w", "limit_frac", "throttle_status",
                                  "indep_throttle_status") if k in sus}
     if power:
+        if work and unit == "flop" and power.get("power_w"):
+            power["pj_per_flop"] = round(power["power_w"] * t["mean_ms"] * 1e-3 / work * 1e12, 3)
         out["power"] = power
     if "graph_us_per_launch" in t:
         out["graph_replay_us_per_launch"] = round(t["graph_us_per_launch"], 2)
@@ -720,7 +734,7 @@ def main():
     gemm_ref = None
     if not args.no_gemm_reference:
         print("[bench] vendor GEMM reference ...", file=sys.stderr, flush=True)
-        gemm_ref = vendor_gemm_reference()
+        gemm_ref = vendor_gemm_reference(clock=clock)
         print(f"[bench] vendor GEMM reference: {gemm_ref['tflops']} TFLOP/s", file=sys.stderr,
               flush=True)
     cpu = head.get("cpu_baseline")
@@ -731,7 +745,7 @@ def main():
             continue
         e = {"config": r["config"], "ms_per_step": round(r["timing"]["mean_ms"], 4),
              "median_ms": round(r["timing"]["median_ms"], 4), "roofline": r["roofline"]}
-        e.update(side_measurements(r["timing"]))
+        e.update(side_measurements(r["timing"], r.get("flops_per_step"), "flop"))
         e["cpu_baseline"] = r.get("cpu_baseline")
         extra[f"config{c}"] = e
 
@@ -752,7 +766,7 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": head["config"],
         "roofline": head["roofline"],
-        **side_measurements(head["timing"]),
+        **side_measurements(head["timing"], head.get("flops_per_step"), "flop"),
         "cpu_baseline": cpu,
         "cpu_host": None if args.no_cpu_baseline else host_info(),
         "extra": extra,
