@@ -70,6 +70,27 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+// Sum / max of an int over the 64 lanes of a wave (every lane active), as a
+// wave-uniform value: butterflies inside each quad and row of 16 lanes by DPP
+// (quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, row_ror 8), then the four row
+// results read out.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Workgroup -> work item.  The dispatcher sends workgroup w to XCD w % 8; give
 // each XCD a contiguous range of work items so one head's tiles share an L2.
 // Bijective on [0, total).

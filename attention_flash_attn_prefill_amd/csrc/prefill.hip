@@ -97,7 +97,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[BN * D];
-  __shared__ int ext_seq;  // extend: the sequence this workgroup works on
+  // Extend: this workgroup's unit (sequence, query tile) and the sequence's
+  // first row, new tokens and prefix length, when wave 0 has looked them up.
+  __shared__ int ext_unit[5];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,49 +114,118 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // Work item L = ((b * H_kv + kv_head) * n_items + item) * (group / HPW) + gg:
   // the query heads that share a KV head are adjacent, so they run the same
   // query tile at the same time on one XCD and read the same K/V tiles
-  // through its L2 (group = 1 is plain (b, h, item) order).  Extend batches
-  // are ragged, so there the (sequence, KV head) blocks are interleaved over
-  // the XCDs instead of given out in contiguous ranges.
+  // through its L2 (group = 1 is plain (b, h, item) order).
   //
   // Causal prefill pairs the query tiles of a head: item p runs query tile
   // n - 1 - p (the heaviest left) and then tile p (the lightest), so every
   // workgroup walks about n + 1 tiles' worth of keys and the grid has no
   // tail of short workgroups (n = n_mtiles; the middle tile of an odd n runs
   // alone).  Other work has one query tile per item.
+  //
+  // Extend batches are ragged.  With at most 64 sequences the work goes out
+  // longest first over the whole batch: a unit is (sequence b, query tile
+  // mt), worth ceil(P_b / RPW) + mt + 1 (its prefix plus causal keys, in
+  // query-tile lengths), and units are taken in decreasing worth (ties by
+  // sequence), each as H_kv * group / HPW adjacent workgroups (its KV heads
+  // and head groups: with that a multiple of 8, a KV head always runs on the
+  // same XCD).  The dispatcher hands an XCD's workgroups to its shader
+  // engines in turn and in order, so heavy units last would leave engines
+  // idle behind a long one.  Wave 0 finds this workgroup's unit from the
+  // batch's sizes (one lane per sequence): the unit's worth c by bisection
+  // on the count of units worth at least c, then its sequence among those
+  // with a unit worth exactly c.  Units past the last non-empty one have no
+  // rows.  Larger batches go in (sequence, KV head) blocks interleaved over
+  // the XCDs, heaviest query tile first within a block.
   constexpr bool PAIRS = CAUSAL && !EXT;
   const int hgroups = a.group / HPW;
   const int n_items = PAIRS ? (a.n_mtiles + 1) >> 1 : a.n_mtiles;
-  int L = EXT ? xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * hgroups),
-                               a.n_mtiles * hgroups)
-              : xcd_remap(blockIdx.x, a.total_tiles);
-  const int gg = L % hgroups;
-  L /= hgroups;
-  const int item = L % n_items;
-  L /= n_items;
-  const int hk = L % a.H_kv;
-  int b = L / a.H_kv;
+  int gg, item, hk, b;
+  int e_r0 = 0, e_len = 0, e_pre = 0;  // sequence b's first row, new tokens, prefix
+  bool e_known = false;                // whether those three are set (workgroup-uniform)
   if constexpr (EXT) {
-    // Longest prefix first: the work order takes sequences by rank of their
-    // prefix length (descending, ties by index), so the longest work items of
-    // a ragged batch start first instead of last.  Thread t ranks sequence t
-    // and the one whose rank is this workgroup's sequence slot publishes it.
-    // Only for small batches (B <= 64: at most 64 uniform loads per thread),
-    // and only when there can be a prefix: with max_pages = 0 prefix_lens may
-    // be null and every prefix is empty, so index order is already the rank.
     const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv);
-    if (a.max_pages > 0 && nb > 1 && nb <= 64) {
-      if (tid < nb) {
-        const int pt = a.prefix_lens[tid];
-        int rank = 0;
-        for (int u = 0; u < nb; ++u) {
-          const int pu = a.prefix_lens[u];
-          rank += (pu > pt) || (pu == pt && u < tid);
+    if (nb <= 64) {
+      int L = blockIdx.x;
+      gg = L % hgroups;
+      L /= hgroups;
+      hk = L % a.H_kv;
+      const int u = L / a.H_kv;  // rank of the unit
+      if (wave == 0) {
+        // Lane t: sequence t's first row, new tokens and prefix length (an
+        // invalid row range counts as no rows), and its query tiles and
+        // prefix in query-tile lengths.
+        int r0 = 0, len = 0, pre = 0;
+        if (lane < nb) {
+          r0 = a.qo_start[lane];
+          const int r1 = a.qo_start[lane + 1];
+          if (r0 >= 0 && r1 >= r0 && r1 <= a.total_tokens) {
+            len = min(r1 - r0, a.Sq);
+            pre = a.max_pages > 0 ? max(0, min(a.prefix_lens[lane], a.max_pages * kDecodePageSize))
+                                  : 0;
+          }
         }
-        if (rank == b) ext_seq = tid;
+        const int nt = (len + RPW - 1) / RPW, npre = (pre + RPW - 1) / RPW;
+        // Units of sequence t are worth npre + 1 .. npre + nt; at least c:
+        auto count = [&](int c) __attribute__((always_inline)) {
+          return wave_sum_i32(max(0, min(nt, npre + nt - c + 1)));
+        };
+        int sel_b = -1, sel_mt = 0, sel_r0 = 0, sel_len = 0, sel_pre = 0;
+        if (u < wave_sum_i32(nt)) {
+          int lo = 1, hi = wave_max_i32(npre + nt) + 1;  // count(lo) > u >= count(hi)
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (count(mid) > u) lo = mid;
+            else hi = mid;
+          }
+          const int j = u - count(lo + 1);  // among the sequences with a unit worth lo
+          const bool has = nt > 0 && npre < lo && lo <= npre + nt;
+          const uint64_t m = __builtin_amdgcn_read_exec() & __ballot(has);
+          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          const uint64_t pick = __ballot(has && below == j);
+          if (pick != 0) {
+            sel_b = __builtin_ctzll(pick);
+            sel_mt = lo - __builtin_amdgcn_readlane(npre, sel_b) - 1;
+            sel_r0 = __builtin_amdgcn_readlane(r0, sel_b);
+            sel_len = __builtin_amdgcn_readlane(len, sel_b);
+            sel_pre = __builtin_amdgcn_readlane(pre, sel_b);
+          }
+        }
+        if (lane == 0) {
+          ext_unit[0] = sel_b;
+          ext_unit[1] = sel_mt;
+          ext_unit[2] = sel_r0;
+          ext_unit[3] = sel_len;
+          ext_unit[4] = sel_pre;
+        }
       }
       __syncthreads();
-      b = ext_seq;
+      b = __builtin_amdgcn_readfirstlane(ext_unit[0]);
+      const int mt = __builtin_amdgcn_readfirstlane(ext_unit[1]);
+      if (b < 0 || b >= nb || mt < 0 || mt >= a.n_mtiles) return;  // no rows (workgroup-uniform)
+      item = a.n_mtiles - 1 - mt;  // the part loop takes query tile n_mtiles - 1 - item
+      e_r0 = __builtin_amdgcn_readfirstlane(ext_unit[2]);
+      e_len = __builtin_amdgcn_readfirstlane(ext_unit[3]);
+      e_pre = __builtin_amdgcn_readfirstlane(ext_unit[4]);
+      e_known = true;
+    } else {
+      int L = xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * hgroups),
+                             a.n_mtiles * hgroups);
+      gg = L % hgroups;
+      L /= hgroups;
+      item = L % n_items;
+      L /= n_items;
+      hk = L % a.H_kv;
+      b = L / a.H_kv;
     }
+  } else {
+    int L = xcd_remap(blockIdx.x, a.total_tiles);
+    gg = L % hgroups;
+    L /= hgroups;
+    item = L % n_items;
+    L /= n_items;
+    hk = L % a.H_kv;
+    b = L / a.H_kv;
   }
   const int h = hk * a.group + gg * HPW + wave / WPH;  // wave-uniform
   const int n_parts = (PAIRS && a.n_mtiles - 1 - item != item) ? 2 : 1;
@@ -173,10 +244,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     int64_t q_base = b * a.q_sb + h * a.q_sh;   // o shares q's element strides
     int64_t kv_base = b * a.k_sb + hk * a.k_sh;
     if constexpr (EXT) {
-      const int r0 = a.qo_start[b], r1 = a.qo_start[b + 1];
-      if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // invalid range: not computed
-      Sq = min(r1 - r0, a.Sq);                                // a.Sq = max_extend_len
-      P = a.max_pages > 0 ? max(0, min(a.prefix_lens[b], a.max_pages * kDecodePageSize)) : 0;
+      int r0 = e_r0;
+      if (e_known) {
+        Sq = e_len;
+        P = e_pre;
+      } else {
+        r0 = a.qo_start[b];
+        const int r1 = a.qo_start[b + 1];
+        if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // invalid range: not computed
+        Sq = min(r1 - r0, a.Sq);                                // a.Sq = max_extend_len
+        P = a.max_pages > 0 ? max(0, min(a.prefix_lens[b], a.max_pages * kDecodePageSize)) : 0;
+      }
       Skv = P + Sq;
       coff = P;
       n_pre = (P + BN - 1) / BN;

@@ -190,10 +190,11 @@ def _permuted(batch, perm):
 
 @pytest.mark.parametrize("H,H_kv", [(32, 8), (8, 8)])
 def test_extend_sequence_order_independent_bitwise(gpu_lib, H, H_kv):
-    """Work is taken longest prefix first (ties by batch index) for batches of
-    up to 64 sequences: any batch order, with tied, empty and long prefixes
-    and sequences without new tokens, gives each sequence bitwise the same
-    rows, and those rows match the oracle."""
+    """Batches of up to 64 sequences are taken longest work unit first across
+    the batch (a unit is a sequence's query tile, worth its prefix plus causal
+    keys; ties by batch index): any batch order, with tied, empty and long
+    prefixes and sequences without new tokens, gives each sequence bitwise the
+    same rows, and those rows match the oracle."""
     pl = [700, 0, 700, 65, 3000, 700, 1, 0, 1500, 64, 700, 2999]
     el = [40, 300, 0, 129, 64, 1, 256, 17, 90, 200, 33, 5]
     batch = workloads.extend_inputs(len(pl), H, 128, pl, el, "bf16", seed=95 + H, h_kv=H_kv)
@@ -227,8 +228,8 @@ def test_extend_no_cache_null_pointers_equals_causal_prefill_bitwise(gpu_lib, B)
     """max_pages_per_seq = 0 with k_cache, v_cache, page_table and prefix_lens
     all NULL (the header allows it when there is no prefix): every sequence's
     rows are bitwise those of causal prefill over its new tokens.  B = 2 and
-    B = 64 are batch sizes for which the kernel would rank sequences by prefix
-    length if a prefix could exist."""
+    B = 64 take the longest-first work order, which then reads no prefix
+    length."""
     attn = gpu_lib
     rng = np.random.default_rng(97 + B)
     el = [300, 77] if B == 2 else rng.integers(0, 90, B).tolist()
@@ -253,3 +254,38 @@ def test_extend_no_cache_null_pointers_equals_causal_prefill_bitwise(gpu_lib, B)
                            v[None, s[b]:s[b + 1]].contiguous(), causal=True, layout="BSHD")
         torch.cuda.synchronize()
         assert torch.equal(o[s[b]:s[b + 1]], ref[0].cpu()), f"sequence {b}"
+
+
+@pytest.mark.parametrize("B", [6, 70])
+@pytest.mark.parametrize("bad", ["past_end", "negative"])
+def test_extend_invalid_row_range_skipped(gpu_lib, B, bad):
+    """A sequence whose row range is invalid (it ends past total_tokens, or a
+    start is negative) is not computed: its rows keep the caller's values,
+    and every other sequence is still right (B = 6 takes the longest-first
+    order, B = 70 the plain one)."""
+    rng = np.random.default_rng(98 + B)
+    pl = rng.integers(0, 300, B).tolist()
+    el = rng.integers(1, 90, B).tolist()
+    batch = workloads.extend_inputs(B, 8, 128, pl, el, "bf16", seed=98 + B, h_kv=2)
+    g = _gpu(batch)
+    T = batch.q.shape[0]
+    starts = batch.qo_start.clone()
+    if bad == "past_end":
+        starts[B] = T + 3
+        skipped = [B - 1]
+    else:
+        starts[2] = -1
+        skipped = [1, 2]
+    out = torch.full(batch.q.shape, 7.0, dtype=batch.q.dtype, device="cuda")
+    print(f"[case] extend B{B} invalid range {bad}", flush=True)
+    gpu_lib.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                   g["prefix_lens"], starts.cuda(), max_extend_len=max(el), out=out)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    s = batch.qo_start.tolist()
+    for b in skipped:
+        assert torch.all(o[s[b]:s[b + 1]] == 7.0), f"sequence {b} (invalid range) was written"
+    seqs = [b for b in range(B) if b not in skipped]
+    ref = _ref(batch, seqs=seqs)
+    rows = [r for b in seqs for r in range(s[b], s[b + 1])]
+    assert_parity(o[rows].double().numpy(), ref[rows], f"extend B{B} around an invalid range")
