@@ -189,13 +189,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BackwardArgs a) {
     g_off[i] = (row * a.q_ss + ((pos ^ swz<D>(row)) * 8)) * 2;
   }
   const uint32_t row_bytes = (uint32_t)a.q_ss * 2u;
-  // A step's position: query head h (of the group), query tile t.  Steps go
-  // through the tiles of one head, then the next head.
+  // A step's position: query head h (of the group), query tile t.  One query
+  // head per KV head: the tiles in order.  Several (grouped heads): the
+  // tiles from the last down with the group's heads innermost, so all the
+  // resident workgroups of a KV head read the same Q/dO tile at about the
+  // same time (causal: they all start at the last tile, whatever their first
+  // one) and the group's larger Q/dO stream comes from HBM about once per
+  // XCD.  In order, each head a workgroup finishes puts it further out of
+  // step with the others and their shared tiles drop out of L2 in between.
   struct Pos {
     int h, t;
   };
   const int qt_end = qt0 + n_qt;
+  const int h_first = hk * a.group, h_end = h_first + a.group;
+  const bool grouped = a.group > 1;  // uniform
   auto advance = [&](Pos p) __attribute__((always_inline)) {
+    if (grouped) return p.h + 1 < h_end ? Pos{p.h + 1, p.t} : Pos{h_first, p.t - 1};
     return p.t + 1 < qt_end ? Pos{p.h, p.t + 1} : Pos{p.h + 1, qt0};
   };
   auto issue = [&](Pos p, LDS_AS uint16_t* qd, LDS_AS uint16_t* dd, LDS_AS float* rd) __attribute__((always_inline)) {
@@ -372,7 +381,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BackwardArgs a) {
   // copy of the loop (same trip count, same barriers), so the registers of
   // one role's work are not held across the other's.
   auto run = [&](auto role_c) __attribute__((always_inline)) {
-    Pos cur{hk * a.group, qt0};
+    Pos cur{h_first, grouped ? qt_end - 1 : qt0};
     Pos nxt = advance(cur);
     if (steps > 0) issue(cur, Qs[0], Ds[0], Rs[0]);
     auto iteration = [&](int u, auto par) __attribute__((always_inline)) {
