@@ -104,6 +104,24 @@ def _draw(shape, g, amp, dtype):
     return x.to(DTYPES[dtype])
 
 
+def device_normal(shape, dtype="f16", seed=0, device="cuda", amp=1.0, chunk=1 << 28):
+    """Seeded N(0,1) * amp rounded (RNE) to ``dtype``, drawn on ``device`` by a
+    device generator seeded with ``seed``: for tensors of billions of
+    elements, too large to draw on the host and copy.  float32 draws in chunks
+    of ``chunk`` elements, in memory order."""
+    out = torch.empty(shape, dtype=DTYPES[dtype], device=device)
+    g = torch.Generator(device=device).manual_seed(seed)
+    flat = out.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        x = torch.randn(n, generator=g, dtype=torch.float32, device=device)
+        if amp != 1.0:
+            x.mul_(amp)
+        flat[i:i + n].copy_(x)
+        del x
+    return out
+
+
 def prefill_inputs(B, H, Sq, Skv, D, dtype="f16", layout="BHSD", amp=1.0, seed=0, h_kv=None):
     """Seeded q, k, v (CPU tensors in ``layout``), drawn q then k then v.
     k and v have ``h_kv`` heads (default H)."""
