@@ -15,6 +15,7 @@ struct PrefillArgs {
   int H, Sq, Skv;       // H query heads
   int H_kv, group;     // KV heads and query heads per KV head (H = H_kv * group)
   int n_mtiles;        // ceil(Sq / BM), set by launch_prefill
+  int pair_tiles;      // causal: one workgroup per pair of query tiles, set by launch_prefill
   int total_tiles;     // grid size (work items), set by launch_prefill
   int64_t q_sb, q_sh;  // element strides of q and o between batches / heads
   int q_ss;            // element stride between query rows
@@ -80,6 +81,7 @@ hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, i
 // split, chunk of up to 32 query heads of the group).
 constexpr int kDecodeHeadsPerWG = 4;
 constexpr int kDecodePageSize = 16;
+constexpr int kNumCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
 // Grouped-query decode: the batch's KV tiles are cut into at most this many
 // equal ranges (half as many for groups of 16 or more query heads), one wave
 // each -- the waves one launch keeps resident on 256 CUs at eight per CU, so

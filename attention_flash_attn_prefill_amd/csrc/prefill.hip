@@ -116,11 +116,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // query tile at the same time on one XCD and read the same K/V tiles
   // through its L2 (group = 1 is plain (b, h, item) order).
   //
-  // Causal prefill pairs the query tiles of a head: item p runs query tile
-  // n - 1 - p (the heaviest left) and then tile p (the lightest), so every
-  // workgroup walks about n + 1 tiles' worth of keys and the grid has no
-  // tail of short workgroups (n = n_mtiles; the middle tile of an odd n runs
-  // alone).  Other work has one query tile per item.
+  // Causal prefill over a large grid pairs the query tiles of a head: item p
+  // runs query tile n - 1 - p (the heaviest left) and then tile p (the
+  // lightest), so every workgroup walks about n + 1 tiles' worth of keys and
+  // the grid has no tail of short workgroups (n = n_mtiles; the middle tile of
+  // an odd n runs alone).  The launcher pairs only when the unpaired grid
+  // fills the CUs at least twice (a.pair_tiles); a smaller grid would be left
+  // with idle CUs.  Other work has one query tile per item, heaviest first.
   //
   // Extend batches are ragged.  With at most 64 sequences the work goes out
   // longest first over the whole batch: a unit is (sequence b, query tile
@@ -136,9 +138,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // with a unit worth exactly c.  Units past the last non-empty one have no
   // rows.  Larger batches go in (sequence, KV head) blocks interleaved over
   // the XCDs, heaviest query tile first within a block.
-  constexpr bool PAIRS = CAUSAL && !EXT;
+  const bool pairs = CAUSAL && !EXT && a.pair_tiles;  // uniform
   const int hgroups = a.group / HPW;
-  const int n_items = PAIRS ? (a.n_mtiles + 1) >> 1 : a.n_mtiles;
+  const int n_items = pairs ? (a.n_mtiles + 1) >> 1 : a.n_mtiles;
   int gg, item, hk, b;
   int e_r0 = 0, e_len = 0, e_pre = 0;  // sequence b's first row, new tokens, prefix
   bool e_known = false;                // whether those three are set (workgroup-uniform)
@@ -228,11 +230,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     b = L / a.H_kv;
   }
   const int h = hk * a.group + gg * HPW + wave / WPH;  // wave-uniform
-  const int n_parts = (PAIRS && a.n_mtiles - 1 - item != item) ? 2 : 1;
+  const int n_parts = (pairs && a.n_mtiles - 1 - item != item) ? 2 : 1;
 
   for (int part = 0; part < n_parts; ++part) {
     // Query tile of this part: extend in order; causal heaviest first.
-    const int mt = !CAUSAL ? item : (PAIRS && part == 1 ? item : a.n_mtiles - 1 - item);
+    const int mt = !CAUSAL ? item : (pairs && part == 1 ? item : a.n_mtiles - 1 - item);
     // The second part refills the LDS stages: every wave must be done with
     // the first part's last tile.
     if (part > 0) __syncthreads();
@@ -713,8 +715,11 @@ template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = f
 hipError_t launch_t(PrefillArgs a, int B, hipStream_t s) {
   constexpr int RPW = 32 * NW / HPW;  // query rows per head in a workgroup
   const int64_t n_mtiles = (a.Sq + RPW - 1) / RPW;
-  // causal prefill: one workgroup per pair of query tiles (see the kernel)
-  const int64_t n_items = (CAUSAL && !EXT) ? (n_mtiles + 1) / 2 : n_mtiles;
+  // Causal prefill: one workgroup per pair of query tiles (see the kernel)
+  // when the unpaired grid covers the GPU's 256 CUs at least twice.
+  const int64_t unpaired = (int64_t)B * (a.H / HPW) * n_mtiles;
+  a.pair_tiles = (CAUSAL && !EXT && unpaired >= 2 * kNumCUs) ? 1 : 0;
+  const int64_t n_items = a.pair_tiles ? (n_mtiles + 1) / 2 : n_mtiles;
   const int64_t total = (int64_t)B * (a.H / HPW) * n_items;
   if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   a.n_mtiles = (int)n_mtiles;

@@ -250,17 +250,28 @@ def test_prefill_out_f32(gpu_lib, dtype, D, causal):
 @pytest.mark.parametrize("Sq", [1, 63, 64, 65, 255, 256, 257, 511, 767, 1024, 1280])
 @pytest.mark.parametrize("D,H,H_kv", [(128, 2, 2), (64, 2, 2), (128, 8, 2)])
 def test_prefill_causal_tile_pairs(gpu_lib, Sq, D, H, H_kv):
-    """Causal prefill gives each workgroup a pair of query tiles (the
-    heaviest left, then the lightest; the middle one alone when the count is
-    odd): 1 to 10 tiles of 256 (D = 128), 128 (D = 64) or, with four query
-    heads per workgroup, 64 rows, with Skv = Sq + 37 so the diagonal is
-    offset, into a NaN-filled output."""
+    """Causal prefill over a grid that fills the CUs at least twice gives each
+    workgroup a pair of query tiles (the heaviest left, then the lightest; the
+    middle one alone when the count is odd); a smaller grid keeps one tile per
+    workgroup.  1 to 10 tiles of 256 (D = 128), 128 (D = 64) or, with four
+    query heads per workgroup, 64 rows, with Skv = Sq + 37 so the diagonal is
+    offset.  A batch of 256 (paired: at least 512 tiles) into a NaN-filled
+    output; three of its sequences alone (unpaired) must give bitwise the
+    same rows, and those match the oracle."""
     Skv = Sq + 37
-    q, k, v = workloads.prefill_inputs(1, H, Sq, Skv, D, "bf16", "BHSD", seed=Sq + D + H_kv,
-                                       h_kv=H_kv)
-    print(f"[case] causal pairs Sq{Sq} Skv{Skv} D{D} H{H}/{H_kv}", flush=True)
-    qg = q.cuda()
-    o = gpu_lib.prefill(qg, k.cuda(), v.cuda(), causal=True, out=whole.nan_like(qg))
+    Bb = 256
+    seed = Sq + D + H_kv
+    print(f"[case] causal pairs B{Bb} Sq{Sq} Skv{Skv} D{D} H{H}/{H_kv}", flush=True)
+    q = workloads.device_normal((Bb, H, Sq, D), "bf16", seed=3 * seed)
+    k = workloads.device_normal((Bb, H_kv, Skv, D), "bf16", seed=3 * seed + 1)
+    v = workloads.device_normal((Bb, H_kv, Skv, D), "bf16", seed=3 * seed + 2)
+    o = gpu_lib.prefill(q, k, v, causal=True, out=whole.nan_like(q))
     torch.cuda.synchronize()
-    assert_parity(_f64(o.cpu()), oracle.sdpa(q, k, v, causal=True),
-                  f"causal pairs Sq{Sq} D{D} H{H}/{H_kv}")
+    assert bool(torch.isfinite(o).all()), "paired grid left rows unwritten"
+    for b in (0, 137, Bb - 1):
+        qs, ks, vs = q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous()
+        o1 = gpu_lib.prefill(qs, ks, vs, causal=True, out=whole.nan_like(qs))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o[b:b + 1]), f"sequence {b}: paired and unpaired rows differ"
+        assert_parity(_f64(o1.cpu()), oracle.sdpa(qs.cpu(), ks.cpu(), vs.cpu(), causal=True),
+                      f"causal pairs Sq{Sq} D{D} H{H}/{H_kv} sequence {b}")
