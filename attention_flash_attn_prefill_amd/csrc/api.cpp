@@ -392,8 +392,11 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
     if (!aligned16(k_cache) || !aligned16(v_cache)) return ATTN_E_INVALID;
     if (((uintptr_t)page_table & 3u) || ((uintptr_t)prefix_lens & 3u)) return ATTN_E_INVALID;
   }
-  // Row offsets within a sequence's new tokens are 32-bit in the kernel.
+  // Row offsets within a sequence's new tokens are 32-bit in the kernel, and
+  // so are key positions (prefix plus new tokens).
   if ((int64_t)max_extend_len * H * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)max_pages_per_seq * kDecodePageSize + max_extend_len >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;
   if ((int64_t)kDecodePageSize * H_kv * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
   PrefillArgs a;

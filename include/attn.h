@@ -194,6 +194,9 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o,
  * (the new tokens' K/V are not written to the cache here).  max_extend_len
  * >= every E_b bounds the grid: rows of a sequence past max_extend_len are
  * not written.  page_size: 16; D: 64 or 128.  Arithmetic as attn_prefill.
+ * Key positions are 32-bit: max_pages_per_seq * 16 + max_extend_len must be
+ * below 2^31, and max_extend_len * H * D * 2 (a sequence's rows of q in
+ * bytes) too (else ATTN_E_UNSUPPORTED).
  *
  * Device data (read only on the device): prefix_lens[b] is clamped to
  * [0, max_pages_per_seq * 16]; a sequence whose qo_start range is not within

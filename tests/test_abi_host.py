@@ -321,6 +321,9 @@ def _extend(**kw):
     (dict(num_pages=0), attn.ATTN_E_INVALID),
     (dict(q=FAKE + 8), attn.ATTN_E_INVALID),
     (dict(max_extend_len=1 << 20, H=64, H_kv=8), attn.ATTN_E_UNSUPPORTED),
+    # key positions (prefix plus new tokens) must stay below 2^31
+    (dict(max_pages_per_seq=1 << 27), attn.ATTN_E_UNSUPPORTED),
+    (dict(max_pages_per_seq=(1 << 27) - 4, max_extend_len=64), attn.ATTN_E_UNSUPPORTED),
 ])
 def test_extend_validation(kw, status):
     assert _extend(**kw) == status
