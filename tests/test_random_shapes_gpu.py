@@ -1,10 +1,10 @@
 """A seeded sweep of random shapes through prefill (with and without the LSE
-output), grouped-query decode and extend, each against the fp64 oracle at the
-standard bar.  The draws mix batch, head counts and grouping, lengths on and
-off tile boundaries (including Sq > Skv under the bottom-right causal mask),
-head size, dtype, layout and scale, so that combinations the hand-picked
-cases do not name are still exercised.  Sizes stay small enough for the
-oracle to finish in seconds."""
+output), grouped-query decode, extend, the backward and fp8 prefill, each
+against the fp64 oracle at its bar.  The draws mix batch, head counts and
+grouping, lengths on and off tile boundaries (including Sq > Skv under the
+bottom-right causal mask), head size, dtype, layout and scale, so that
+combinations the hand-picked cases do not name are still exercised.  Sizes
+stay small enough for the oracle to finish in seconds."""
 import math
 
 import numpy as np
@@ -102,3 +102,42 @@ def test_extend_random(gpu_lib, i):
     ref = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
                         batch.page_table, batch.prefix_lens, batch.qo_start, scale=scale)
     assert_parity(o.double().cpu().numpy(), ref, f"extend random {i}")
+
+
+# The backward's bar for gradients (relative to max|ref|; derived from a CPU
+# model of the kernels' rounding, see the docstring of test_backward_gpu.py).
+BWD_TOL = {"f16": (2e-3, 1e-3), "bf16": (1e-2, 6e-3)}
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_backward_random(gpu_lib, i):
+    c = _draw_prefill(100 + i)
+    c["Sq"], c["Skv"] = min(c["Sq"], 400), min(c["Skv"], 400)
+    print(f"[case] backward random {i}: {c}", flush=True)
+    q, k, v, do = workloads.backward_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                            c["layout"], amp=0.5, seed=7000 + i, h_kv=c["H_kv"])
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    kw = dict(causal=c["causal"], scale=c["scale"], layout=c["layout"])
+    o, lse = gpu_lib.prefill_with_lse(qg, kg, vg, **kw)
+    grads = gpu_lib.prefill_backward(qg, kg, vg, o, dog, lse, **kw)
+    torch.cuda.synchronize()
+    refs = oracle.sdpa_backward(q, k, v, do, **kw)
+    ma, rf = BWD_TOL[c["dtype"]]
+    for name, g, ref in zip(("dq", "dk", "dv"), grads, refs):
+        big = max(float(np.abs(ref).max()) if ref.size else 0.0, 1e-3)
+        assert_parity(g.double().cpu().numpy(), ref, f"backward random {i} {name}",
+                      max_abs_tol=ma * big, rel_fro_tol=rf)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_prefill_fp8_random(gpu_lib, i):
+    c = _draw_prefill(200 + i)
+    print(f"[case] fp8 prefill random {i}: {c}", flush=True)
+    q8, k8, v8, sc = workloads.prefill_inputs_fp8(c["B"], c["H"], c["Sq"], c["Skv"], c["D"],
+                                                  c["layout"], seed=8000 + i, h_kv=c["H_kv"])
+    o = gpu_lib.prefill_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sc, causal=c["causal"],
+                            scale=c["scale"], layout=c["layout"])
+    torch.cuda.synchronize()
+    deq = [torch.from_numpy(oracle.dequantize_fp8(t, d)) for t, d in zip((q8, k8, v8), sc)]
+    ref = oracle.sdpa(*deq, causal=c["causal"], scale=c["scale"], layout=c["layout"])
+    assert_parity(o.double().cpu().numpy(), ref, f"fp8 prefill random {i}")
