@@ -39,7 +39,7 @@ extern "C" {
 enum {
   ATTN_OK = 0,
   ATTN_E_INVALID = 1,      /* null pointer, negative size, bad scale, misaligned pointer */
-  ATTN_E_UNSUPPORTED = 2,  /* valid request this build does not implement (head dim, page size) */
+  ATTN_E_UNSUPPORTED = 2,  /* valid request the library does not implement (head dim, page size) */
   ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than the entry point's *_workspace_size */
   ATTN_E_HIP = 4           /* the HIP runtime reported an error at launch */
 };

@@ -17,7 +17,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library, loaded for GPU tests.  Fails (not skips) if it is missing on a GPU machine."""
+    """The HIP library, loaded for GPU tests.  Fails (not skips) if it is missing where a GPU is present."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")

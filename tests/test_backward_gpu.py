@@ -156,7 +156,7 @@ def test_backward_writes_every_row(gpu_lib):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [11, 12])
-def test_backward_full_config_whole(gpu_lib, cfg, progress):
+def test_backward_full_size_whole(gpu_lib, cfg, progress):
     """The 8k causal BSHD backward at full size (32 query heads; and with
     four query heads per KV head), in the bench's launch configuration:
     gradients written into NaN-prefilled buffers and compared with the

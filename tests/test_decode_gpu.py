@@ -98,7 +98,7 @@ def test_decode_scale(gpu_lib):
                       _ref(batch, scale=scale), f"scale {scale}")
 
 
-def test_decode_full_config4(gpu_lib):
+def test_decode_paged_b64_full_size(gpu_lib):
     """Every (sequence, head) of the paged-decode workload, written into a
     NaN-prefilled output."""
     batch = workloads.decode_config(4)

@@ -160,7 +160,7 @@ def test_extend_rows_past_max_extend_len_untouched(gpu_lib):
 
 
 @pytest.mark.timeout(600)
-def test_extend_full_config9_whole(gpu_lib, progress):
+def test_extend_gqa_b8_whole(gpu_lib, progress):
     """The ragged extend batch at full size: NaN-prefilled output, every
     sequence's rows against the oracle."""
     batch = workloads.extend_config(9)

@@ -62,7 +62,7 @@ def test_prefill_fp8_exact_identities(gpu_lib):
 
 
 @pytest.mark.timeout(900)
-def test_prefill_fp8_full_config10_whole(gpu_lib, progress):
+def test_prefill_fp8_llama2_13b_whole(gpu_lib, progress):
     """fp8 prefill of the Llama-2-13B shape at full size: NaN-prefilled
     output, the whole tensor against the oracle on the dequantised inputs."""
     q8, k8, v8, m = workloads.prefill_config(10)

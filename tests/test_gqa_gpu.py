@@ -51,7 +51,7 @@ def test_prefill_gqa_equals_repeated_kv_bitwise(gpu_lib):
 
 
 @pytest.mark.timeout(900)
-def test_prefill_gqa_full_config6_whole(gpu_lib, progress):
+def test_prefill_gqa_causal_bshd_8k_whole(gpu_lib, progress):
     """The grouped-query causal 8k workload at full size, NaN-prefilled
     output, compared with the oracle over the whole tensor."""
     q, k, v, m = workloads.prefill_config(6)
@@ -141,7 +141,7 @@ def test_decode_gqa_bad_page_ids(gpu_lib):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg", [7, 8])
-def test_decode_gqa_full_config_whole(gpu_lib, cfg, progress):
+def test_decode_gqa_full_size_whole(gpu_lib, cfg, progress):
     """Grouped- and multi-query decode workloads at full size: NaN-prefilled
     output, every (sequence, head) compared with the oracle."""
     batch = workloads.decode_config(cfg)

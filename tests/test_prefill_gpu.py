@@ -58,7 +58,7 @@ def test_prefill_odd_shapes(gpu_lib, shape, D, dtype, layout, causal):
     assert_parity(_f64(o), ref, f"{shape} D{D} {dtype} {layout} causal={causal}")
 
 
-def test_prefill_config1_full(gpu_lib):
+def test_prefill_tiny_mha_d64_full(gpu_lib):
     q, k, v, m = workloads.prefill_config(1)
     o = _run(gpu_lib, q, k, v, m["causal"], m["scale"], m["layout"])
     ref = oracle.sdpa(q, k, v, causal=m["causal"], scale=m["scale"], layout=m["layout"])
@@ -139,7 +139,7 @@ F32_MAX_ABS_FULL, F32_REL_FRO_FULL = 3e-3, 5e-4
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_prefill_full_config_whole(gpu_lib, cfg, progress):
+def test_prefill_full_size_whole(gpu_lib, cfg, progress):
     attn = gpu_lib
     q, k, v, m = workloads.prefill_config(cfg)
     print(f"[case] prefill {m['name']} whole tensor", flush=True)
