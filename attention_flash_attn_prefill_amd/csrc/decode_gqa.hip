@@ -179,11 +179,23 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
   LDS_AS uint16_t* const Ks = (LDS_AS uint16_t*)k_lds;
   LDS_AS uint16_t* const Vs = (LDS_AS uint16_t*)v_lds;
 
+  // The lengths and the page table do not change while the kernel runs.
+  // Where a wave reads one of their entries at a wave-uniform index at the
+  // start of a segment, it reads through the constant address space, so the
+  // read is a scalar load: a vector load there would wait (the vector memory
+  // counter being shared) for the previous segment's partial stores.  The
+  // per-tile page ids stay vector loads (as scalar loads they made batches of
+  // 32+ tiles per range 1-2% slower).
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  auto seq_tiles_u = [&](int b) {
+    return (max(0, min(((ConstI32)a.seq_lens)[b], cap)) + T - 1) / T;
+  };
+
   // ---- one segment: tiles [tile0, tile1) of line (b, hk, qc), written to
   // partial slot `slot` (one row per query of the chunk).
   auto segment = [&](int b, int hk, int qc, int tile0, int tile1, int slot)
                      __attribute__((always_inline)) {
-    const int n = max(0, min(a.seq_lens[b], cap));
+    const int n = max(0, min(((ConstI32)a.seq_lens)[b], cap));
     const int t_begin = tile0 * T;
     const int t_end = min(n, tile1 * T);
     const int n_tiles = tile1 - tile0;
@@ -204,6 +216,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
     // r / 16, slot r % 16), position P % CPR, holding logical chunk
     // position ^ swz(r).
     const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+    const ConstI32 ptab_s = (ConstI32)a.page_table + (int64_t)b * a.max_pages;
     const int64_t page_elems = (int64_t)PS * a.H_kv * D;
     const uint32_t row_bytes = (uint32_t)a.H_kv * D * 2u;
     int g_off[LOADS];
@@ -222,13 +235,14 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
 
     u32x4 vreg[LOADS], kreg[LOADS];  // the next tile, in flight
     bool bad_page = false;  // wave-uniform
-    // Issue the loads of the tile starting at token tb; false (and nothing
-    // issued) if a page id lies outside the pool.
-    auto issue = [&](int tb) {
+    // Issue the loads of the tile starting at token tb (the segment's first
+    // tile: its page ids by scalar loads); false (and nothing issued) if a
+    // page id lies outside the pool.
+    auto issue = [&](int tb, bool first) {
       const int live0 = min(PS, t_end - tb);
       const int live1 = max(0, min(PS, t_end - tb - PS));
-      const int pg0 = ptab[tb / PS];
-      const int pg1 = live1 > 0 ? ptab[tb / PS + 1] : pg0;
+      const int pg0 = first ? ptab_s[tb / PS] : ptab[tb / PS];
+      const int pg1 = live1 > 0 ? (first ? ptab_s[tb / PS + 1] : ptab[tb / PS + 1]) : pg0;
       if ((uint32_t)pg0 >= (uint32_t)a.num_pages || (uint32_t)pg1 >= (uint32_t)a.num_pages)
         return false;
       const auto k0 = page_rsrc(a.k_cache, pg0, live0), k1 = page_rsrc(a.k_cache, pg1, live1);
@@ -336,11 +350,11 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
     // One tile per step: tile t goes registers -> LDS (the LDS writes follow
     // the previous tile's LDS reads in the wave's own order), tile t+1's loads
     // are issued, tile t is computed from LDS.
-    if (!issue(t_begin)) bad_page = true;
+    if (!issue(t_begin, true)) bad_page = true;
     for (int t = 0; t < n_tiles && !bad_page; ++t) {
       const int tb = t_begin + t * T;
       store_kv(Ks, Vs);
-      if (t + 1 < n_tiles && !issue(tb + T)) {
+      if (t + 1 < n_tiles && !issue(tb + T, false)) {
         bad_page = true;
         break;
       }
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
   };
 
   // ---- walk the range: a segment per line it touches.
-  int b = b0, pb = p0, ntb = seq_tiles(b0);  // ntb > 0: b0 holds tile s0
+  int b = b0, pb = p0, ntb = seq_tiles_u(b0);  // ntb > 0: b0 holds tile s0
   for (int s = s0; s < s1;) {
     const int o = s - pb;
     const int j = o / ntb;  // line of sequence b
@@ -384,7 +398,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_split_kernel(DecodeArgs a) {
       pb += ntb * lines;
       do {
         ++b;
-        ntb = seq_tiles(b);
+        ntb = seq_tiles_u(b);
       } while (ntb == 0);
     }
   }
