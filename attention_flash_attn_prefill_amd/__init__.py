@@ -156,10 +156,9 @@ def attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_
 
 
 def attn_paged_decode_gqa_num_splits(B, H, H_kv, max_pages_per_seq, page_size):
-    """Work plan of grouped-query decode.  H_kv == H: (n_splits,
-    tokens_per_split) of the multi-head split plan.  H_kv < H: (the largest
-    number of equal work ranges a call cuts the batch's KV tiles into, the
-    fewest tokens a range covers unless the batch holds fewer)."""
+    """Work plan of paged decode: (the largest number of equal work ranges a
+    call cuts the batch's KV tiles into, the fewest tokens a range covers
+    unless the batch holds fewer)."""
     tps = ctypes.c_int(0)
     n = load_library().attn_paged_decode_gqa_num_splits(B, H, H_kv, max_pages_per_seq,
                                                         page_size, ctypes.byref(tps))
@@ -211,7 +210,7 @@ def attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size) -> i
 
 
 def attn_paged_decode_num_splits(B, H, max_pages_per_seq, page_size):
-    """(n_splits, tokens_per_split) of the decode split plan."""
+    """attn_paged_decode_gqa_num_splits with H_kv = H."""
     tps = ctypes.c_int(0)
     n = load_library().attn_paged_decode_num_splits(B, H, max_pages_per_seq, page_size,
                                                     ctypes.byref(tps))

@@ -22,8 +22,7 @@ LIB_NAME = "libmi355attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "decode_gqa.hip", "backward.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode_gqa.hip", "backward.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

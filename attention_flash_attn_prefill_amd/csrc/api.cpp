@@ -37,66 +37,33 @@ float exp2_multiplier(float scale) {
   return c > 0.f ? c : 1.17549435e-38f;
 }
 
-struct SplitPlan {
-  int n_splits;
-  int tokens_per_split;
-};
-
-// Tokens per split: a multiple of four pages (64 tokens), 512 by default,
-// halved while the grid holds fewer than 8192 work items (workgroups), so
-// short batches still fill 256 CUs.  Partial results cost one D+1 fp32 row
-// per split and query head: about 0.5% of the KV bytes at 512 tokens.  The
-// plan depends only on host-side sizes (never on seq_lens).
-//
-// Work items per split (group = 1, decode.hip): B x ceil(H / 4) workgroups
-// of four waves.  Grouped heads (decode_gqa.hip) use plan_gqa below instead.
-SplitPlan plan_splits(int B, int H, int H_kv, int max_pages, int page_size) {
-  SplitPlan p{0, 0};
-  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || max_pages <= 0 ||
-      page_size != kDecodePageSize)
-    return p;
-  const int group = H / H_kv;
-  const int64_t items = group == 1
-      ? (int64_t)B * ((H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG)
-      : (int64_t)B * H_kv * ((group + 31) / 32);
-  const int64_t max_tokens = (int64_t)max_pages * page_size;
-  int tps = 512;
-  auto splits = [&](int t) { return (max_tokens + t - 1) / t; };
-  // Grouped heads write one partial row per query head and split: keep the
-  // split at least 16 tokens per query head of the group (partials <= ~6%).
-  int floor_tps = 4 * kDecodePageSize;
-  while (group > 1 && floor_tps < 512 && floor_tps < 16 * group) floor_tps *= 2;
-  while (tps > floor_tps && items * splits(tps) < 8192) tps /= 2;
-  while (splits(tps) > 4096) tps *= 2;
-  p.tokens_per_split = tps;
-  p.n_splits = (int)splits(tps);
-  return p;
-}
-
-// Grouped-query plan (group > 1, decode_gqa.hip): lines = B x H_kv x
-// ceil(group / 32), each holding its sequence's 32-token tiles; the tiles of
-// all lines are cut into W equal ranges on the device, W = min(ranges,
-// ceil(NT / min_tiles)) for the batch's actual tile count NT.  A range writes
-// one partial row per query of the chunk for every line it touches, which the
-// combine reads back, so it covers at least min(group, 32) / 2 tiles, at most
-// 8 (more ranges keep small batches' loads in flight).  Groups of 16 or more
-// query heads take at most half the ranges (4 resident waves per CU instead
-// of 8): their partials are 16-32 rows per range, and halving the ranges ran
-// 7-9% faster at group sizes 16 and 32 on batches of 64-256 sequences of up
-// to 8k tokens, no faster at 4 and 8.  Slots = ranges + lines bound the
-// (range, line) pairs.
+// Paged decode plan (decode_gqa.hip), for every group size g = H / H_kv:
+// lines = B x H_kv x ceil(g / 32), each holding its sequence's 32-token tiles;
+// the tiles of all lines are cut into W equal ranges on the device, W =
+// min(ranges, ceil(NT / min_tiles)) for the batch's actual tile count NT.  A
+// range writes one partial row per query of the chunk for every line it
+// touches, which the combine reads back, so it covers at least min(g, 32) / 2
+// tiles, at most 8 and at least 4: shorter ranges made batches of 1-8
+// sequences up to 20% slower (each range also pays a start: the range
+// search, then its first tile's latency), longer ones keep fewer loads in
+// flight.  Groups of 16 or more query heads take at most half the ranges (4
+// resident waves per CU instead of 8): their partials are 16-32 rows per
+// range, and halving the ranges ran 7-9% faster at group sizes 16 and 32 on
+// batches of 64-256 sequences of up to 8k tokens, no faster at 4 and 8.
+// Slots = ranges + lines bound the (range, line) pairs.  The plan depends only
+// on host-side sizes; the ranges follow the actual lengths on the device.
 struct GqaPlan {
   int ranges, min_tiles, rows_per_slot;
   int64_t lines, slots;
 };
 GqaPlan plan_gqa(int B, int H, int H_kv, int max_pages, int page_size) {
   GqaPlan p{0, 0, 0, 0, 0};
-  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || H == H_kv || max_pages <= 0 ||
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || max_pages <= 0 ||
       page_size != kDecodePageSize)
     return p;
   const int group = H / H_kv;
   p.rows_per_slot = group < 32 ? group : 32;
-  p.min_tiles = p.rows_per_slot / 2 < 8 ? (p.rows_per_slot > 1 ? p.rows_per_slot / 2 : 1) : 8;
+  p.min_tiles = p.rows_per_slot / 2 < 4 ? 4 : (p.rows_per_slot / 2 > 8 ? 8 : p.rows_per_slot / 2);
   p.lines = (int64_t)B * H_kv * ((group + 31) / 32);
   const int64_t max_tiles = ((int64_t)max_pages * page_size + 31) / 32;
   const int64_t nt_max = p.lines * max_tiles;
@@ -135,18 +102,13 @@ int check_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   if ((int64_t)max_pages_per_seq * page_size >= ((int64_t)1 << 31))
     return ATTN_E_UNSUPPORTED;  // token positions are 32-bit
   if (num_pages == 0 || max_pages_per_seq == 0) return ATTN_E_INVALID;  // seq_len >= 1 needs a page
-  const int group = H / H_kv;
-  if (group == 1 && B > 65535) return ATTN_E_UNSUPPORTED;  // grid limit
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o) return ATTN_E_INVALID;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return ATTN_E_INVALID;
   if (((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_E_INVALID;
 
-  const SplitPlan p = group == 1 ? plan_splits(B, H, H_kv, max_pages_per_seq, page_size)
-                                 : SplitPlan{0, 0};
-  const GqaPlan g = group == 1 ? GqaPlan{} : plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
-  if (group == 1 ? (p.n_splits == 0 || p.n_splits > 65535) : g.ranges == 0)
-    return ATTN_E_UNSUPPORTED;  // grid or index limits
+  if (plan_gqa(B, H, H_kv, max_pages_per_seq, page_size).ranges == 0)
+    return ATTN_E_UNSUPPORTED;  // index limits
   *need = attn_paged_decode_gqa_workspace_size(B, H, H_kv, D, max_pages_per_seq, page_size);
   return *need > 0 ? ATTN_OK : ATTN_E_UNSUPPORTED;
 }
@@ -431,14 +393,9 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
 
 int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
                                      int page_size, int* tokens_per_split) {
-  if (H_kv > 0 && H > H_kv) {
-    const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
-    if (tokens_per_split) *tokens_per_split = g.min_tiles * 32;
-    return g.ranges;
-  }
-  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
-  if (tokens_per_split) *tokens_per_split = p.tokens_per_split;
-  return p.n_splits;
+  const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+  if (tokens_per_split) *tokens_per_split = g.ranges > 0 ? g.min_tiles * 32 : 0;
+  return g.ranges;
 }
 
 int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
@@ -450,21 +407,13 @@ int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_s
 size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D, int max_pages_per_seq,
                                             int page_size) {
   if (D != 64 && D != 128) return 0;
-  if (H_kv > 0 && H > H_kv) {
-    // partial outputs [slots, rows, D], log-sum-exps [slots, rows], then the
-    // range metadata (B + 3 ints), each 256-B aligned
-    const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
-    if (g.ranges == 0) return 0;
-    const size_t rows = (size_t)g.slots * g.rows_per_slot;
-    return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) +
-           ((size_t)B + 3) * sizeof(int);
-  }
-  const SplitPlan p = plan_splits(B, H, H_kv, max_pages_per_seq, page_size);
-  if (p.n_splits == 0) return 0;
-  const size_t rows = (size_t)B * H * p.n_splits;
-  // partial outputs [B,H,S,D] fp32, then log-sum-exps [B,H,S] fp32, 256-B aligned
-  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
-  return o_bytes + rows * sizeof(float);
+  // partial outputs [slots, rows, D], log-sum-exps [slots, rows], then the
+  // range metadata (B + 3 ints), each 256-B aligned
+  const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+  if (g.ranges == 0) return 0;
+  const size_t rows = (size_t)g.slots * g.rows_per_slot;
+  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) +
+         ((size_t)B + 3) * sizeof(int);
 }
 
 size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
@@ -488,11 +437,9 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
   parse_dtype(dtype, &bf16, &out_f32);
   const int group = H / H_kv;
   const int qchunks = (group + 31) / 32;
-  const SplitPlan p = group == 1 ? plan_splits(B, H, H_kv, max_pages_per_seq, page_size)
-                                 : SplitPlan{0, 0};
-  const GqaPlan g = group == 1 ? GqaPlan{} : plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
+  const GqaPlan g = plan_gqa(B, H, H_kv, max_pages_per_seq, page_size);
 
-  const size_t rows = group == 1 ? (size_t)B * H * p.n_splits : (size_t)g.slots * g.rows_per_slot;
+  const size_t rows = (size_t)g.slots * g.rows_per_slot;
   const size_t o_bytes = align256(rows * D * sizeof(float));
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -511,14 +458,12 @@ int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cach
   a.group = group;
   a.qchunks = qchunks;
   a.max_pages = max_pages_per_seq;
-  a.n_splits = group == 1 ? p.n_splits : g.ranges;
-  a.tokens_per_split = p.tokens_per_split;
+  a.n_splits = g.ranges;
   a.min_tiles = g.min_tiles;
   a.rows_per_slot = g.rows_per_slot;
   a.num_pages = num_pages;
   a.c = exp2_multiplier(scale);
-  hipError_t e = group == 1 ? launch_paged_decode(D, bf16, out_f32, a, stream)
-                            : launch_paged_decode_gqa(D, bf16, out_f32, a, stream);
+  hipError_t e = launch_paged_decode_gqa(D, bf16, out_f32, a, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -1,11 +1,14 @@
-// Grouped-query paged flash decoding for gfx950: the query heads that share a
-// KV head (grouped-query / multi-query attention, H_kv < H) are decoded
-// together, so each K/V row is read from HBM once for the whole group and the
-// group's queries become the N dimension of the matrix-core products.  The
-// flash-decoding structure is the MHA kernel's (split the KV range, one
-// partial output and log-sum-exp per split, merge by log-sum-exp: "Wave
-// February 2025 Release", FlashDecoding list; splits sized to fill the GPU:
-// "[FlyDSL] FP8 MQA logits improvements for gfx950", Changes / Host side).
+// Paged flash decoding for gfx950, one query per sequence, for every group
+// size: the query heads that share a KV head (grouped-query and multi-query
+// attention, H_kv < H; one head per KV head for multi-head attention) are
+// decoded together, so each K/V row is read from HBM once for the whole
+// group, and the group's queries are the N dimension of the matrix-core
+// products (zero-padded to 32: the products are a small share of the time
+// of this memory-bound kernel even for one query head).  Flash decoding:
+// split the KV range, one partial output and log-sum-exp per piece, merge by
+// log-sum-exp ("Wave February 2025 Release", FlashDecoding list; pieces sized
+// to fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950",
+// Changes / Host side).
 //
 // Work: a line is one (sequence, KV head, 32-query chunk of the group) and
 // holds its sequence's 32-token tiles; the batch's tiles, line after line,

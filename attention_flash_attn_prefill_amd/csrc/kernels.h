@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (api.cpp) and the HIP kernel
-// translation units (prefill.hip, decode.hip).  Not installed; not part of the ABI.
+// translation units (prefill.hip, decode_gqa.hip, backward.hip).  Not installed; not
+// part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -75,14 +76,12 @@ hipError_t launch_prefill_backward(int D, bool bf16, bool causal, bool out_f32,
 hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
                          hipStream_t s);
 
-// Paged decode.  H query heads share H_kv KV heads (group = H / H_kv).
-// group = 1: decode.hip, one wave per (sequence, head, split), four heads per
-// workgroup.  group > 1: decode_gqa.hip, one wave per (sequence, KV head,
-// split, chunk of up to 32 query heads of the group).
-constexpr int kDecodeHeadsPerWG = 4;
+// Paged decode (decode_gqa.hip).  H query heads share H_kv KV heads (group =
+// H / H_kv, 1 for multi-head attention): one wave per work range of the
+// batch's (sequence, KV head, chunk of up to 32 query heads) lines.
 constexpr int kDecodePageSize = 16;
 constexpr int kNumCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
-// Grouped-query decode: the batch's KV tiles are cut into at most this many
+// Paged decode: the batch's KV tiles are cut into at most this many
 // equal ranges (half as many for groups of 16 or more query heads), one wave
 // each -- the waves one launch keeps resident on 256 CUs at eight per CU, so
 // all of them start at once.
@@ -95,28 +94,21 @@ struct DecodeArgs {
   const int32_t* page_table;  // [B, max_pages]
   const int32_t* seq_lens;    // [B]
   void* o;                    // [B, H, D], dtype of q or fp32 (out_f32)
-  // Partials (workspace).  group = 1: [B, H, n_splits, D] and [B, H, n_splits]
-  // (log2 domain).  group > 1: [slots, rows_per_slot, D] and [slots,
-  // rows_per_slot], slot = work range + line; meta = {NT, W, first tile of
-  // each sequence (B + 1 entries)}.
+  // Partials (workspace): [slots, rows_per_slot, D] and [slots,
+  // rows_per_slot] (log2 domain), slot = work range + line; meta = {NT, W,
+  // first tile of each sequence (B + 1 entries)}.
   float* part_o;
   float* part_lse;
   int* meta;
-  int B, H, max_pages, n_splits, tokens_per_split;  // group > 1: n_splits = max work ranges
+  int B, H, max_pages, n_splits;  // n_splits = the most work ranges
   int H_kv, group, qchunks;   // qchunks = ceil(group / 32)
-  int min_tiles, rows_per_slot;  // group > 1: tiles per range at least; min(group, 32)
+  int min_tiles, rows_per_slot;  // tiles per range at least; min(group, 32)
   int num_pages;              // page ids outside [0, num_pages) are rejected on the device
   float c;                    // scale * log2(e)
 };
 
-hipError_t launch_paged_decode(int D, bool bf16, bool out_f32, const DecodeArgs& a,
-                               hipStream_t s);
 hipError_t launch_paged_decode_gqa(int D, bool bf16, bool out_f32, const DecodeArgs& a,
                                    hipStream_t s);
-// The log-sum-exp merge of the per-split partials (eight (b, h) rows per
-// 64-lane workgroup).
-hipError_t launch_decode_combine(int D, bool bf16, bool out_f32, const DecodeArgs& a,
-                                 hipStream_t s);
 
 // Argument checks of paged decode (api.cpp), shared by the entry point that
 // takes a workspace and the one that uses the library's own array.

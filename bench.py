@@ -47,7 +47,6 @@ PEAK_MFMA_F16 = 2516.6   # TFLOP/s, MI355X dense fp16/bf16
 PEAK_MFMA_FP8 = 5033.2   # TFLOP/s, MI355X dense fp8
 PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
 PREFILL_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "prefill.hip")
-DECODE_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode.hip")
 DECODE_GQA_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "decode_gqa.hip")
 BACKWARD_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "backward.hip")
 
@@ -347,14 +346,11 @@ def bench_decode(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
                "dtype": batch.meta["dtype"],
                "page_size": batch.page_size, "num_pages": batch.num_pages,
                "live_tokens": n_tok}
-    if H_kv == H:
-        cfg_out.update(n_splits=n_splits, tokens_per_split=tps)
-    else:  # tiles of the whole batch cut into equal ranges on the device
-        cfg_out.update(max_work_ranges=n_splits, min_tokens_per_range=tps)
+    # tiles of the whole batch cut into equal ranges on the device
+    cfg_out.update(max_work_ranges=n_splits, min_tokens_per_range=tps)
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM, 4),
-            "traffic": load_traffic(f"decode_split__{batch.meta['name']}", DECODE_SRC) if H_kv == H
-            else load_traffic(f"decode_gqa_split__{batch.meta['name']}", DECODE_GQA_SRC)}
+            "traffic": load_traffic(f"decode_gqa_split__{batch.meta['name']}", DECODE_GQA_SRC)}
     del g, ws, o
     torch.cuda.empty_cache()
     cpu = cpu_baseline_decode(batch, cpu_budget) if cpu_budget > 0 else None

@@ -214,7 +214,8 @@ int attn_extend(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace attn_paged_decode needs for these sizes: the
- * per-split partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
+ * partial outputs and log-sum-exps of the work ranges, and the ranges'
+ * metadata.  Returns 0 for invalid sizes.
  */
 size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_seq,
                                         int page_size);
@@ -241,11 +242,14 @@ size_t attn_paged_decode_workspace_size(int B, int H, int D, int max_pages_per_s
  *     [0, num_pages) is never dereferenced, and O[b] (every head) is NaN.
  *   - Other page-table entries and cache slots past seq_lens[b] are never read.
  *
- * The KV range of each sequence is cut into splits; each split produces a
- * partial output and its log-sum-exp, and a combine kernel merges them
- * (flash decoding; "Wave February 2025 Release", FlashDecoding list; KV split
- * sized to fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950",
- * Changes / Host side).  Splits past a sequence's end do no work.
+ * Flash decoding ("Wave February 2025 Release", FlashDecoding list): the
+ * batch's KV is cut into pieces, each producing a partial output and its
+ * log-sum-exp, and a combine kernel merges them.  The pieces are equal work
+ * ranges of the batch's 32-token tiles, cut on the device from the actual
+ * lengths (sized to fill the GPU: "[FlyDSL] FP8 MQA logits improvements for
+ * gfx950", Changes / Host side); see attn_paged_decode_gqa for the details
+ * and the arithmetic, which are the same (this is attn_paged_decode_gqa with
+ * H_kv = H).
  */
 int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* page_table, const int32_t* seq_lens, void* o,
@@ -257,24 +261,22 @@ int attn_paged_decode(const void* q, const void* k_cache, const void* v_cache,
  * Grouped-query (and multi-query) paged decode: as attn_paged_decode, with a
  * cache of H_kv heads ([num_pages, page_size, H_kv, D]) shared by the H query
  * heads of q: query head h reads KV head h / (H / H_kv).  H_kv must divide H
- * (else ATTN_E_INVALID).  With H_kv < H the query heads of a group are
- * decoded together, so each cache row is read from memory once per group;
- * with H_kv = H this is attn_paged_decode.  The workspace comes from
+ * (else ATTN_E_INVALID).  The query heads of a group are decoded together,
+ * so each cache row is read from memory once per group; with H_kv = H this
+ * is attn_paged_decode.  The workspace comes from
  * attn_paged_decode_gqa_workspace_size; page ids and lengths are treated as
  * in attn_paged_decode (a bad page id makes O[b] NaN for every head).
- * Arithmetic for H_kv < H: Q.K^T on MFMA in the input dtype with fp32
- * accumulation, softmax in fp32, P rounded to fp16 and P.V on fp16 MFMA
- * (bf16 V converted to fp16 on staging, as in attn_prefill).
- * Work division for H_kv < H: instead of fixed per-sequence splits, the
- * batch's 32-token tiles, taken sequence by sequence and KV head by KV head,
- * are cut on the device into W equal contiguous ranges (W at most
- * attn_paged_decode_gqa_num_splits, fewer for short batches), one wave each;
- * a range that crosses sequences writes one partial per sequence and KV head
- * it touches, and the log-sum-exp combine merges them (flash decoding with
- * the KV split sized to fill the GPU, as above).  The workspace also holds
- * the range metadata, rewritten by every call.  With fp16 inputs and fp16
- * output the partial outputs (normalised, so within fp16 range) are kept in
- * fp16; otherwise in fp32.
+ * Arithmetic: Q.K^T on MFMA in the input dtype with fp32 accumulation,
+ * softmax in fp32, P rounded to fp16 and P.V on fp16 MFMA (bf16 V converted
+ * to fp16 on staging, as in attn_prefill).
+ * Work division: the batch's 32-token tiles, taken sequence by sequence and
+ * KV head by KV head, are cut on the device into W equal contiguous ranges
+ * (W at most attn_paged_decode_gqa_num_splits, fewer for short batches), one
+ * wave each; a range that crosses sequences writes one partial per sequence
+ * and KV head it touches, and the log-sum-exp combine merges them.  The
+ * workspace also holds the range metadata, rewritten by every call.  With
+ * fp16 inputs and fp16 output the partial outputs (normalised, so within
+ * fp16 range) are kept in fp16; otherwise in fp32.
  */
 int attn_paged_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* page_table, const int32_t* seq_lens, void* o,
@@ -316,20 +318,18 @@ int attn_paged_decode_gqa_noalloc(const void* q, const void* k_cache, const void
 size_t attn_paged_decode_gqa_workspace_size(int B, int H, int H_kv, int D,
                                             int max_pages_per_seq, int page_size);
 
-/* Work plan of attn_paged_decode_gqa.  H_kv = H: the multi-head split plan
- * (see attn_paged_decode_num_splits).  H_kv < H: returns the largest number
- * of work ranges W a call uses (0 on invalid sizes) and stores in
- * tokens_per_split the fewest tokens a range covers unless the batch holds
- * fewer: 16 per query head of the group, at most 256, at least 32.  W is
- * at most 2048, or 1024 for groups of 16 or more query heads. */
+/* Work plan of attn_paged_decode_gqa: returns the largest number of work
+ * ranges W a call uses (0 on invalid sizes) and, if tokens_per_split is not
+ * NULL, stores there the fewest tokens a range covers unless the batch holds
+ * fewer: 16 per query head of the group, at most 256, at least 128.  W is at
+ * most 2048, or 1024 for groups of 16 or more query heads.  The plan depends
+ * only on these host-side sizes (the host never reads seq_lens); the ranges
+ * themselves are cut on the device from the actual lengths. */
 int attn_paged_decode_gqa_num_splits(int B, int H, int H_kv, int max_pages_per_seq,
                                      int page_size, int* tokens_per_split);
 
-/* Split plan of attn_paged_decode: returns the number of KV splits per
- * sequence (0 on invalid sizes) and, if tokens_per_split is not NULL, stores
- * the tokens per split there.  The plan depends only on these host-side
- * sizes (the host never reads seq_lens), so it is the same for every call
- * with the same sizes. */
+/* Work plan of attn_paged_decode: attn_paged_decode_gqa_num_splits with
+ * H_kv = H. */
 int attn_paged_decode_num_splits(int B, int H, int max_pages_per_seq, int page_size,
                                  int* tokens_per_split);
 

@@ -219,18 +219,19 @@ def test_decode_gqa_validation(kw, status):
 
 
 def test_gqa_split_plan_and_workspace():
-    # H_kv = H is the multi-head plan
+    # attn_paged_decode is the H_kv = H case
     assert attn.attn_paged_decode_gqa_num_splits(64, 32, 32, 512, 16) == \
         attn.attn_paged_decode_num_splits(64, 32, 512, 16)
     assert attn.attn_paged_decode_gqa_workspace_size(64, 32, 32, 128, 512, 16) == \
         attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
-    # H_kv < H: (work ranges, tokens per range at least).  The batch's tiles
-    # are cut into at most 2048 equal ranges (one resident wave each; 1024
-    # for groups of 16 or more query heads, whose partials are larger), each
-    # covering at least min(min(group, 32) / 2, 8) tiles of 32 tokens, so a
+    # (work ranges, tokens per range at least).  The batch's tiles are cut
+    # into at most 2048 equal ranges (one resident wave each; 1024 for groups
+    # of 16 or more query heads, whose partials are larger), each covering at
+    # least min(group, 32) / 2 tiles of 32 tokens, clamped to [4, 8], so a
     # range's partial rows (one per query of the group) stay a small share of
-    # its K/V
-    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16) == (2048, 64)
+    # its K/V and its start a small share of its time
+    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 32, 512, 16) == (2048, 128)
+    assert attn.attn_paged_decode_gqa_num_splits(64, 32, 8, 512, 16) == (2048, 128)
     assert attn.attn_paged_decode_gqa_num_splits(256, 32, 1, 512, 16) == (1024, 256)
     assert attn.attn_paged_decode_gqa_num_splits(64, 32, 2, 512, 16) == (1024, 256)
     assert attn.attn_paged_decode_gqa_num_splits(64, 64, 8, 512, 16) == (2048, 128)
@@ -270,7 +271,7 @@ def _decode(**kw):
     (dict(k_cache=FAKE + 4), attn.ATTN_E_INVALID),
     (dict(workspace=None), attn.ATTN_E_WORKSPACE),
     (dict(workspace_bytes=16), attn.ATTN_E_WORKSPACE),
-    (dict(B=70000), attn.ATTN_E_UNSUPPORTED),
+    (dict(B=1 << 28), attn.ATTN_E_UNSUPPORTED),  # B * H past 32-bit indexing
 ])
 def test_decode_validation(kw, status):
     assert _decode(**kw) == status
@@ -282,15 +283,17 @@ def test_decode_empty_is_a_noop():
 
 
 def test_split_plan_and_workspace():
+    # one line per (sequence, head): 64 x 32 lines of up to 256 tiles, cut
+    # into at most 2048 ranges of at least 4 tiles (128 tokens)
     n, tps = attn.attn_paged_decode_num_splits(64, 32, 512, 16)
-    assert tps % 64 == 0 and tps >= 64
-    assert n == math.ceil(512 * 16 / tps)
+    assert (n, tps) == (2048, 128)
     ws = attn.attn_paged_decode_workspace_size(64, 32, 128, 512, 16)
-    rows = 64 * 32 * n
-    assert ws >= rows * 129 * 4
-    # a small batch splits finer so the grid still fills the GPU
-    n1, tps1 = attn.attn_paged_decode_num_splits(1, 32, 512, 16)
-    assert tps1 <= tps and n1 >= n
+    slots = n + 64 * 32  # (range, line) pairs a call can touch
+    assert ws >= slots * 129 * 4 + (64 + 3) * 4
+    # fewer ranges when the batch cannot hold 2048 of at least 4 tiles
+    assert attn.attn_paged_decode_num_splits(1, 1, 8, 16) == (1, 128)
+    assert attn.attn_paged_decode_num_splits(1, 32, 512, 16) == (2048, 128)
+    assert attn.attn_paged_decode_num_splits(1, 4, 64, 16) == (32, 128)
     assert attn.attn_paged_decode_num_splits(4, 8, 8, 7) == (0, 0)
     assert attn.attn_paged_decode_workspace_size(4, 8, 96, 8, 16) == 0
 
@@ -379,7 +382,7 @@ def _decode_noalloc(**kw):
     (dict(B=0), attn.ATTN_OK),
     # partials beyond the library's 32 MiB array: refused before any HIP call
     (dict(B=4096, H=32, H_kv=32, max_pages_per_seq=512), attn.ATTN_E_WORKSPACE),
-    (dict(B=64, H=32, H_kv=32, max_pages_per_seq=8192), attn.ATTN_E_WORKSPACE),
+    (dict(B=2048, H=32, H_kv=1, max_pages_per_seq=512), attn.ATTN_E_WORKSPACE),
 ])
 def test_decode_noalloc_validation(kw, status):
     assert _decode_noalloc(**kw) == status

@@ -2,9 +2,9 @@
 
 The oracle gathers each sequence's K/V through the page table explicitly.
 Full-size workload: every (sequence, head) output is compared.  Edge cases:
-sequence lengths around page and split boundaries, NaN-poisoned unused cache
-slots, bitwise invariance under a page-pool permutation, and split-plan
-invariance within fp32 noise.
+sequence lengths around page (16), tile (32) and range boundaries,
+NaN-poisoned unused cache slots, bitwise invariance under a page-pool
+permutation and under a wider page table, a single sequence in short ranges.
 """
 import math
 
@@ -74,19 +74,19 @@ def test_decode_pool_permutation_bitwise(gpu_lib):
     assert_parity(a.double().numpy(), _ref(batch), "pool permutation")
 
 
-def test_decode_split_plan_invariance(gpu_lib):
-    """Widening the page table (unused columns) changes the split plan, not O."""
+def test_decode_wide_page_table_changes_nothing(gpu_lib):
+    """Widening the page table (unused columns, holding an id past the pool)
+    leaves O bitwise the same: the work ranges are cut from the actual
+    lengths on the device, not from the table's width, and the unused
+    columns are never read."""
     attn = gpu_lib
     batch = workloads.paged_decode_inputs(B=32, H=8, D=128, page_size=16, num_pages=8192,
                                           max_seq=4096, seed=31)
-    plan_a = attn.attn_paged_decode_num_splits(32, 8, batch.max_pages_per_seq, 16)
-    wide = torch.full((32, 4096), batch.meta["unused_page"], dtype=torch.int32)
+    wide = torch.full((32, 4096), batch.num_pages + 7, dtype=torch.int32)
     wide[:, :batch.max_pages_per_seq] = batch.page_table
-    plan_b = attn.attn_paged_decode_num_splits(32, 8, 4096, 16)
-    assert plan_a[1] != plan_b[1], (plan_a, plan_b)
     a = _run(attn, batch)
     b = _run(attn, batch, page_table=wide)
-    assert float((a.double() - b.double()).abs().max()) <= 2e-3
+    assert torch.equal(a, b)
     assert_parity(b.double().numpy(), _ref(batch), "wide page table")
 
 
@@ -120,15 +120,16 @@ def test_decode_large_logits(gpu_lib, dtype, amp):
     assert_parity(o.double().numpy(), _ref(batch), f"decode amp {amp} {dtype}")
 
 
-def test_decode_small_batch_fine_splits(gpu_lib):
-    """One sequence: the plan picks its smallest split, so most splits hold
-    one 64-token batch and some hold none."""
+def test_decode_small_batch_short_ranges(gpu_lib):
+    """One sequence of 3000 tokens over four heads: 376 tiles in ranges of the
+    fewest tiles the plan allows (4), some of them crossing from one head's
+    line to the next."""
     batch = workloads.paged_decode_inputs(B=1, H=4, D=64, page_size=16, num_pages=700,
                                           seq_lens=[3000], max_pages_per_seq=640, seed=42)
     n, tps = gpu_lib.attn_paged_decode_num_splits(1, 4, 640, 16)
-    assert tps == 64 and n == 160
+    assert (n, tps) == (320, 128)
     o = _run(gpu_lib, batch)
-    assert_parity(o.double().numpy(), _ref(batch), "B1 fine splits")
+    assert_parity(o.double().numpy(), _ref(batch), "B1 short ranges")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -143,11 +144,21 @@ def test_decode_out_f32(gpu_lib, dtype):
     o32 = attn.paged_decode(*args, out_dtype=torch.float32)
     o16 = attn.paged_decode(*args)
     torch.cuda.synchronize()
-    # Decode keeps P in fp32 (no fp16 rounding anywhere), so with an fp32
-    # output only fp32 accumulation error remains.
+    # With an fp32 output only the rounding of P to fp16 for the P.V product
+    # (2^-11 relative per weight) and fp32 accumulation remain: the bar of the
+    # grouped-query fp32-output test.
     assert_parity(o32.double().cpu().numpy(), _ref(batch), f"decode out_f32 {dtype}",
-                  max_abs_tol=1e-5, rel_fro_tol=1e-5)
-    assert torch.equal(o32.to(o16.dtype), o16)
+                  max_abs_tol=3e-3, rel_fro_tol=5e-4)
+    if dtype == "bf16":
+        # both outputs come from the same fp32 partials: the default output is
+        # the fp32 one rounded
+        assert torch.equal(o32.to(o16.dtype), o16)
+    else:
+        # fp16 inputs and output keep the partials in fp16, rounded once
+        # more than for the fp32 output
+        assert_parity(o16.double().cpu().numpy(), o32.double().cpu().numpy(),
+                      "decode fp16 output against the fp32 output", max_abs_tol=2e-3,
+                      rel_fro_tol=5e-4)
 
 
 def test_decode_rejects_bad_page_ids_on_device(gpu_lib):

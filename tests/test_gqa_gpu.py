@@ -208,8 +208,7 @@ def test_decode_combine_row_groups(gpu_lib, lens, H, H_kv, dtype):
     """The combines merge eight (sequence, head) rows per workgroup: B*H not a
     multiple of eight leaves the last workgroup part empty, and long
     sequences give a row more partials than one batch of loads holds (fp16
-    partials 16 at a time, fp32 ones 8; the multi-head case has up to 16
-    splits)."""
+    partials 16 at a time, fp32 ones 8)."""
     assert (len(lens) * H) % 8 != 0
     batch = _lens_batch(lens, H, H_kv, seed=81 + H, dtype=dtype)
     print(f"[case] decode combine rows B{len(lens)} H{H}/{H_kv} {dtype} {lens}", flush=True)

@@ -41,7 +41,7 @@ def test_decode_noalloc_matches_workspace_form_twice(gpu_lib):
     o_ws, o_na = _both(attn, big, big.meta["scale"])
     assert torch.isfinite(o_na.float()).all()
     assert torch.equal(o_na, o_ws)
-    # a smaller batch through the same array (multi-head split plan, bf16)
+    # a smaller batch through the same array (one head per KV head, bf16)
     small = workloads.paged_decode_inputs(B=5, H=8, D=128, dtype="bf16", page_size=16,
                                           num_pages=300, seq_lens=[1, 700, 16, 2000, 33], seed=9)
     o_ws, o_na = _both(attn, small, 0.09)
