@@ -191,3 +191,24 @@ def test_decode_rejects_bad_page_ids_on_device(gpu_lib):
     assert torch.isfinite(o[good]).all()
     ref = _ref(batch)
     assert_parity(o[good].double().numpy(), ref[good], "sequences with valid pages")
+
+
+def test_decode_many_sequences(gpu_lib):
+    """70000 short sequences (more than a 16-bit grid dimension holds), two
+    heads, lengths 0-40: every row is written (NaN-prefilled output), empty
+    sequences give 0, and sampled sequences match the oracle."""
+    r = np.random.default_rng(5)
+    lens = r.integers(0, 41, 70000).tolist()
+    pages = sum(-(-n // 16) for n in lens)
+    batch = workloads.paged_decode_inputs(B=70000, H=2, D=64, dtype="f16", page_size=16,
+                                          num_pages=pages + 16, seq_lens=lens,
+                                          max_pages_per_seq=3, seed=77)
+    out = torch.full(tuple(batch.q.shape), float("nan"), dtype=batch.q.dtype, device="cuda")
+    o = _run(gpu_lib, batch, out=out)
+    assert torch.isfinite(o.float()).all()
+    empty = [b for b, n in enumerate(lens) if n == 0]
+    assert torch.count_nonzero(o[empty]) == 0
+    idx = list(range(0, 70000, 117)) + list(range(69990, 70000))
+    ref = oracle.paged_decode(batch.q, batch.k_cache, batch.v_cache, batch.page_table,
+                              batch.seq_lens, batch_indices=idx)
+    assert_parity(o[idx].double().numpy(), ref, "decode 70000 sequences (sampled)")
