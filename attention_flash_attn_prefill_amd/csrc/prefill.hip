@@ -68,6 +68,10 @@ namespace {
 
 #include "cdna4_common.h"
 
+// Extend batches of up to 64 * kExtMaxPerLane sequences are ordered longest
+// unit first (wave 0 holds kExtMaxPerLane sequences per lane).
+constexpr int kExtMaxPerLane = 8;
+
 // NW waves per workgroup (BM = 32 * NW query rows), BN keys per KV tile.
 // OF32: O is stored in fp32 instead of the input type.  EXT (with CAUSAL):
 // extend attention -- a sequence's keys are its cached prefix, read through
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // fills the CUs at least twice (a.pair_tiles); a smaller grid would be left
   // with idle CUs.  Other work has one query tile per item, heaviest first.
   //
-  // Extend batches are ragged.  With at most 64 sequences the work goes out
+  // Extend batches are ragged.  With at most 512 sequences the work goes out
   // longest first over the whole batch: a unit is (sequence b, query tile
   // mt), worth ceil(P_b / RPW) + mt + 1 (its prefix plus causal keys, in
   // query-tile lengths), and units are taken in decreasing worth (ties by
@@ -133,9 +137,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // same XCD).  The dispatcher hands an XCD's workgroups to its shader
   // engines in turn and in order, so heavy units last would leave engines
   // idle behind a long one.  Wave 0 finds this workgroup's unit from the
-  // batch's sizes (one lane per sequence): the unit's worth c by bisection
-  // on the count of units worth at least c, then its sequence among those
-  // with a unit worth exactly c.  Units past the last non-empty one have no
+  // batch's sizes (lane l holding sequences l, 64 + l, ...): the unit's
+  // worth c by bisection on the count of units worth at least c, then its
+  // sequence among those with a unit worth exactly c.  Units past the last non-empty one have no
   // rows.  Larger batches go in (sequence, KV head) blocks interleaved over
   // the XCDs, heaviest query tile first within a block.
   const bool pairs = CAUSAL && !EXT && a.pair_tiles;  // uniform
@@ -146,51 +150,80 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   bool e_known = false;                // whether those three are set (workgroup-uniform)
   if constexpr (EXT) {
     const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv);
-    if (nb <= 64) {
+    if (nb <= 64 * kExtMaxPerLane) {
       int L = blockIdx.x;
       gg = L % hgroups;
       L /= hgroups;
       hk = L % a.H_kv;
       const int u = L / a.H_kv;  // rank of the unit
-      if (wave == 0) {
-        // Lane t: sequence t's first row, new tokens and prefix length (an
-        // invalid row range counts as no rows), and its query tiles and
-        // prefix in query-tile lengths.
-        int r0 = 0, len = 0, pre = 0;
-        if (lane < nb) {
-          r0 = a.qo_start[lane];
-          const int r1 = a.qo_start[lane + 1];
-          if (r0 >= 0 && r1 >= r0 && r1 <= a.total_tokens) {
-            len = min(r1 - r0, a.Sq);
-            pre = a.max_pages > 0 ? max(0, min(a.prefix_lens[lane], a.max_pages * kDecodePageSize))
-                                  : 0;
+      // Lane l holds sequences k * 64 + l, k < PER: their first row, new
+      // tokens and prefix length (an invalid row range counts as no rows),
+      // and their query tiles and prefix in query-tile lengths.  PER = 1 for
+      // up to 64 sequences, kExtMaxPerLane beyond.
+      auto find_unit = [&](auto per_c) __attribute__((always_inline)) {
+        constexpr int PER = decltype(per_c)::value;
+        int r0[PER], len[PER], pre[PER], nt[PER], npre[PER];
+  #pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          r0[k] = 0;
+          len[k] = 0;
+          pre[k] = 0;
+          const int t = k * 64 + lane;
+          if (t < nb) {
+            r0[k] = a.qo_start[t];
+            const int r1 = a.qo_start[t + 1];
+            if (r0[k] >= 0 && r1 >= r0[k] && r1 <= a.total_tokens) {
+              len[k] = min(r1 - r0[k], a.Sq);
+              pre[k] = a.max_pages > 0
+                           ? max(0, min(a.prefix_lens[t], a.max_pages * kDecodePageSize))
+                           : 0;
+            }
           }
+          nt[k] = (len[k] + RPW - 1) / RPW;
+          npre[k] = (pre[k] + RPW - 1) / RPW;
         }
-        const int nt = (len + RPW - 1) / RPW, npre = (pre + RPW - 1) / RPW;
-        // Units of sequence t are worth npre + 1 .. npre + nt; at least c:
+        // Units of a sequence are worth npre + 1 .. npre + nt; at least c:
         auto count = [&](int c) __attribute__((always_inline)) {
-          return wave_sum_i32(max(0, min(nt, npre + nt - c + 1)));
+          int n = 0;
+  #pragma unroll
+          for (int k = 0; k < PER; ++k) n += max(0, min(nt[k], npre[k] + nt[k] - c + 1));
+          return wave_sum_i32(n);
         };
+        int units = 0, top = 0;
+  #pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          units += nt[k];
+          top = max(top, npre[k] + nt[k]);
+        }
         int sel_b = -1, sel_mt = 0, sel_r0 = 0, sel_len = 0, sel_pre = 0;
-        if (u < wave_sum_i32(nt)) {
-          int lo = 1, hi = wave_max_i32(npre + nt) + 1;  // count(lo) > u >= count(hi)
+        if (u < wave_sum_i32(units)) {
+          int lo = 1, hi = wave_max_i32(top) + 1;  // count(lo) > u >= count(hi)
           while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (count(mid) > u) lo = mid;
             else hi = mid;
           }
-          const int j = u - count(lo + 1);  // among the sequences with a unit worth lo
-          const bool has = nt > 0 && npre < lo && lo <= npre + nt;
-          const uint64_t m = __builtin_amdgcn_read_exec() & __ballot(has);
-          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-          const uint64_t pick = __ballot(has && below == j);
-          if (pick != 0) {
-            sel_b = __builtin_ctzll(pick);
-            sel_mt = lo - __builtin_amdgcn_readlane(npre, sel_b) - 1;
-            sel_r0 = __builtin_amdgcn_readlane(r0, sel_b);
-            sel_len = __builtin_amdgcn_readlane(len, sel_b);
-            sel_pre = __builtin_amdgcn_readlane(pre, sel_b);
+          // Among the sequences with a unit worth lo (in sequence order),
+          // this workgroup's is the j-th.
+          int j = u - count(lo + 1);
+  #pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            if (sel_b >= 0) break;  // uniform
+            const bool has = nt[k] > 0 && npre[k] < lo && lo <= npre[k] + nt[k];
+            const uint64_t m = __builtin_amdgcn_read_exec() & __ballot(has);
+            const int c = __builtin_popcountll(m);
+            if (j >= c) {
+              j -= c;
+              continue;
+            }
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const int pick = __builtin_ctzll(__ballot(has && below == j));
+            sel_b = k * 64 + pick;
+            sel_mt = lo - __builtin_amdgcn_readlane(npre[k], pick) - 1;
+            sel_r0 = __builtin_amdgcn_readlane(r0[k], pick);
+            sel_len = __builtin_amdgcn_readlane(len[k], pick);
+            sel_pre = __builtin_amdgcn_readlane(pre[k], pick);
           }
         }
         if (lane == 0) {
@@ -200,6 +233,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
           ext_unit[3] = sel_len;
           ext_unit[4] = sel_pre;
         }
+      };
+      if (wave == 0) {
+        if (nb <= 64) find_unit(std::integral_constant<int, 1>{});
+        else find_unit(std::integral_constant<int, kExtMaxPerLane>{});
       }
       __syncthreads();
       b = __builtin_amdgcn_readfirstlane(ext_unit[0]);
