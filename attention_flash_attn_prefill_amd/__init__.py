@@ -6,12 +6,14 @@ device memory and the current stream; nothing here computes attention, and
 there is no CPU fallback: if the shared library is missing the calls raise.
 
 Low-level functions carry the C names (``attn_prefill``,
-``attn_prefill_gqa``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
+``attn_prefill_gqa``, ``attn_prefill_lse``, ``attn_prefill_splitkv``,
+``attn_prefill_bwd``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
 workspace-size and split-plan queries, ``attn_prefill_fp8``, ``attn_extend``,
-``attn_status_string``)
-and take tensors or raw integer pointers; ``prefill``, ``prefill_fp8``,
-``paged_decode`` and ``extend`` are conveniences that derive the sizes (including the number of KV heads) from
-tensor shapes and allocate the output.
+``attn_status_string``) and take tensors or raw integer pointers;
+``prefill``, ``prefill_with_lse``, ``prefill_splitkv``, ``prefill_backward``,
+``prefill_fp8``, ``paged_decode`` and ``extend`` are conveniences that derive
+the sizes (including the number of KV heads) from tensor shapes and allocate
+the output.
 """
 from __future__ import annotations
 
@@ -51,6 +53,10 @@ SIGNATURES = {
                          _I, _I, _I, _F, _VP]),
     "attn_prefill_lse": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                               _VP]),
+    "attn_prefill_splitkv": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                  _VP, _SZ, _VP]),
+    "attn_prefill_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "attn_prefill_splitkv_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "attn_prefill_bwd_workspace_size": (_SZ, [_I, _I, _I]),
     "attn_prefill_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
                               _I, _I, _I, _F, _VP, _SZ, _VP]),
@@ -135,6 +141,23 @@ def attn_prefill_lse(q, k, v, o, lse, B, H, H_kv, Sq, Skv, D, layout, dtype, cau
     return load_library().attn_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
                                            H_kv, Sq, Skv, D, layout, dtype, int(bool(causal)),
                                            float(scale), _stream(stream))
+
+
+def attn_prefill_splitkv(q, k, v, o, B, H, H_kv, Sq, Skv, D, layout, dtype, causal, scale,
+                         workspace, workspace_bytes, stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_prefill_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, H_kv,
+                                               Sq, Skv, D, layout, dtype, int(bool(causal)),
+                                               float(scale), _ptr(workspace),
+                                               int(workspace_bytes), _stream(stream))
+
+
+def attn_prefill_splitkv_num_splits(B, H, Sq, Skv, D) -> int:
+    return int(load_library().attn_prefill_splitkv_num_splits(B, H, Sq, Skv, D))
+
+
+def attn_prefill_splitkv_workspace_size(B, H, Sq, Skv, D) -> int:
+    return int(load_library().attn_prefill_splitkv_workspace_size(B, H, Sq, Skv, D))
 
 
 def attn_prefill_bwd_workspace_size(B, H, Sq) -> int:
@@ -295,6 +318,31 @@ def prefill(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None, out_d
     o = _like(out, q, odt, "out")
     _check(attn_prefill_gqa(q, k, v, o, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], code,
                             causal, scale, stream), "attn_prefill_gqa")
+    return o
+
+
+def prefill_splitkv(q, k, v, *, causal=False, scale=None, layout="BHSD", out=None,
+                    out_dtype=None, workspace=None, stream=None):
+    """``prefill`` through attn_prefill_splitkv: for grids too small to fill
+    the GPU (few query tiles against many keys) the keys are split over
+    workgroups and the partial results merged.  `workspace` (a uint8 GPU
+    tensor of at least attn_prefill_splitkv_workspace_size bytes) is
+    allocated when not given."""
+    import torch
+    B, H, H_kv, Sq, Skv, D = _prefill_shapes(q, k, v, layout)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code, odt = _out_code(q, out, out_dtype)
+    o = _like(out, q, odt, "out")
+    need = attn_prefill_splitkv_workspace_size(B, H, Sq, Skv, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(attn_prefill_splitkv(q, k, v, o, B, H, H_kv, Sq, Skv, D, LAYOUTS[layout], code,
+                                causal, scale, workspace, nbytes, stream),
+           "attn_prefill_splitkv")
     return o
 
 

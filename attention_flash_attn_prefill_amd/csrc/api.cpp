@@ -141,9 +141,17 @@ int attn_prefill_gqa(const void* q, const void* k, const void* v, void* o, int B
                           scale, stream);
 }
 
-int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
-                     float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of a dense prefill and its kernel arguments, before any HIP
+// call.  ATTN_OK with *run = false: nothing to compute.
+int prepare_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
+                    float scale, PrefillArgs* ap, bool* bf16_out, bool* out_f32_out,
+                    bool* run) {
+  *run = false;
   if (B < 0 || H < 0 || H_kv < 0 || Sq < 0 || Skv < 0) return ATTN_E_INVALID;
   if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
   if (layout != ATTN_BHSD && layout != ATTN_BSHD) return ATTN_E_INVALID;
@@ -167,7 +175,7 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
   if (q_row >= ((int64_t)1 << 24) || kv_row >= ((int64_t)1 << 24)) return ATTN_E_UNSUPPORTED;
   if ((int64_t)B * H * ((Sq + 127) / 128) >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
 
-  PrefillArgs a;
+  PrefillArgs& a = *ap;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -193,7 +201,91 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
   a.page_table = a.prefix_lens = a.qo_start = nullptr;
   a.max_pages = a.num_pages = a.total_tokens = 0;
   a.lse = lse;
+  a.n_splits = 1;
+  a.split_tiles = (Skv + 63) / 64;
+  a.split_o_stride = a.split_lse_stride = 0;
+  *bf16_out = bf16;
+  *out_f32_out = out_f32;
+  *run = true;
+  return ATTN_OK;
+}
+
+// Split-KV plan of attn_prefill_splitkv, from sizes only: split the keys of
+// each query tile when the grid (one workgroup per head and 256-row query
+// tile; 128 rows for D = 64) would hold fewer than two workgroups per CU, into
+// at most enough ranges for two per CU, each at least 8 key tiles (512 keys).
+struct SplitKvPlan {
+  int n_splits, split_tiles;
+};
+SplitKvPlan plan_prefill_splitkv(int B, int H, int Sq, int Skv, int D) {
+  constexpr int64_t kMinSplitTiles = 8;
+  const int64_t rows = D == 128 ? 256 : 128;
+  const int64_t items = (int64_t)B * H * ((Sq + rows - 1) / rows);
+  const int64_t n_kt = ((int64_t)Skv + 63) / 64;
+  if (items <= 0 || items >= 2 * kNumCUs || n_kt < 2 * kMinSplitTiles)
+    return SplitKvPlan{1, (int)n_kt};
+  const int64_t want = (2 * kNumCUs + items - 1) / items;
+  const int64_t n = want < n_kt / kMinSplitTiles ? want : n_kt / kMinSplitTiles;
+  const int64_t tiles = (n_kt + n - 1) / n;
+  return SplitKvPlan{(int)((n_kt + tiles - 1) / tiles), (int)tiles};
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
+                     float scale, hipStream_t stream) {
+  PrefillArgs a;
+  bool bf16 = false, out_f32 = false, run = false;
+  const int st = prepare_prefill(q, k, v, o, lse, B, H, H_kv, Sq, Skv, D, layout, dtype, scale, &a,
+                                 &bf16, &out_f32, &run);
+  if (st != ATTN_OK || !run) return st;
   hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+size_t attn_prefill_splitkv_workspace_size(int B, int H, int Sq, int Skv, int D) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0 || (D != 64 && D != 128)) return 0;
+  const SplitKvPlan p = plan_prefill_splitkv(B, H, Sq, Skv, D);
+  if (p.n_splits <= 1) return 0;
+  const size_t rows = (size_t)B * H * Sq;
+  return (size_t)p.n_splits * (align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)));
+}
+
+int attn_prefill_splitkv_num_splits(int B, int H, int Sq, int Skv, int D) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0 || (D != 64 && D != 128)) return 0;
+  return plan_prefill_splitkv(B, H, Sq, Skv, D).n_splits;
+}
+
+int attn_prefill_splitkv(const void* q, const void* k, const void* v, void* o, int B, int H,
+                         int H_kv, int Sq, int Skv, int D, int layout, int dtype, int causal,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  PrefillArgs a;
+  bool bf16 = false, out_f32 = false, run = false;
+  const int st = prepare_prefill(q, k, v, o, nullptr, B, H, H_kv, Sq, Skv, D, layout, dtype,
+                                 scale, &a, &bf16, &out_f32, &run);
+  if (st != ATTN_OK || !run) return st;
+  const SplitKvPlan p = plan_prefill_splitkv(B, H, Sq, Skv, D);
+  if (p.n_splits <= 1) {  // the grid fills the GPU: the plain prefill
+    hipError_t e = launch_prefill(D, bf16, causal != 0, out_f32, a, B, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  }
+  const size_t need = attn_prefill_splitkv_workspace_size(B, H, Sq, Skv, D);
+  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_E_INVALID;
+  const size_t rows = (size_t)B * H * Sq;
+  a.n_splits = p.n_splits;
+  a.split_tiles = p.split_tiles;
+  a.split_o_stride = (int64_t)rows * D;
+  a.split_lse_stride = (int64_t)rows;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             p.n_splits * align256(rows * D * sizeof(float)));
+  hipError_t e = launch_prefill_splitkv(D, bf16, causal != 0, out_f32, a, B, part_o, part_lse,
+                                        stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

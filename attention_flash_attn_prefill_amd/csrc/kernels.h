@@ -38,10 +38,20 @@ struct PrefillArgs {
   // Forward only: if not null, the natural log-sum-exp of each query row's
   // scaled logits, [B, H, Sq] fp32 (-inf for a row with no visible key).
   float* lse;
+  // Split-KV prefill only (launch_prefill_splitkv): the keys of each query
+  // tile are cut into n_splits ranges of split_tiles 64-key tiles.
+  int n_splits, split_tiles;
+  int64_t split_o_stride, split_lse_stride;  // elements between the partials' planes
 };
 
 hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const PrefillArgs& a,
                           int B, hipStream_t s);
+// Split-KV prefill: the split kernel writes partial O (fp32, q's strides)
+// and log-sum-exps per key range into part_o / part_lse (n_splits planes of
+// B*H*Sq*D and B*H*Sq floats), then a combine kernel merges them into a.o.
+hipError_t launch_prefill_splitkv(int D, bool bf16, bool causal, bool out_f32,
+                                  const PrefillArgs& a, int B, float* part_o, float* part_lse,
+                                  hipStream_t s);
 // FP8 (e4m3fn) q, k, v: Q.K^T on the fp8 MFMA, V widened to fp16 on staging;
 // O in fp16 (out_bf16 = false), bf16 or fp32.  Strides are in elements (bytes).
 hipError_t launch_prefill_fp8(int D, bool out_bf16, bool causal, bool out_f32,

@@ -78,13 +78,19 @@ constexpr int kExtMaxPerLane = 8;
 // the page table, followed by its new tokens (PrefillArgs, extend fields).
 // FP8: q, k, v are e4m3fn bytes; Q.K^T runs on the fp8 MFMA (32x32x64), V is
 // widened to fp16 on staging, and BF16 then selects only the output type.
+// SPLIT (with OF32, not EXT): the keys of each query tile are cut into
+// a.n_splits ranges of a.split_tiles tiles, one work item each, which writes
+// its partial O (normalised by its own row sums) and log-sum-exp into its
+// split's planes of a.o and a.lse (flash decoding applied to prefill, for
+// grids too small to fill the GPU); prefill_split_combine_kernel merges them.
 template <int D, bool BF16, bool CAUSAL, bool OF32, int NW, int BN, bool EXT = false,
-          bool FP8 = false, int HPW = 1>
+          bool FP8 = false, int HPW = 1, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) {
   // The body uses amdgcn-only types (buffer resources, LDS address space); the
   // host pass only needs the kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(!(EXT && FP8), "extend takes fp16/bf16");
+  static_assert(!SPLIT || (OF32 && !EXT && HPW == 1), "split partials are fp32, dense, one head");
   static_assert(NW % HPW == 0, "whole waves per query head");
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;
@@ -142,10 +148,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // sequence among those with a unit worth exactly c.  Units past the last non-empty one have no
   // rows.  Larger batches go in (sequence, KV head) blocks interleaved over
   // the XCDs, heaviest query tile first within a block.
-  const bool pairs = CAUSAL && !EXT && a.pair_tiles;  // uniform
+  const bool pairs = CAUSAL && !EXT && !SPLIT && a.pair_tiles;  // uniform
   const int hgroups = a.group / HPW;
   const int n_items = pairs ? (a.n_mtiles + 1) >> 1 : a.n_mtiles;
   int gg, item, hk, b;
+  int split = 0;  // SPLIT: this work item's key range (workgroup-uniform)
   int e_r0 = 0, e_len = 0, e_pre = 0;  // sequence b's first row, new tokens, prefix
   bool e_known = false;                // whether those three are set (workgroup-uniform)
   if constexpr (EXT) {
@@ -259,6 +266,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     }
   } else {
     int L = xcd_remap(blockIdx.x, a.total_tiles);
+    if constexpr (SPLIT) {  // the splits of a query tile are adjacent (one XCD)
+      split = L % a.n_splits;
+      L /= a.n_splits;
+    }
     gg = L % hgroups;
     L /= hgroups;
     item = L % n_items;
@@ -338,14 +349,22 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     // Keys this workgroup needs: [0, kv_end).
     int kv_end = Skv;
     if (CAUSAL) kv_end = min(kv_end, max(0, min(m0 + RPW, Sq) + coff));
-    const int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
+    // SPLIT: this work item takes key tiles [kt0, kt0 + n_tiles) of them.
+    int kt0 = 0;
+    int n_tiles = EXT ? n_pre + (kv_end - P + BN - 1) / BN : (kv_end + BN - 1) / BN;
+    if constexpr (SPLIT) {
+      kt0 = split * a.split_tiles;
+      n_tiles = max(0, min(n_tiles, kt0 + a.split_tiles) - kt0);
+    }
     // Keys this wave needs: [0, wave_kv_end).
     const bool wave_active = q0 < Sq;
     const int wave_kv_end = CAUSAL ? min(Skv, min(q0 + 32, Sq) + coff) : Skv;
     // First key (in the whole key sequence) of tile t, and whether it is a
     // prefix tile (extend only).
     auto is_pre = [&](int t) { return EXT && t < n_pre; };
-    auto tile_key0 = [&](int t) { return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : t * BN; };
+    auto tile_key0 = [&](int t) {
+      return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : (kt0 + t) * BN;
+    };
 
     // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
     // LDS chunk P = (wave * LOADS + i) * 64 + lane of the tile: row P / CPR,
@@ -710,11 +729,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     // Epilogue: O = acc / l.  Lane owns query qi and, in block db, the four
     // consecutive d = 32db + 8g + 4hi .. +3 for g = 0..3.
     const float l_tot = pair_sum(l_run);
-    if (a.lse != nullptr && q_ok && hi == 0) {
+    // SPLIT: the work item's planes of the partial outputs.
+    float* const lse_out = SPLIT ? a.lse + split * a.split_lse_stride : a.lse;
+    void* const o_out = SPLIT ? static_cast<void*>(static_cast<float*>(a.o) + split * a.split_o_stride)
+                              : a.o;
+    if (lse_out != nullptr && q_ok && hi == 0) {
       // log2-sum-exp of s c is m_run + log2(l); the natural one of s scale is
       // that times ln 2.
       const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
-      a.lse[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
+      lse_out[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
     }
     // A rejected prefix page makes the rows NaN (the key set is unknown).
     const float inv =
@@ -729,7 +752,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
           const int d0 = 32 * db + 8 * g + 4 * hi;
           if constexpr (OF32) {
             const f32x4 out = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + row + d0) = out;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + row + d0) = out;
           } else {
             u32x2 out;
             if constexpr (BF16) {
@@ -739,7 +762,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
               out[0] = pack_f16(v4[0] * inv, v4[1] * inv);
               out[1] = pack_f16(v4[2] * inv, v4[3] * inv);
             }
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + row + d0) = out;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o_out) + row + d0) = out;
           }
         }
     }
@@ -804,6 +827,120 @@ hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const Pre
                           int B, hipStream_t s) {
   if (D == 128) return launch_o<128>(bf16, causal, out_f32, a, B, s);
   if (D == 64) return launch_o<64>(bf16, causal, out_f32, a, B, s);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+// Merge of the split-KV partials: for each query row (b, h, i), the mean of
+// the splits' normalised partial rows weighted by exp(lse_s - max lse); a
+// row no split saw (every lse_s = -inf) gets O = 0.  Eight rows per 64-lane
+// workgroup, eight lanes per row, each lane D/8 consecutive outputs.
+template <int D, bool BF16, bool OF32>
+__global__ __launch_bounds__(64) void prefill_split_combine_kernel(PrefillArgs a, int B,
+                                                                   const float* part_o,
+                                                                   const float* part_lse) {
+  constexpr int E = D / 8;  // outputs per lane
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int lane = threadIdx.x;
+  const int k = lane & 7;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (lane >> 3);
+  if (row >= (int64_t)B * a.H * a.Sq) return;  // whole 8-lane groups leave together
+  const int qi = (int)(row % a.Sq);
+  const int64_t bh = row / a.Sq;
+  const int h = (int)(bh % a.H);
+  const int64_t b = bh / a.H;
+  const int64_t off = b * a.q_sb + h * a.q_sh + (int64_t)qi * a.q_ss + k * E;
+  float m = kNegInf;
+  for (int sp = 0; sp < a.n_splits; ++sp) m = fmaxf(m, part_lse[sp * a.split_lse_stride + row]);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != kNegInf) {
+    for (int sp = 0; sp < a.n_splits; ++sp) {
+      const float w =
+          __builtin_amdgcn_exp2f((part_lse[sp * a.split_lse_stride + row] - m) * kLog2e);
+      const f32x4* src = reinterpret_cast<const f32x4*>(part_o + sp * a.split_o_stride + off);
+      wsum += w;
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        const f32x4 x = src[c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * c + j] = __builtin_fmaf(w, x[j], acc[4 * c + j]);
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if constexpr (OF32) {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + off);
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c)
+      dst[c] = (f32x4){acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv,
+                       acc[4 * c + 3] * inv};
+  } else {
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + off);
+#pragma unroll
+    for (int c = 0; c < E / 8; ++c) {
+      u32x4 w4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = acc[8 * c + 2 * j] * inv, x1 = acc[8 * c + 2 * j + 1] * inv;
+        w4[j] = BF16 ? pack_bf16(x0, x1) : pack_f16(x0, x1);
+      }
+      dst[c] = w4;
+    }
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_split_t(const PrefillArgs& a, int B, float* part_o, float* part_lse,
+                          bool out_f32, hipStream_t s) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int BN = 64;
+  constexpr int RPW = 32 * NW;
+  const int64_t n_mtiles = (a.Sq + RPW - 1) / RPW;
+  const int64_t total = (int64_t)B * a.H * n_mtiles * a.n_splits;
+  const int64_t rows = (int64_t)B * a.H * a.Sq;
+  if (total >= ((int64_t)1 << 31) || (rows + 7) / 8 >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  PrefillArgs p = a;
+  p.o = part_o;
+  p.lse = part_lse;
+  p.n_mtiles = (int)n_mtiles;
+  p.pair_tiles = 0;
+  p.total_tiles = (int)total;
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, true, NW, BN, false, false, 1, true>),
+                     dim3(p.total_tiles), dim3(64 * NW), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((rows + 7) / 8));
+  if (out_f32)
+    hipLaunchKernelGGL((prefill_split_combine_kernel<D, BF16, true>), grid, dim3(64), 0, s, a, B,
+                       part_o, part_lse);
+  else
+    hipLaunchKernelGGL((prefill_split_combine_kernel<D, BF16, false>), grid, dim3(64), 0, s, a,
+                       B, part_o, part_lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_d(bool bf16, bool causal, bool out_f32, const PrefillArgs& a, int B,
+                          float* part_o, float* part_lse, hipStream_t s) {
+  if (bf16)
+    return causal ? launch_split_t<D, true, true>(a, B, part_o, part_lse, out_f32, s)
+                  : launch_split_t<D, true, false>(a, B, part_o, part_lse, out_f32, s);
+  return causal ? launch_split_t<D, false, true>(a, B, part_o, part_lse, out_f32, s)
+                : launch_split_t<D, false, false>(a, B, part_o, part_lse, out_f32, s);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_splitkv(int D, bool bf16, bool causal, bool out_f32,
+                                  const PrefillArgs& a, int B, float* part_o, float* part_lse,
+                                  hipStream_t s) {
+  if (D == 128) return launch_split_d<128>(bf16, causal, out_f32, a, B, part_o, part_lse, s);
+  if (D == 64) return launch_split_d<64>(bf16, causal, out_f32, a, B, part_o, part_lse, s);
   return hipErrorInvalidValue;
 }
 

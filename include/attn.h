@@ -118,6 +118,41 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int H_kv, int Sq, int Skv, int D, int layout, int dtype,
                      int causal, float scale, hipStream_t stream);
 
+/*
+ * attn_prefill_gqa for grids too small to fill the GPU (few query tiles
+ * against many keys: chunked prefill, a short query block over a long
+ * context): the keys of each query tile are split across workgroups, each
+ * writing a partial output and log-sum-exp into the workspace, and a second
+ * kernel merges them by log-sum-exp (flash decoding applied to prefill:
+ * "Wave February 2025 Release", FlashDecoding list; the KV split sized to
+ * fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950", Changes /
+ * Host side).  The split count comes from sizes only
+ * (attn_prefill_splitkv_num_splits); with one split (the grid already holds
+ * two workgroups per CU, or fewer than 1024 keys) this is attn_prefill_gqa,
+ * needs no workspace and gives its result bitwise.  Otherwise the result is
+ * attn_prefill_gqa's up to the rounding of the merge (the partials are fp32;
+ * each split's P is rounded to fp16 as in attn_prefill).
+ *
+ *   workspace: device scratch of at least attn_prefill_splitkv_workspace_size
+ *       bytes (0: may be NULL), 16-byte aligned, owned by the caller; its
+ *       contents need no initialisation.  ATTN_E_WORKSPACE if missing or small.
+ * Every other argument and error as in attn_prefill_gqa.
+ */
+int attn_prefill_splitkv(const void* q, const void* k, const void* v, void* o,
+                         int B, int H, int H_kv, int Sq, int Skv, int D, int layout,
+                         int dtype, int causal, float scale, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Key splits per query tile attn_prefill_splitkv uses for these sizes (1: no
+ * split; 0 for invalid sizes): at most enough for two workgroups per CU on
+ * 256 CUs, each split at least 512 keys. */
+int attn_prefill_splitkv_num_splits(int B, int H, int Sq, int Skv, int D);
+
+/* Workspace bytes of attn_prefill_splitkv (0 when it does not split): per
+ * split, fp32 partial outputs [B*H*Sq*D] and log-sum-exps [B*H*Sq], each
+ * array padded to 256 bytes. */
+size_t attn_prefill_splitkv_workspace_size(int B, int H, int Sq, int Skv, int D);
+
 /* Workspace bytes of attn_prefill_bwd: two fp32 per query row (delta =
  * rowsum(dO * O) and -LSE log2(e)), each array padded to 256 bytes. */
 size_t attn_prefill_bwd_workspace_size(int B, int H, int Sq);

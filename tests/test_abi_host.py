@@ -30,7 +30,9 @@ def test_header_declares_the_boundary():
                             "attn_paged_decode_gqa_num_splits", "attn_extend",
                             "attn_prefill_fp8", "attn_prefill_lse", "attn_prefill_bwd",
                             "attn_prefill_bwd_workspace_size",
-                            "attn_paged_decode_gqa_noalloc"])
+                            "attn_paged_decode_gqa_noalloc", "attn_prefill_splitkv",
+                            "attn_prefill_splitkv_num_splits",
+                            "attn_prefill_splitkv_workspace_size"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -397,3 +399,52 @@ def test_decode_noalloc_limit_matches_workspace_size():
         assert 0 < attn.attn_paged_decode_gqa_workspace_size(B, H, H_kv, 128, mp, 16) <= cap
     big = attn.attn_paged_decode_gqa_workspace_size(4096, 32, 32, 128, 512, 16)
     assert big > cap
+
+
+def _splitkv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=8, H_kv=8, Sq=128, Skv=32768, D=128,
+             layout=0, dtype=0, causal=0, scale=0.1, workspace=FAKE, workspace_bytes=1 << 40,
+             stream=0)
+    a.update(kw)
+    return attn.attn_prefill_splitkv(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(layout=2), attn.ATTN_E_INVALID),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+    (dict(scale=-1.0), attn.ATTN_E_INVALID),
+    (dict(q=None), attn.ATTN_E_INVALID),
+    (dict(o=FAKE + 4), attn.ATTN_E_INVALID),
+    # this shape splits: a workspace is required, big enough, 16-byte aligned
+    (dict(workspace=None), attn.ATTN_E_WORKSPACE),
+    (dict(workspace_bytes=1024), attn.ATTN_E_WORKSPACE),
+    (dict(workspace=FAKE + 8), attn.ATTN_E_INVALID),
+])
+def test_prefill_splitkv_validation(kw, status):
+    assert _splitkv(**kw) == status
+
+
+def test_prefill_splitkv_empty_is_a_noop():
+    assert _splitkv(Sq=0, q=None, o=None, workspace=None, workspace_bytes=0) == attn.ATTN_OK
+
+
+def test_prefill_splitkv_plan_and_workspace():
+    # 8 heads x 1 query tile = 8 workgroups: split until two per CU (64
+    # splits), each split at least 8 key tiles (512 keys): 512 tiles -> 64
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 32768, 128) == 64
+    rows = 1 * 8 * 128
+    assert attn.attn_prefill_splitkv_workspace_size(1, 8, 128, 32768, 128) == \
+        64 * (rows * 128 * 4 + rows * 4)
+    # keys too few to split twice (under 16 key tiles): no split, no workspace
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 960, 128) == 1
+    assert attn.attn_prefill_splitkv_workspace_size(1, 8, 128, 960, 128) == 0
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 1000, 128) == 2
+    # a grid of two workgroups per CU already: no split
+    assert attn.attn_prefill_splitkv_num_splits(4, 32, 4096, 4096, 128) == 1
+    # splits limited by the keys: 20 tiles -> 2 splits of 10
+    assert attn.attn_prefill_splitkv_num_splits(1, 1, 64, 1280, 64) == 2
+    # D = 64 tiles hold 128 query rows
+    assert attn.attn_prefill_splitkv_num_splits(1, 32, 256, 65536, 64) == 8
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 32768, 80) == 0
+    assert attn.attn_prefill_splitkv_workspace_size(-1, 8, 128, 32768, 128) == 0
