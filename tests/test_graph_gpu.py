@@ -57,8 +57,8 @@ def test_graph_capture_and_replay(gpu_lib):
 
 def test_graph_capture_backward_extend_fp8(gpu_lib):
     """The other entry points in one captured graph: forward with LSE,
-    backward, extend after a paged prefix, fp8 prefill and grouped-query
-    decode, replayed three times against the eager results."""
+    backward, extend after a paged prefix, fp8 prefill, grouped-query decode
+    and split-KV prefill, replayed three times against the eager results."""
     attn = gpu_lib
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev) for t in workloads.backward_inputs(1, 8, 200, 260, 128, "bf16",
@@ -83,7 +83,13 @@ def test_graph_capture_backward_extend_fp8(gpu_lib):
                                                                 16),
                       dtype=torch.uint8, device=dev)
     o_dec = torch.empty_like(gd["q"])
-    outs = (o, lse, dq, dk, dv, o_ext, o8, o_dec)
+    qs, ks, vs = (t.to(dev) for t in workloads.prefill_inputs(1, 4, 100, 3000, 128, "f16",
+                                                              "BHSD", seed=37, h_kv=2))
+    assert attn.attn_prefill_splitkv_num_splits(1, 4, 100, 3000, 128) > 1
+    sws = torch.empty(attn.attn_prefill_splitkv_workspace_size(1, 4, 100, 3000, 128),
+                      dtype=torch.uint8, device=dev)
+    o_split = torch.empty_like(qs)
+    outs = (o, lse, dq, dk, dv, o_ext, o8, o_dec, o_split)
 
     def work(stream=None):
         attn.prefill_with_lse(q, k, v, causal=True, layout="BSHD", out=o, lse=lse, stream=stream)
@@ -95,8 +101,9 @@ def test_graph_capture_backward_extend_fp8(gpu_lib):
         attn.prefill_fp8(q8, k8, v8, desc, causal=True, out=o8, stream=stream)
         attn.paged_decode(gd["q"], gd["k_cache"], gd["v_cache"], gd["page_table"],
                           gd["seq_lens"], out=o_dec, workspace=dws, stream=stream)
+        attn.prefill_splitkv(qs, ks, vs, causal=True, out=o_split, workspace=sws, stream=stream)
 
-    print("[case] graph capture of lse/backward/extend/fp8/gqa decode", flush=True)
+    print("[case] graph capture of lse/backward/extend/fp8/gqa decode/split-kv", flush=True)
     work()
     torch.cuda.synchronize()
     refs = [t.clone() for t in outs]
