@@ -115,3 +115,21 @@ def test_backward_stays_in_bounds(gpu_lib, layout, causal):
     torch.cuda.synchronize()
     assert bool((bw[:GUARD_BYTES] == SENTINEL).all()) and \
         bool((bw[bw.numel() - GUARD_BYTES:] == SENTINEL).all()), "workspace overrun"
+
+
+@pytest.mark.parametrize("layout,causal", [("BHSD", False), ("BSHD", True)])
+def test_prefill_splitkv_stays_in_bounds(gpu_lib, layout, causal):
+    attn = gpu_lib
+    B, H, H_kv, Sq, Skv, D = 1, 4, 2, 77, 2100, 128
+    q, k, v = workloads.prefill_inputs(B, H, Sq, Skv, D, "bf16", layout, seed=97, h_kv=H_kv)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    assert attn.attn_prefill_splitkv_num_splits(B, H, Sq, Skv, D) > 1
+    print(f"[case] guard split-kv prefill {layout} causal={causal}", flush=True)
+    buf, o = _guarded(tuple(q.shape), torch.bfloat16)
+    need = attn.attn_prefill_splitkv_workspace_size(B, H, Sq, Skv, D)
+    wbuf, ws = _guarded((need,), torch.uint8)
+    attn.prefill_splitkv(qg, kg, vg, causal=causal, layout=layout, out=o, workspace=ws)
+    _check(buf, o, "split-kv o")
+    torch.cuda.synchronize()
+    assert bool((wbuf[:GUARD_BYTES] == SENTINEL).all()) and \
+        bool((wbuf[wbuf.numel() - GUARD_BYTES:] == SENTINEL).all()), "workspace overrun"
