@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11,12]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11,12,13]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -10,8 +10,9 @@ Sq=Skv=4096 D=128 fp16 BHSD non-causal, with inputs resident in HBM.  The
 headline `value` is its throughput in TFLOP/s (4*B*H*Sq*Skv*D flops per
 step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
-multi-query paged decode, extend after a paged prefix, fp8 prefill, and the
-backward of the causal 8k workload with and without grouped KV heads) are measured the same way and reported
+multi-query paged decode, extend after a paged prefix, fp8 prefill, the
+backward of the causal 8k workload with and without grouped KV heads, and a
+512-token chunk against 32k keys through the split-KV prefill) are measured the same way and reported
 under "extra", decode in GB/s of algorithmic K/V bytes, the backward in
 TFLOP/s of its five products (2.5x the forward's flops).
 
@@ -52,8 +53,18 @@ BACKWARD_SRC = os.path.join(ROOT, "attention_flash_attn_prefill_amd", "csrc", "b
 
 
 def prefill_flops(m):
+    """4 B H D per visible (query, key) pair: all Sq x Skv pairs, or for causal
+    attention half of them when Sq = Skv (the diagonal overcount ignored), and
+    the exact count under the bottom-right mask when Sq != Skv."""
     full = 4.0 * m["B"] * m["H"] * m["Sq"] * m["Skv"] * m["D"]
-    return full / 2 if m["causal"] else full
+    if not m["causal"]:
+        return full
+    if m["Sq"] == m["Skv"]:
+        return full / 2
+    Sq, Skv = m["Sq"], m["Skv"]
+    off = Skv - Sq
+    visible = sum(min(Skv, max(0, i + 1 + off)) for i in range(Sq))
+    return 4.0 * m["B"] * m["H"] * m["D"] * visible
 
 
 def source_hash(path):
@@ -283,6 +294,14 @@ def bench_prefill(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
         def step():
             attn.prefill_fp8(q, k, v, m["descales"], causal=m["causal"], scale=m["scale"],
                              layout=m["layout"], out=o, stream=stream)
+    elif m.get("splitkv"):
+        o = torch.empty_like(q)
+        need = attn.attn_prefill_splitkv_workspace_size(m["B"], m["H"], m["Sq"], m["Skv"], m["D"])
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+        def step():
+            attn.prefill_splitkv(q, k, v, causal=m["causal"], scale=m["scale"],
+                                 layout=m["layout"], out=o, workspace=ws, stream=stream)
     else:
         o = torch.empty_like(q)
 
@@ -304,6 +323,10 @@ def bench_prefill(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     cfg_out = {"workload": m["name"], "B": m["B"], "H": m["H"], "H_kv": m["H_kv"],
                "Sq": m["Sq"], "Skv": m["Skv"],
                "D": m["D"], "layout": m["layout"], "causal": m["causal"], "dtype": m["dtype"]}
+    if m.get("splitkv"):
+        cfg_out["entry_point"] = "attn_prefill_splitkv"
+        cfg_out["key_splits"] = attn.attn_prefill_splitkv_num_splits(m["B"], m["H"], m["Sq"],
+                                                                     m["Skv"], m["D"])
     traffic = load_traffic(f"prefill_fwd__{m['name']}", PREFILL_SRC)
     # fp8: the Q.K^T half of the flops runs on the fp8 MFMA (5.0 PFLOP/s), the
     # P.V half on fp16 (2.5): the peak for the mix is their harmonic blend.
@@ -660,7 +683,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11,12",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11,12,13",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")

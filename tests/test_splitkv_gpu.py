@@ -76,3 +76,28 @@ def test_splitkv_without_split_is_prefill(gpu_lib, layout, causal):
     b = attn.prefill(qg, kg, vg, causal=causal, layout=layout)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(900)
+def test_splitkv_chunk_workload_whole(gpu_lib, progress):
+    """The benchmark's chunked-prefill workload (B1 H32/8, a 512-token chunk
+    against 32k keys, bottom-right causal, bf16 BSHD) in its launch
+    configuration, compared with the oracle over the whole output
+    (NaN-prefilled)."""
+    import whole_tensor as whole
+    attn = gpu_lib
+    q, k, v, m = workloads.prefill_config(13)
+    assert attn.attn_prefill_splitkv_num_splits(m["B"], m["H"], m["Sq"], m["Skv"], m["D"]) > 1
+    print(f"[case] split-kv prefill {m['name']} whole tensor", flush=True)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    kw = dict(causal=m["causal"], scale=m["scale"], layout=m["layout"])
+    o = attn.prefill_splitkv(qg, kg, vg, out=whole.nan_like(qg), **kw)
+    torch.cuda.synchronize()
+    outs = {"o": o.cpu()}
+    del qg, kg, vg
+    stats = whole.compare(whole.prefill_units(q, k, v, list(outs), **kw), outs,
+                          progress=progress)
+    st = stats["o"]
+    print(f"[parity] {m['name']} (whole tensor): {st}", flush=True)
+    assert st.nonfinite == 0, f"{st.nonfinite} elements not written (or not finite)"
+    assert st.max_abs <= 1e-2 and st.rel_fro <= 2e-3, st

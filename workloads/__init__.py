@@ -51,6 +51,11 @@ PREFILL_CONFIGS = {
     # FP8 (e4m3fn, per-tensor descales) inputs in the headline shape; O in fp16.
     10: dict(name="fp8-llama2-13b-prefill", B=4, H=40, Sq=4096, Skv=4096, D=128, dtype="fp8",
              layout="BHSD", causal=False, amp=1.0, scale=None, out_dtype="f16"),
+    # One 512-token chunk of a long prompt against its 32k keys so far
+    # (bottom-right causal), run through the split-KV prefill: 64 workgroups
+    # unsplit, too few for 256 CUs.
+    13: dict(name="chunk-prefill-512-at-32k", B=1, H=32, H_kv=8, Sq=512, Skv=32768, D=128,
+             dtype="bf16", layout="BSHD", causal=True, amp=1.0, scale=None, splitkv=True),
 }
 
 # Backward workloads: the gradients of the causal 8k BSHD prefill (a training
