@@ -210,10 +210,24 @@ int prepare_prefill(const void* q, const void* k, const void* v, void* o, float*
   return ATTN_OK;
 }
 
-// Split-KV plan of attn_prefill_splitkv, from sizes only: split the keys of
-// each query tile when the grid (one workgroup per head and 256-row query
-// tile; 128 rows for D = 64) would hold fewer than two workgroups per CU, into
-// at most enough ranges for two per CU, each at least 8 key tiles (512 keys).
+// Split-KV plan of attn_prefill_splitkv, from sizes only.  Work items are
+// (batch, head, query tile of 256 rows; 128 for D = 64); each item's keys
+// are cut into n ranges of `split_tiles` 64-key tiles, at least 8 tiles
+// (512 keys) each.  A split is considered only when the plain grid holds fewer
+// than two workgroups per CU (above that the plain causal grid pairs its
+// tiles) and there are at least 16 key tiles.  The plan takes the n with the
+// least modelled time, the smallest n on a tie.  The model, fitted to
+// measured split and plain prefill times:
+//   * the split kernel takes as long as its busiest CU, which holds w =
+//     ceil(items * n / 256) workgroups (run one after another at D = 128,
+//     where one workgroup of 8 waves fills a CU; up to three at a time at
+//     D = 64, 4 waves each); each costs its key tiles at the per-CU tile time
+//     (D = 128: 2.1 us; D = 64: 0.8 us with three workgroups resident, 4.5%
+//     more with two, 22% more with one) plus, at D = 64, ~3 us of its own
+//     (Q loads, the epilogue);
+//   * for n > 1, every split's fp32 partials (O and LSE of each query row,
+//     written by the split kernel and read back by the combine) at 5.5 TB/s,
+//     plus the combine's launch (~5 us).
 struct SplitKvPlan {
   int n_splits, split_tiles;
 };
@@ -222,12 +236,36 @@ SplitKvPlan plan_prefill_splitkv(int B, int H, int Sq, int Skv, int D) {
   const int64_t rows = D == 128 ? 256 : 128;
   const int64_t items = (int64_t)B * H * ((Sq + rows - 1) / rows);
   const int64_t n_kt = ((int64_t)Skv + 63) / 64;
-  if (items <= 0 || items >= 2 * kNumCUs || n_kt < 2 * kMinSplitTiles)
-    return SplitKvPlan{1, (int)n_kt};
-  const int64_t want = (2 * kNumCUs + items - 1) / items;
-  const int64_t n = want < n_kt / kMinSplitTiles ? want : n_kt / kMinSplitTiles;
-  const int64_t tiles = (n_kt + n - 1) / n;
-  return SplitKvPlan{(int)((n_kt + tiles - 1) / tiles), (int)tiles};
+  const SplitKvPlan none{1, (int)n_kt};
+  if (items <= 0 || items >= 2 * kNumCUs || n_kt < 2 * kMinSplitTiles) return none;
+  const double split_us = (double)B * H * Sq * (D + 1) * 8 / 5.5e6;
+  constexpr double kCombineUs = 5.0;
+  auto cost = [&](int64_t n, int64_t tiles) {
+    const int64_t w = (items * n + kNumCUs - 1) / kNumCUs;
+    double per_wg;
+    if (D == 128) {
+      per_wg = 2.1 * (double)tiles;
+    } else {
+      const double occ = w >= 3 ? 1.0 : (w == 2 ? 1.045 : 1.22);
+      per_wg = 0.8 * occ * (double)tiles + 3.0;
+    }
+    const double t = (double)w * per_wg;
+    return n > 1 ? t + (double)n * split_us + kCombineUs : t;
+  };
+  SplitKvPlan best = none;
+  double best_t = cost(1, n_kt);
+  const int64_t n_cap = 16 * kNumCUs;
+  const int64_t n_max = n_kt / kMinSplitTiles < n_cap ? n_kt / kMinSplitTiles : n_cap;
+  for (int64_t n = 2; n <= n_max; ++n) {
+    const int64_t tiles = (n_kt + n - 1) / n;
+    const int64_t ns = (n_kt + tiles - 1) / tiles;  // ranges actually used
+    const double t = cost(ns, tiles);
+    if (t < best_t) {
+      best_t = t;
+      best = SplitKvPlan{(int)ns, (int)tiles};
+    }
+  }
+  return best;
 }
 
 }  // namespace

@@ -128,7 +128,8 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float
  * fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950", Changes /
  * Host side).  The split count comes from sizes only
  * (attn_prefill_splitkv_num_splits); with one split (the grid already holds
- * two workgroups per CU, or fewer than 1024 keys) this is attn_prefill_gqa,
+ * two workgroups per CU, fewer than 1024 keys, or no split modelled faster)
+ * this is attn_prefill_gqa,
  * needs no workspace and gives its result bitwise.  Otherwise the result is
  * attn_prefill_gqa's up to the rounding of the merge (the partials are fp32;
  * each split's P is rounded to fp16 as in attn_prefill).
@@ -144,8 +145,11 @@ int attn_prefill_splitkv(const void* q, const void* k, const void* v, void* o,
                          size_t workspace_bytes, hipStream_t stream);
 
 /* Key splits per query tile attn_prefill_splitkv uses for these sizes (1: no
- * split; 0 for invalid sizes): at most enough for two workgroups per CU on
- * 256 CUs, each split at least 512 keys. */
+ * split; 0 for invalid sizes).  Each split covers at least 512 keys; the
+ * count is the one with the least modelled time on 256 CUs: the busiest CU's
+ * workgroups times one key range's tiles, plus the fp32 partials of every
+ * split at HBM rate.  Splits are considered only below two workgroups (query
+ * tiles x heads x batch) per CU. */
 int attn_prefill_splitkv_num_splits(int B, int H, int Sq, int Skv, int D);
 
 /* Workspace bytes of attn_prefill_splitkv (0 when it does not split): per

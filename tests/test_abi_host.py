@@ -430,12 +430,21 @@ def test_prefill_splitkv_empty_is_a_noop():
 
 
 def test_prefill_splitkv_plan_and_workspace():
-    # 8 heads x 1 query tile = 8 workgroups: split until two per CU (64
-    # splits), each split at least 8 key tiles (512 keys): 512 tiles -> 64
-    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 32768, 128) == 64
+    # 8 heads x 1 query tile = 8 workgroups over 512 key tiles: 32 splits of
+    # 16 tiles fill the 256 CUs once (64 would take two rounds of 8 tiles,
+    # the same time plus twice the partials)
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 32768, 128) == 32
     rows = 1 * 8 * 128
     assert attn.attn_prefill_splitkv_workspace_size(1, 8, 128, 32768, 128) == \
-        64 * (rows * 128 * 4 + rows * 4)
+        32 * (rows * 128 * 4 + rows * 4)
+    # a 512-query, 32-head chunk against 32k keys: 64 items x 4 splits = 256
+    assert attn.attn_prefill_splitkv_num_splits(1, 32, 512, 32768, 128) == 4
+    # 100 items: 5 splits (500 workgroups, two per CU) beat 2 (one round of
+    # 200, 78% of the CUs) and 3 (300: a second round of 44)
+    assert attn.attn_prefill_splitkv_num_splits(1, 25, 1024, 16384, 128) == 5
+    # 240 items nearly fill the CUs: no split is modelled faster than any
+    assert attn.attn_prefill_splitkv_num_splits(1, 40, 1536, 16384, 128) == 1
+    assert attn.attn_prefill_splitkv_workspace_size(1, 40, 1536, 16384, 128) == 0
     # keys too few to split twice (under 16 key tiles): no split, no workspace
     assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 960, 128) == 1
     assert attn.attn_prefill_splitkv_workspace_size(1, 8, 128, 960, 128) == 0
@@ -444,7 +453,11 @@ def test_prefill_splitkv_plan_and_workspace():
     assert attn.attn_prefill_splitkv_num_splits(4, 32, 4096, 4096, 128) == 1
     # splits limited by the keys: 20 tiles -> 2 splits of 10
     assert attn.attn_prefill_splitkv_num_splits(1, 1, 64, 1280, 64) == 2
-    # D = 64 tiles hold 128 query rows
-    assert attn.attn_prefill_splitkv_num_splits(1, 32, 256, 65536, 64) == 8
+    # D = 64 tiles hold 128 query rows and a CU holds three workgroups: 64
+    # items x 12 splits = 768
+    assert attn.attn_prefill_splitkv_num_splits(1, 32, 256, 65536, 64) == 12
+    # ... but with few key tiles per split the per-workgroup cost wins: two
+    # per CU (21 splits of 15 tiles), not three (32 of 10)
+    assert attn.attn_prefill_splitkv_num_splits(1, 8, 300, 20000, 64) == 21
     assert attn.attn_prefill_splitkv_num_splits(1, 8, 128, 32768, 80) == 0
     assert attn.attn_prefill_splitkv_workspace_size(-1, 8, 128, 32768, 128) == 0
