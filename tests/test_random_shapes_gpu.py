@@ -1,5 +1,6 @@
 """A seeded sweep of random shapes through prefill (with and without the LSE
-output), grouped-query decode, extend, the backward and fp8 prefill (with
+output), split-KV prefill, grouped-query decode, extend, the backward and
+fp8 prefill (with
 the output in the input type or, in some draws, in fp32), each
 against the fp64 oracle at its bar.  The draws mix batch, head counts and
 grouping, lengths on and off tile boundaries (including Sq > Skv under the
@@ -54,6 +55,35 @@ def test_prefill_random(gpu_lib, i):
         fin = np.isfinite(want)
         assert np.array_equal(fin, np.isfinite(got))
         assert np.all(np.abs(got[fin] - want[fin]) <= 1e-3 + 1e-6 * np.abs(want[fin]))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_prefill_splitkv_random(gpu_lib, i):
+    """Split-KV prefill on random small grids over 1k-9k keys (so that the
+    plan splits), written into NaN-filled output and workspace."""
+    r = np.random.default_rng(5000 + i)
+    H_kv = int(r.choice([1, 2]))
+    c = dict(B=int(r.integers(1, 3)), H=H_kv * int(r.integers(1, 5)), H_kv=H_kv,
+             Sq=int(r.integers(1, 400)), Skv=int(r.integers(1024, 9000)),
+             D=int(r.choice([64, 128])), dtype=str(r.choice(["f16", "bf16"])),
+             layout=str(r.choice(["BHSD", "BSHD"])), causal=bool(r.integers(0, 2)),
+             scale=float(r.uniform(0.02, 0.3)), out32=bool(r.integers(0, 4) == 0))
+    n = gpu_lib.attn_prefill_splitkv_num_splits(c["B"], c["H"], c["Sq"], c["Skv"], c["D"])
+    print(f"[case] splitkv random {i}: {c} splits {n}", flush=True)
+    assert n > 1
+    q, k, v = workloads.prefill_inputs(c["B"], c["H"], c["Sq"], c["Skv"], c["D"], c["dtype"],
+                                       c["layout"], seed=6000 + i, h_kv=c["H_kv"])
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    odt = torch.float32 if c["out32"] else q.dtype
+    out = torch.full(tuple(q.shape), float("nan"), dtype=odt, device="cuda")
+    need = gpu_lib.attn_prefill_splitkv_workspace_size(c["B"], c["H"], c["Sq"], c["Skv"], c["D"])
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
+    o = gpu_lib.prefill_splitkv(qg, kg, vg, causal=c["causal"], scale=c["scale"],
+                                layout=c["layout"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    ref = oracle.sdpa(q, k, v, causal=c["causal"], scale=c["scale"], layout=c["layout"])
+    assert_parity(o.double().cpu().numpy(), ref, f"splitkv random {i}")
 
 
 @pytest.mark.parametrize("i", range(18))
