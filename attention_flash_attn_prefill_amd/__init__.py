@@ -9,9 +9,10 @@ Low-level functions carry the C names (``attn_prefill``,
 ``attn_prefill_gqa``, ``attn_prefill_lse``, ``attn_prefill_splitkv``,
 ``attn_prefill_bwd``, ``attn_paged_decode``, ``attn_paged_decode_gqa``, their
 workspace-size and split-plan queries, ``attn_prefill_fp8``, ``attn_extend``,
-``attn_status_string``) and take tensors or raw integer pointers;
-``prefill``, ``prefill_with_lse``, ``prefill_splitkv``, ``prefill_backward``,
-``prefill_fp8``, ``paged_decode`` and ``extend`` are conveniences that derive
+``attn_extend_splitkv``, ``attn_status_string``) and take tensors or raw
+integer pointers; ``prefill``, ``prefill_with_lse``, ``prefill_splitkv``,
+``prefill_backward``, ``prefill_fp8``, ``paged_decode``, ``extend`` and
+``extend_splitkv`` are conveniences that derive
 the sizes (including the number of KV heads) from tensor shapes and allocate
 the output.
 """
@@ -57,6 +58,10 @@ SIGNATURES = {
                                   _VP, _SZ, _VP]),
     "attn_prefill_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_prefill_splitkv_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "attn_extend_splitkv": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I,
+                                 _I, _I, _I, _I, _I, _F, _VP, _SZ, _VP]),
+    "attn_extend_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_extend_splitkv_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_prefill_bwd_workspace_size": (_SZ, [_I, _I, _I]),
     "attn_prefill_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I,
                               _I, _I, _I, _F, _VP, _SZ, _VP]),
@@ -225,6 +230,30 @@ def attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o,
         _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         _ptr(prefix_lens), _ptr(qo_start), _ptr(o), B, H, H_kv, D, total_tokens, max_extend_len,
         page_size, num_pages, max_pages_per_seq, dtype, float(scale), _stream(stream))
+
+
+def attn_extend_splitkv(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H,
+                        H_kv, D, total_tokens, max_extend_len, page_size, num_pages,
+                        max_pages_per_seq, dtype, scale, workspace, workspace_bytes,
+                        stream=None) -> int:
+    """Direct call of the C entry point; returns its status code."""
+    return load_library().attn_extend_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        _ptr(prefix_lens), _ptr(qo_start), _ptr(o), B, H, H_kv, D, total_tokens, max_extend_len,
+        page_size, num_pages, max_pages_per_seq, dtype, float(scale), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+
+
+def attn_extend_splitkv_num_splits(B, H, H_kv, D, total_tokens, max_extend_len,
+                                   max_pages_per_seq) -> int:
+    return int(load_library().attn_extend_splitkv_num_splits(B, H, H_kv, D, total_tokens,
+                                                             max_extend_len, max_pages_per_seq))
+
+
+def attn_extend_splitkv_workspace_size(B, H, H_kv, D, total_tokens, max_extend_len,
+                                       max_pages_per_seq) -> int:
+    return int(load_library().attn_extend_splitkv_workspace_size(
+        B, H, H_kv, D, total_tokens, max_extend_len, max_pages_per_seq))
 
 
 def attn_paged_decode_workspace_size(B, H, D, max_pages_per_seq, page_size) -> int:
@@ -444,15 +473,9 @@ def paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale=None, out=N
     return o
 
 
-def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *, max_extend_len=None,
-           scale=None, out=None, out_dtype=None, stream=None):
-    """Extend attention: new tokens (q [T,H,D], k, v [T,H_kv,D], packed by
-    qo_start [B+1]) after cached prefixes (k_cache, v_cache [P,16,H_kv,D],
-    page_table [B,max_pages], prefix_lens [B]); see attn_extend in attn.h.
-
-    max_extend_len bounds every sequence's new-token count; if omitted it is
-    read from qo_start, which synchronises with the device.
-    """
+def _extend_args(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, max_extend_len,
+                 scale, out, out_dtype):
+    """Checks of extend's tensors; returns (o, sizes...) for the C call."""
     import torch
     T, H, D = q.shape
     H_kv = k.shape[1]
@@ -480,9 +503,43 @@ def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *, max_
     o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
     if o.shape != q.shape or not o.is_cuda or not o.is_contiguous():
         raise ValueError("out must be a contiguous GPU tensor shaped like q")
-    _check(attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, B, H,
-                       H_kv, D, T, max_extend_len, page_size, num_pages, page_table.shape[1],
-                       code, scale, stream), "attn_extend")
+    return o, (B, H, H_kv, D, T, max_extend_len, page_size, num_pages, page_table.shape[1],
+               code, scale)
+
+
+def extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *, max_extend_len=None,
+           scale=None, out=None, out_dtype=None, stream=None):
+    """Extend attention: new tokens (q [T,H,D], k, v [T,H_kv,D], packed by
+    qo_start [B+1]) after cached prefixes (k_cache, v_cache [P,16,H_kv,D],
+    page_table [B,max_pages], prefix_lens [B]); see attn_extend in attn.h.
+
+    max_extend_len bounds every sequence's new-token count; if omitted it is
+    read from qo_start, which synchronises with the device.
+    """
+    o, a = _extend_args(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start,
+                        max_extend_len, scale, out, out_dtype)
+    _check(attn_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o, *a,
+                       stream), "attn_extend")
+    return o
+
+
+def extend_splitkv(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, *,
+                   max_extend_len=None, scale=None, out=None, out_dtype=None, workspace=None,
+                   stream=None):
+    """``extend`` with each unit's keys split over workgroups when the grid is
+    too small to fill the GPU (see attn_extend_splitkv in attn.h).
+    `workspace` (a uint8 GPU tensor of at least
+    attn_extend_splitkv_workspace_size bytes) is allocated when not given."""
+    import torch
+    o, a = _extend_args(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start,
+                        max_extend_len, scale, out, out_dtype)
+    B, H, H_kv, D, T, mx, _, _, max_pages = a[:9]
+    need = attn_extend_splitkv_workspace_size(B, H, H_kv, D, T, mx, max_pages)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(attn_extend_splitkv(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o,
+                               *a, workspace, nbytes, stream), "attn_extend_splitkv")
     return o
 
 

@@ -210,8 +210,9 @@ int prepare_prefill(const void* q, const void* k, const void* v, void* o, float*
   return ATTN_OK;
 }
 
-// Split-KV plan of attn_prefill_splitkv, from sizes only.  Work items are
-// (batch, head, query tile of 256 rows; 128 for D = 64); each item's keys
+// Split-KV plans of attn_prefill_splitkv and attn_extend_splitkv, from sizes
+// only.  Work items are the plain grid's workgroups (prefill: batch, head,
+// query tile of 256 rows, 128 for D = 64; extend: below); each item's keys
 // are cut into n ranges of `split_tiles` 64-key tiles, at least 8 tiles
 // (512 keys) each.  A split is considered only when the plain grid holds fewer
 // than two workgroups per CU (above that the plain causal grid pairs its
@@ -231,14 +232,13 @@ int prepare_prefill(const void* q, const void* k, const void* v, void* o, float*
 struct SplitKvPlan {
   int n_splits, split_tiles;
 };
-SplitKvPlan plan_prefill_splitkv(int B, int H, int Sq, int Skv, int D) {
+// The model over items work items of n_kt key tiles each, rows_total query
+// rows (times heads) of partials per split.
+SplitKvPlan plan_splits_modelled(int64_t items, int64_t n_kt, double rows_total, int D) {
   constexpr int64_t kMinSplitTiles = 8;
-  const int64_t rows = D == 128 ? 256 : 128;
-  const int64_t items = (int64_t)B * H * ((Sq + rows - 1) / rows);
-  const int64_t n_kt = ((int64_t)Skv + 63) / 64;
   const SplitKvPlan none{1, (int)n_kt};
   if (items <= 0 || items >= 2 * kNumCUs || n_kt < 2 * kMinSplitTiles) return none;
-  const double split_us = (double)B * H * Sq * (D + 1) * 8 / 5.5e6;
+  const double split_us = rows_total * (D + 1) * 8 / 5.5e6;
   constexpr double kCombineUs = 5.0;
   auto cost = [&](int64_t n, int64_t tiles) {
     const int64_t w = (items * n + kNumCUs - 1) / kNumCUs;
@@ -268,7 +268,98 @@ SplitKvPlan plan_prefill_splitkv(int B, int H, int Sq, int Skv, int D) {
   return best;
 }
 
+SplitKvPlan plan_prefill_splitkv(int B, int H, int Sq, int Skv, int D) {
+  const int64_t rows = D == 128 ? 256 : 128;
+  const int64_t items = (int64_t)B * H * ((Sq + rows - 1) / rows);
+  return plan_splits_modelled(items, ((int64_t)Skv + 63) / 64, (double)B * H * Sq, D);
+}
+
+// Split-KV extend: units (sequence, KV head, head group, query tile) as in
+// attn_extend's grid, sized from the bounds max_extend_len and the prefix
+// capacity max_pages_per_seq * 16 (a unit walks its prefix tiles, then its
+// new tokens' tiles); the partials cover total_tokens rows of every head.
+SplitKvPlan plan_extend_splitkv(int B, int H, int H_kv, int D, int total_tokens,
+                                int max_extend_len, int max_pages_per_seq) {
+  const int hpw = (H / H_kv) % 4 == 0 ? 4 : 1;
+  const int64_t rpw = (D == 128 ? 256 : 128) / hpw;
+  const int64_t items = (int64_t)B * (H / hpw) * ((max_extend_len + rpw - 1) / rpw);
+  const int64_t n_kt = ((int64_t)max_pages_per_seq * kDecodePageSize + 63) / 64 +
+                       ((int64_t)max_extend_len + 63) / 64;
+  return plan_splits_modelled(items, n_kt, (double)total_tokens * H, D);
+}
+
 }  // namespace
+
+// Argument checks and kernel arguments of attn_extend (shared with
+// attn_extend_splitkv).  *run is false when there is nothing to compute.
+static int prepare_extend(const void* q, const void* k, const void* v, const void* k_cache,
+                          const void* v_cache, const int32_t* page_table,
+                          const int32_t* prefix_lens, const int32_t* qo_start, void* o, int B,
+                          int H, int H_kv, int D, int total_tokens, int max_extend_len,
+                          int page_size, int num_pages, int max_pages_per_seq, int dtype,
+                          float scale, PrefillArgs* out, bool* bf16_out, bool* out_f32_out,
+                          bool* run) {
+  *run = false;
+  if (B < 0 || H < 0 || H_kv < 0 || total_tokens < 0 || max_extend_len < 0 || num_pages < 0 ||
+      max_pages_per_seq < 0)
+    return ATTN_E_INVALID;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
+  bool bf16, out_f32;
+  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
+  if ((int64_t)B * H * max_extend_len == 0 || total_tokens == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !qo_start) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
+  if ((uintptr_t)qo_start & 3u) return ATTN_E_INVALID;
+  if (max_pages_per_seq > 0) {  // prefixes may exist: the cache must be there
+    if (num_pages == 0 || !k_cache || !v_cache || !page_table || !prefix_lens)
+      return ATTN_E_INVALID;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return ATTN_E_INVALID;
+    if (((uintptr_t)page_table & 3u) || ((uintptr_t)prefix_lens & 3u)) return ATTN_E_INVALID;
+  }
+  // Row offsets within a sequence's new tokens are 32-bit in the kernel, and
+  // so are key positions (prefix plus new tokens).
+  if ((int64_t)max_extend_len * H * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)max_pages_per_seq * kDecodePageSize + max_extend_len >= ((int64_t)1 << 31))
+    return ATTN_E_UNSUPPORTED;
+  if ((int64_t)kDecodePageSize * H_kv * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
+
+  PrefillArgs& a = *out;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.group = H / H_kv;
+  a.Sq = max_extend_len;  // bounds every sequence's new tokens; sets the grid
+  a.Skv = 0;
+  a.causal_off = 0;
+  a.n_mtiles = 0;
+  a.total_tiles = 0;
+  a.q_sb = 0; a.q_sh = D; a.q_ss = H * D;          // [T, H, D]
+  a.k_sb = 0; a.k_sh = D; a.k_ss = H_kv * D;       // [T, H_kv, D]
+  a.c = exp2_multiplier(scale);
+  a.o_scale = 1.f;
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.page_table = page_table;
+  a.prefix_lens = prefix_lens;
+  a.qo_start = qo_start;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.total_tokens = total_tokens;
+  a.lse = nullptr;
+  a.n_splits = 1;
+  a.split_tiles = 0;
+  a.split_o_stride = a.split_lse_stride = 0;
+  *bf16_out = bf16;
+  *out_f32_out = out_f32;
+  *run = true;
+  return ATTN_OK;
+}
 
 extern "C" {
 
@@ -465,59 +556,74 @@ int attn_extend(const void* q, const void* k, const void* v, const void* k_cache
                 const int32_t* qo_start, void* o, int B, int H, int H_kv, int D,
                 int total_tokens, int max_extend_len, int page_size, int num_pages,
                 int max_pages_per_seq, int dtype, float scale, hipStream_t stream) {
-  if (B < 0 || H < 0 || H_kv < 0 || total_tokens < 0 || max_extend_len < 0 || num_pages < 0 ||
-      max_pages_per_seq < 0)
-    return ATTN_E_INVALID;
-  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return ATTN_E_INVALID;
-  bool bf16, out_f32;
-  if (!parse_dtype(dtype, &bf16, &out_f32)) return ATTN_E_INVALID;
-  if (!isfinite(scale) || scale < 0.f) return ATTN_E_INVALID;
-  if (D != 64 && D != 128) return D <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
-  if (page_size != kDecodePageSize) return page_size <= 0 ? ATTN_E_INVALID : ATTN_E_UNSUPPORTED;
-  if ((int64_t)B * H * max_extend_len == 0 || total_tokens == 0) return ATTN_OK;
-  if (!q || !k || !v || !o || !qo_start) return ATTN_E_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_E_INVALID;
-  if ((uintptr_t)qo_start & 3u) return ATTN_E_INVALID;
-  if (max_pages_per_seq > 0) {  // prefixes may exist: the cache must be there
-    if (num_pages == 0 || !k_cache || !v_cache || !page_table || !prefix_lens)
-      return ATTN_E_INVALID;
-    if (!aligned16(k_cache) || !aligned16(v_cache)) return ATTN_E_INVALID;
-    if (((uintptr_t)page_table & 3u) || ((uintptr_t)prefix_lens & 3u)) return ATTN_E_INVALID;
-  }
-  // Row offsets within a sequence's new tokens are 32-bit in the kernel, and
-  // so are key positions (prefix plus new tokens).
-  if ((int64_t)max_extend_len * H * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
-  if ((int64_t)max_pages_per_seq * kDecodePageSize + max_extend_len >= ((int64_t)1 << 31))
-    return ATTN_E_UNSUPPORTED;
-  if ((int64_t)kDecodePageSize * H_kv * D * 2 >= ((int64_t)1 << 31)) return ATTN_E_UNSUPPORTED;
-
   PrefillArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = o;
-  a.H = H;
-  a.H_kv = H_kv;
-  a.group = H / H_kv;
-  a.Sq = max_extend_len;  // bounds every sequence's new tokens; sets the grid
-  a.Skv = 0;
-  a.causal_off = 0;
-  a.n_mtiles = 0;
-  a.total_tiles = 0;
-  a.q_sb = 0; a.q_sh = D; a.q_ss = H * D;          // [T, H, D]
-  a.k_sb = 0; a.k_sh = D; a.k_ss = H_kv * D;       // [T, H_kv, D]
-  a.c = exp2_multiplier(scale);
-  a.o_scale = 1.f;
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.page_table = page_table;
-  a.prefix_lens = prefix_lens;
-  a.qo_start = qo_start;
-  a.max_pages = max_pages_per_seq;
-  a.num_pages = num_pages;
-  a.total_tokens = total_tokens;
-  a.lse = nullptr;
+  bool bf16 = false, out_f32 = false, run = false;
+  const int st = prepare_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o,
+                                B, H, H_kv, D, total_tokens, max_extend_len, page_size,
+                                num_pages, max_pages_per_seq, dtype, scale, &a, &bf16, &out_f32,
+                                &run);
+  if (st != ATTN_OK || !run) return st;
   hipError_t e = launch_extend(D, bf16, out_f32, a, B, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+static bool extend_sizes_ok(int B, int H, int H_kv, int D, int total_tokens, int max_extend_len,
+                            int max_pages_per_seq) {
+  return B >= 0 && H >= 0 && H_kv >= 0 && total_tokens >= 0 && max_extend_len >= 0 &&
+         max_pages_per_seq >= 0 && (H == 0 || (H_kv > 0 && H % H_kv == 0)) &&
+         (D == 64 || D == 128);
+}
+
+int attn_extend_splitkv_num_splits(int B, int H, int H_kv, int D, int total_tokens,
+                                   int max_extend_len, int max_pages_per_seq) {
+  if (!extend_sizes_ok(B, H, H_kv, D, total_tokens, max_extend_len, max_pages_per_seq)) return 0;
+  if ((int64_t)B * H * max_extend_len == 0 || total_tokens == 0) return 1;
+  return plan_extend_splitkv(B, H, H_kv, D, total_tokens, max_extend_len, max_pages_per_seq)
+      .n_splits;
+}
+
+size_t attn_extend_splitkv_workspace_size(int B, int H, int H_kv, int D, int total_tokens,
+                                          int max_extend_len, int max_pages_per_seq) {
+  const int n = attn_extend_splitkv_num_splits(B, H, H_kv, D, total_tokens, max_extend_len,
+                                               max_pages_per_seq);
+  if (n <= 1) return 0;
+  const size_t rows = (size_t)total_tokens * H;
+  return (size_t)n * (align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)));
+}
+
+int attn_extend_splitkv(const void* q, const void* k, const void* v, const void* k_cache,
+                        const void* v_cache, const int32_t* page_table,
+                        const int32_t* prefix_lens, const int32_t* qo_start, void* o, int B,
+                        int H, int H_kv, int D, int total_tokens, int max_extend_len,
+                        int page_size, int num_pages, int max_pages_per_seq, int dtype,
+                        float scale, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  PrefillArgs a;
+  bool bf16 = false, out_f32 = false, run = false;
+  const int st = prepare_extend(q, k, v, k_cache, v_cache, page_table, prefix_lens, qo_start, o,
+                                B, H, H_kv, D, total_tokens, max_extend_len, page_size,
+                                num_pages, max_pages_per_seq, dtype, scale, &a, &bf16, &out_f32,
+                                &run);
+  if (st != ATTN_OK || !run) return st;
+  const SplitKvPlan p =
+      plan_extend_splitkv(B, H, H_kv, D, total_tokens, max_extend_len, max_pages_per_seq);
+  if (p.n_splits <= 1) {  // the grid fills the GPU: the plain extend
+    hipError_t e = launch_extend(D, bf16, out_f32, a, B, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  }
+  const size_t need = attn_extend_splitkv_workspace_size(B, H, H_kv, D, total_tokens,
+                                                         max_extend_len, max_pages_per_seq);
+  if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_E_INVALID;
+  const size_t rows = (size_t)total_tokens * H;
+  a.n_splits = p.n_splits;
+  a.split_tiles = p.split_tiles;
+  a.split_o_stride = (int64_t)rows * D;
+  a.split_lse_stride = (int64_t)rows;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             p.n_splits * align256(rows * D * sizeof(float)));
+  hipError_t e = launch_extend_splitkv(D, bf16, out_f32, a, B, part_o, part_lse, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -38,8 +38,8 @@ struct PrefillArgs {
   // Forward only: if not null, the natural log-sum-exp of each query row's
   // scaled logits, [B, H, Sq] fp32 (-inf for a row with no visible key).
   float* lse;
-  // Split-KV prefill only (launch_prefill_splitkv): the keys of each query
-  // tile are cut into n_splits ranges of split_tiles 64-key tiles.
+  // Split-KV prefill and extend only: the keys of each query tile are cut
+  // into n_splits ranges of split_tiles 64-key tiles.
   int n_splits, split_tiles;
   int64_t split_o_stride, split_lse_stride;  // elements between the partials' planes
 };
@@ -85,6 +85,12 @@ hipError_t launch_prefill_backward(int D, bool bf16, bool causal, bool out_f32,
 // Extend attention (causal over a paged prefix followed by the new tokens).
 hipError_t launch_extend(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
                          hipStream_t s);
+// Split-KV extend: the extend kernel over n_splits ranges of split_tiles key
+// tiles of each unit (prefix tiles first, then the new tokens'), partial O
+// (fp32, q's strides) and log-sum-exps ([H, total_tokens] per plane) into
+// part_o / part_lse, then a combine into a.o of the rows attn_extend writes.
+hipError_t launch_extend_splitkv(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
+                                 float* part_o, float* part_lse, hipStream_t s);
 
 // Paged decode (decode_gqa.hip).  H query heads share H_kv KV heads (group =
 // H / H_kv, 1 for multi-head attention): one wave per work range of the

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   // host pass only needs the kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(!(EXT && FP8), "extend takes fp16/bf16");
-  static_assert(!SPLIT || (OF32 && !EXT && HPW == 1), "split partials are fp32, dense, one head");
+  static_assert(!SPLIT || (OF32 && !FP8), "split partials are fp32; fp16/bf16 inputs");
   static_assert(NW % HPW == 0, "whole waves per query head");
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;
@@ -156,13 +156,21 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
   int e_r0 = 0, e_len = 0, e_pre = 0;  // sequence b's first row, new tokens, prefix
   bool e_known = false;                // whether those three are set (workgroup-uniform)
   if constexpr (EXT) {
-    const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv);
+    const int n_sp = SPLIT ? a.n_splits : 1;
+    const int nb = a.total_tiles / (a.n_mtiles * hgroups * a.H_kv * n_sp);
     if (nb <= 64 * kExtMaxPerLane) {
+      // SPLIT: a unit's key ranges follow its KV heads and head groups, so
+      // the same KV head still lands on the same XCD.
       int L = blockIdx.x;
       gg = L % hgroups;
       L /= hgroups;
       hk = L % a.H_kv;
-      const int u = L / a.H_kv;  // rank of the unit
+      L /= a.H_kv;
+      if constexpr (SPLIT) {
+        split = L % n_sp;
+        L /= n_sp;
+      }
+      const int u = L;  // rank of the unit
       // Lane l holds sequences k * 64 + l, k < PER: their first row, new
       // tokens and prefix length (an invalid row range counts as no rows),
       // and their query tiles and prefix in query-tile lengths.  PER = 1 for
@@ -255,7 +263,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
       e_pre = __builtin_amdgcn_readfirstlane(ext_unit[4]);
       e_known = true;
     } else {
-      int L = xcd_interleave((int)blockIdx.x, a.total_tiles / (a.n_mtiles * hgroups),
+      int w = (int)blockIdx.x;
+      if constexpr (SPLIT) {
+        split = w % n_sp;
+        w /= n_sp;
+      }
+      int L = xcd_interleave(w, a.total_tiles / (a.n_mtiles * hgroups * n_sp),
                              a.n_mtiles * hgroups);
       gg = L % hgroups;
       L /= hgroups;
@@ -291,6 +304,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     // new, bottom-right causal (offset = prefix length); the first n_pre tiles
     // hold prefix keys [0, P) from the cache, the rest new keys from k, v.
     int Sq = a.Sq, Skv = a.Skv, coff = a.causal_off, P = 0, n_pre = 0;
+    int row0 = 0;  // extend: the sequence's first row of q, k, v, o
     int64_t q_base = b * a.q_sb + h * a.q_sh;   // o shares q's element strides
     int64_t kv_base = b * a.k_sb + hk * a.k_sh;
     if constexpr (EXT) {
@@ -308,6 +322,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
       Skv = P + Sq;
       coff = P;
       n_pre = (P + BN - 1) / BN;
+      row0 = r0;
       q_base = (int64_t)r0 * a.q_ss + h * a.q_sh;
       kv_base = (int64_t)r0 * a.k_ss + hk * a.k_sh;
     }
@@ -359,11 +374,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     // Keys this wave needs: [0, wave_kv_end).
     const bool wave_active = q0 < Sq;
     const int wave_kv_end = CAUSAL ? min(Skv, min(q0 + 32, Sq) + coff) : Skv;
-    // First key (in the whole key sequence) of tile t, and whether it is a
-    // prefix tile (extend only).
-    auto is_pre = [&](int t) { return EXT && t < n_pre; };
+    // Tile t of this work item is tile gtile(t) of the item's keys; its first
+    // key (in the whole key sequence), and whether it is a prefix tile
+    // (extend only).
+    auto gtile = [&](int t) { return SPLIT ? kt0 + t : t; };
+    auto is_pre = [&](int t) { return EXT && gtile(t) < n_pre; };
     auto tile_key0 = [&](int t) {
-      return EXT ? (t < n_pre ? t * BN : P + (t - n_pre) * BN) : (kt0 + t) * BN;
+      const int g = gtile(t);
+      return EXT ? (g < n_pre ? g * BN : P + (g - n_pre) * BN) : g * BN;
     };
 
     // ---- K/V staging addresses (loop invariant).  Load i of this thread fills
@@ -418,8 +436,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
     static_assert(PPT == 4, "page ids of a tile are held by lanes j & 3");
     int pgv_next = 0;
     auto fetch_pages = [&](int t) {
-      const int tok = t * BN + (lane & 3) * kDecodePageSize;
-      pgv_next = (EXT && t < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : 0;
+      const int tok = gtile(t) * BN + (lane & 3) * kDecodePageSize;
+      pgv_next = (EXT && gtile(t) < n_pre && tok < P) ? ptab[tok / kDecodePageSize] : 0;
     };
     // Every wave checks every page of the tile (as unsigned, so negative ids
     // are rejected too), so all waves agree.
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
         __builtin_amdgcn_make_buffer_rsrc((void*)a.k_cache, (short)0, 0, kBufferConfig);
     __amdgpu_buffer_rsrc_t pv_rsrc = pk_rsrc;
     auto set_page_rsrc = [&](int t) {
-      const int live = min(kDecodePageSize, P - (t * BN + wpage * kDecodePageSize));
+      const int live = min(kDecodePageSize, P - (gtile(t) * BN + wpage * kDecodePageSize));
       const int64_t off = live > 0 ? (int64_t)__builtin_amdgcn_readlane(pgv_next, wpage) * page_elems
                                    : 0;
       const int nbytes = __builtin_amdgcn_readfirstlane(max(live, 0) * (int)slot_bytes);
@@ -735,9 +753,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_fwd_kernel(PrefillArgs a) 
                               : a.o;
     if (lse_out != nullptr && q_ok && hi == 0) {
       // log2-sum-exp of s c is m_run + log2(l); the natural one of s scale is
-      // that times ln 2.
-      const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
-      lse_out[((int64_t)b * a.H + h) * Sq + qi] = lse2 * 0.6931471805599453f;
+      // that times ln 2.  A split that met a rejected prefix page passes NaN
+      // on, so the merged row is NaN too.  Split extend rows are token-major:
+      // the log-sum-exps are [H, total_tokens].
+      const float lse2 = (SPLIT && bad_page) ? __builtin_nanf("")
+                         : l_tot > 0.f       ? m_run + __log2f(l_tot)
+                                             : kNegInf;
+      const int64_t li_row = (EXT && SPLIT) ? (int64_t)h * a.total_tokens + row0 + qi
+                                            : ((int64_t)b * a.H + h) * Sq + qi;
+      lse_out[li_row] = lse2 * 0.6931471805599453f;
     }
     // A rejected prefix page makes the rows NaN (the key set is unknown).
     const float inv =
@@ -832,35 +856,33 @@ hipError_t launch_prefill(int D, bool bf16, bool causal, bool out_f32, const Pre
 
 namespace {
 
-// Merge of the split-KV partials: for each query row (b, h, i), the mean of
-// the splits' normalised partial rows weighted by exp(lse_s - max lse); a
-// row no split saw (every lse_s = -inf) gets O = 0.  Eight rows per 64-lane
-// workgroup, eight lanes per row, each lane D/8 consecutive outputs.
+// Merge of one query row's split-KV partials: the mean of the splits'
+// normalised partial rows weighted by exp(lse_s - max lse).  A row no split
+// saw (every lse_s = -inf) gets O = 0; a row with a NaN log-sum-exp (a split
+// that met a rejected prefix page, or NaN inputs) gets NaN.  Eight lanes per
+// row: lane k of the row owns the D/8 consecutive outputs at element `off`
+// of o (and of each partial plane); lrow indexes the log-sum-exp planes.
 template <int D, bool BF16, bool OF32>
-__global__ __launch_bounds__(64) void prefill_split_combine_kernel(PrefillArgs a, int B,
-                                                                   const float* part_o,
-                                                                   const float* part_lse) {
+__device__ __forceinline__ void merge_split_row(const PrefillArgs& a, const float* part_o,
+                                                const float* part_lse, int64_t lrow,
+                                                int64_t off) {
   constexpr int E = D / 8;  // outputs per lane
   constexpr float kLog2e = 1.4426950408889634f;
-  const int lane = threadIdx.x;
-  const int k = lane & 7;
-  const int64_t row = (int64_t)blockIdx.x * 8 + (lane >> 3);
-  if (row >= (int64_t)B * a.H * a.Sq) return;  // whole 8-lane groups leave together
-  const int qi = (int)(row % a.Sq);
-  const int64_t bh = row / a.Sq;
-  const int h = (int)(bh % a.H);
-  const int64_t b = bh / a.H;
-  const int64_t off = b * a.q_sb + h * a.q_sh + (int64_t)qi * a.q_ss + k * E;
   float m = kNegInf;
-  for (int sp = 0; sp < a.n_splits; ++sp) m = fmaxf(m, part_lse[sp * a.split_lse_stride + row]);
+  bool nan = false;
+  for (int sp = 0; sp < a.n_splits; ++sp) {
+    const float x = part_lse[sp * a.split_lse_stride + lrow];
+    nan |= x != x;
+    m = fmaxf(m, x);
+  }
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (m != kNegInf) {
+  if (m != kNegInf && !nan) {
     for (int sp = 0; sp < a.n_splits; ++sp) {
       const float w =
-          __builtin_amdgcn_exp2f((part_lse[sp * a.split_lse_stride + row] - m) * kLog2e);
+          __builtin_amdgcn_exp2f((part_lse[sp * a.split_lse_stride + lrow] - m) * kLog2e);
       const f32x4* src = reinterpret_cast<const f32x4*>(part_o + sp * a.split_o_stride + off);
       wsum += w;
 #pragma unroll
@@ -871,7 +893,7 @@ __global__ __launch_bounds__(64) void prefill_split_combine_kernel(PrefillArgs a
       }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float inv = nan ? __builtin_nanf("") : (wsum > 0.f ? 1.f / wsum : 0.f);
   if constexpr (OF32) {
     f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + off);
 #pragma unroll
@@ -891,6 +913,44 @@ __global__ __launch_bounds__(64) void prefill_split_combine_kernel(PrefillArgs a
       dst[c] = w4;
     }
   }
+}
+
+// Combine of split-KV prefill: query row (b, h, i) is row (b * H + h) * Sq + i
+// of the log-sum-exp planes; eight rows per 64-lane workgroup.
+template <int D, bool BF16, bool OF32>
+__global__ __launch_bounds__(64) void prefill_split_combine_kernel(PrefillArgs a, int B,
+                                                                   const float* part_o,
+                                                                   const float* part_lse) {
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (lane >> 3);
+  if (row >= (int64_t)B * a.H * a.Sq) return;  // whole 8-lane groups leave together
+  const int qi = (int)(row % a.Sq);
+  const int64_t bh = row / a.Sq;
+  const int h = (int)(bh % a.H);
+  const int64_t b = bh / a.H;
+  const int64_t off = b * a.q_sb + h * a.q_sh + (int64_t)qi * a.q_ss + (lane & 7) * (D / 8);
+  merge_split_row<D, BF16, OF32>(a, part_o, part_lse, row, off);
+}
+
+// Combine of split-KV extend: workgroup (x, y) merges rows 8 * (x / H) ..
+// +7 of query head x % H of sequence y, each the token qo_start[y] + i, row
+// h * total_tokens + token of the log-sum-exp planes.  It writes exactly the
+// rows the extend kernel computes: those of a sequence whose qo_start range
+// lies in [0, total_tokens], below max_extend_len (a.Sq).
+template <int D, bool BF16, bool OF32>
+__global__ __launch_bounds__(64) void extend_split_combine_kernel(PrefillArgs a,
+                                                                  const float* part_o,
+                                                                  const float* part_lse) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.y;
+  const int h = (int)(blockIdx.x % (unsigned)a.H);
+  const int i = (int)(blockIdx.x / (unsigned)a.H) * 8 + (lane >> 3);
+  const int r0 = a.qo_start[b], r1 = a.qo_start[b + 1];
+  if (r0 < 0 || r1 < r0 || r1 > a.total_tokens) return;  // not computed
+  if (i >= min(r1 - r0, a.Sq)) return;                    // whole 8-lane groups
+  const int64_t tok = (int64_t)r0 + i;
+  const int64_t off = tok * a.q_ss + h * a.q_sh + (lane & 7) * (D / 8);
+  merge_split_row<D, BF16, OF32>(a, part_o, part_lse, (int64_t)h * a.total_tokens + tok, off);
 }
 
 template <int D, bool BF16, bool CAUSAL>
@@ -941,6 +1001,60 @@ hipError_t launch_prefill_splitkv(int D, bool bf16, bool causal, bool out_f32,
                                   hipStream_t s) {
   if (D == 128) return launch_split_d<128>(bf16, causal, out_f32, a, B, part_o, part_lse, s);
   if (D == 64) return launch_split_d<64>(bf16, causal, out_f32, a, B, part_o, part_lse, s);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+// Split-KV extend: the extend kernel in SPLIT mode (the grid of attn_extend
+// times n_splits, four query heads per workgroup when the group allows it),
+// then the extend combine over (row block, head) x sequence.
+template <int D, bool BF16, int HPW>
+hipError_t launch_ext_split_t(const PrefillArgs& a, int B, float* part_o, float* part_lse,
+                              bool out_f32, hipStream_t s) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int BN = 64;
+  constexpr int RPW = 32 * NW / HPW;
+  const int64_t n_mtiles = (a.Sq + RPW - 1) / RPW;
+  const int64_t total = (int64_t)B * (a.H / HPW) * n_mtiles * a.n_splits;
+  const int64_t gx = (int64_t)((a.Sq + 7) / 8) * a.H;
+  if (total >= ((int64_t)1 << 31) || gx >= ((int64_t)1 << 31) || B > 65535)
+    return hipErrorInvalidValue;
+  PrefillArgs p = a;
+  p.o = part_o;
+  p.lse = part_lse;
+  p.n_mtiles = (int)n_mtiles;
+  p.pair_tiles = 0;
+  p.total_tiles = (int)total;
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, true, true, NW, BN, true, false, HPW, true>),
+                     dim3(p.total_tiles), dim3(64 * NW), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)gx, (unsigned)B);
+  if (out_f32)
+    hipLaunchKernelGGL((extend_split_combine_kernel<D, BF16, true>), grid, dim3(64), 0, s, a,
+                       part_o, part_lse);
+  else
+    hipLaunchKernelGGL((extend_split_combine_kernel<D, BF16, false>), grid, dim3(64), 0, s, a,
+                       part_o, part_lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_ext_split_d(bool bf16, bool out_f32, const PrefillArgs& a, int B,
+                              float* part_o, float* part_lse, hipStream_t s) {
+  const bool g4 = a.group % 4 == 0;
+  if (bf16)
+    return g4 ? launch_ext_split_t<D, true, 4>(a, B, part_o, part_lse, out_f32, s)
+              : launch_ext_split_t<D, true, 1>(a, B, part_o, part_lse, out_f32, s);
+  return g4 ? launch_ext_split_t<D, false, 4>(a, B, part_o, part_lse, out_f32, s)
+            : launch_ext_split_t<D, false, 1>(a, B, part_o, part_lse, out_f32, s);
+}
+}  // namespace
+
+hipError_t launch_extend_splitkv(int D, bool bf16, bool out_f32, const PrefillArgs& a, int B,
+                                 float* part_o, float* part_lse, hipStream_t s) {
+  if (D == 128) return launch_ext_split_d<128>(bf16, out_f32, a, B, part_o, part_lse, s);
+  if (D == 64) return launch_ext_split_d<64>(bf16, out_f32, a, B, part_o, part_lse, s);
   return hipErrorInvalidValue;
 }
 

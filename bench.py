@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11,12,13]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--configs 2,1,3,4,5,6,7,8,9,10,11,12,13,14]
 
 One step is one pass of the prefill hot path (grid order, Q/K/V staging,
 Q.K^T on MFMA, masking, online softmax, P.V on MFMA, epilogue: one
@@ -12,8 +12,9 @@ step).  The other workloads (tiny 128x128, causal BSHD bf16 8k, paged
 decode, long causal 32k, grouped-query causal 8k, grouped-query and
 multi-query paged decode, extend after a paged prefix, fp8 prefill, the
 backward of the causal 8k workload with and without grouped KV heads, and a
-512-token chunk against 32k keys through the split-KV prefill) are measured the same way and reported
-under "extra", decode in GB/s of algorithmic K/V bytes, the backward in
+512-token chunk against 32k keys through the split-KV prefill and through
+the split-KV extend after a 32k-token paged prefix) are measured the same way
+and reported under "extra", decode in GB/s of algorithmic K/V bytes, the backward in
 TFLOP/s of its five products (2.5x the forward's flops).
 
 Timing: W untimed warmup steps, then K timed steps on the stream the kernels
@@ -402,11 +403,17 @@ def bench_extend(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
     o = torch.empty_like(g["q"])
     stream = torch.cuda.current_stream()
     mx = batch.max_extend_len
+    split = workloads.EXTEND_CONFIGS[cfg].get("splitkv", False)
+    sizes = (len(batch.prefix_lens), batch.q.shape[1], batch.k.shape[1], batch.q.shape[2],
+             batch.q.shape[0], mx, batch.page_table.shape[1])
+    ws = (torch.empty(max(attn.attn_extend_splitkv_workspace_size(*sizes), 1), dtype=torch.uint8,
+                      device="cuda") if split else None)
 
     def step():
-        attn.extend(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
-                    g["prefix_lens"], g["qo_start"], max_extend_len=mx, scale=batch.meta["scale"],
-                    out=o, stream=stream)
+        f = attn.extend_splitkv if split else attn.extend
+        kw = dict(workspace=ws) if split else {}
+        f(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"], g["prefix_lens"],
+          g["qo_start"], max_extend_len=mx, scale=batch.meta["scale"], out=o, stream=stream, **kw)
 
     t = measure(step, steps, warmup, stream, clock)
     flops = extend_flops(batch)
@@ -415,10 +422,13 @@ def bench_extend(attn, cfg, steps, warmup, clock, cpu_budget=0.0):
                "H": batch.q.shape[1], "H_kv": batch.k.shape[1], "D": batch.q.shape[2],
                "dtype": batch.meta["dtype"], "new_tokens": int(batch.q.shape[0]),
                "prefix_tokens": int(batch.prefix_lens.sum()), "max_extend_len": mx}
+    if split:
+        cfg_out["entry_point"] = "attn_extend_splitkv"
+        cfg_out["key_splits"] = attn.attn_extend_splitkv_num_splits(*sizes)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16, 4),
             "traffic": load_traffic(f"prefill_fwd__{batch.meta['name']}", PREFILL_SRC)}
-    del g, o
+    del g, o, ws
     torch.cuda.empty_cache()
     cpu = cpu_baseline_extend(batch, cpu_budget) if cpu_budget > 0 else None
     return dict(config=cfg_out, timing=t, flops_per_step=flops, tflops=tflops, roofline=roof,
@@ -683,7 +693,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11,12,13",
+    ap.add_argument("--configs", default="2,1,3,4,5,6,7,8,9,10,11,12,13,14",
                     help="workloads to measure; the first prefill one is the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GFX clock windows")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache passes")

@@ -252,6 +252,50 @@ int attn_extend(const void* q, const void* k, const void* v,
                 hipStream_t stream);
 
 /*
+ * attn_extend for grids too small to fill the GPU (few sequences and new
+ * tokens after long cached prefixes: chunked prefill of one long prompt
+ * through the paged cache): each unit's keys (its prefix tiles, then its new
+ * tokens' tiles) are split across workgroups, each writing a partial output
+ * and log-sum-exp into the workspace, and a second kernel merges them by
+ * log-sum-exp (flash decoding applied to extend: "Wave February 2025
+ * Release", FlashDecoding list and Extend Attention, split-k; the KV split
+ * sized to fill the GPU: "[FlyDSL] FP8 MQA logits improvements for gfx950",
+ * Changes / Host side).  The split count comes from sizes only
+ * (attn_extend_splitkv_num_splits, from the bounds max_extend_len and
+ * max_pages_per_seq * 16); with one split this is attn_extend, needs no
+ * workspace and gives its result bitwise.  Otherwise the result is
+ * attn_extend's up to the rounding of the merge, and the rows written are
+ * the same: rows of sequences whose qo_start range is invalid, and rows past
+ * max_extend_len, are not written; a rejected prefix page makes the
+ * sequence's rows NaN.
+ *
+ *   workspace: device scratch of at least attn_extend_splitkv_workspace_size
+ *       bytes (0: may be NULL), 16-byte aligned, owned by the caller; its
+ *       contents need no initialisation.  ATTN_E_WORKSPACE if missing or small.
+ * Every other argument and error as in attn_extend.
+ */
+int attn_extend_splitkv(const void* q, const void* k, const void* v,
+                        const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* prefix_lens,
+                        const int32_t* qo_start, void* o, int B, int H, int H_kv, int D,
+                        int total_tokens, int max_extend_len, int page_size, int num_pages,
+                        int max_pages_per_seq, int dtype, float scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Key splits per unit attn_extend_splitkv uses for these sizes (1: no split,
+ * also when there is nothing to compute; 0 for invalid sizes), by the model
+ * of attn_prefill_splitkv_num_splits over attn_extend's grid: units of
+ * max_extend_len new tokens after max_pages_per_seq * 16 prefix tokens. */
+int attn_extend_splitkv_num_splits(int B, int H, int H_kv, int D, int total_tokens,
+                                   int max_extend_len, int max_pages_per_seq);
+
+/* Workspace bytes of attn_extend_splitkv (0 when it does not split): per
+ * split, fp32 partial outputs [total_tokens*H*D] and log-sum-exps
+ * [H*total_tokens], each array padded to 256 bytes. */
+size_t attn_extend_splitkv_workspace_size(int B, int H, int H_kv, int D, int total_tokens,
+                                          int max_extend_len, int max_pages_per_seq);
+
+/*
  * Bytes of device workspace attn_paged_decode needs for these sizes: the
  * partial outputs and log-sum-exps of the work ranges, and the ranges'
  * metadata.  Returns 0 for invalid sizes.

@@ -32,7 +32,9 @@ def test_header_declares_the_boundary():
                             "attn_prefill_bwd_workspace_size",
                             "attn_paged_decode_gqa_noalloc", "attn_prefill_splitkv",
                             "attn_prefill_splitkv_num_splits",
-                            "attn_prefill_splitkv_workspace_size"])
+                            "attn_prefill_splitkv_workspace_size", "attn_extend_splitkv",
+                            "attn_extend_splitkv_num_splits",
+                            "attn_extend_splitkv_workspace_size"])
     assert set(names) == set(attn.SIGNATURES)
 
 
@@ -332,6 +334,55 @@ def _extend(**kw):
 ])
 def test_extend_validation(kw, status):
     assert _extend(**kw) == status
+    # the split form checks its arguments the same way, before the workspace
+    assert _extend_split(**kw) == status
+
+
+def _extend_split(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, k_cache=FAKE, v_cache=FAKE, page_table=FAKE,
+             prefix_lens=FAKE, qo_start=FAKE, o=FAKE, B=1, H=8, H_kv=2, D=128, total_tokens=300,
+             max_extend_len=300, page_size=16, num_pages=512, max_pages_per_seq=250, dtype=1,
+             scale=0.1, workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+    a.update(kw)
+    return attn.attn_extend_splitkv(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # this batch splits: a workspace is required, big enough, 16-byte aligned
+    (dict(workspace=None), attn.ATTN_E_WORKSPACE),
+    (dict(workspace_bytes=1024), attn.ATTN_E_WORKSPACE),
+    (dict(workspace=FAKE + 8), attn.ATTN_E_INVALID),
+    (dict(H_kv=3), attn.ATTN_E_INVALID),
+    (dict(D=96), attn.ATTN_E_UNSUPPORTED),
+])
+def test_extend_splitkv_validation(kw, status):
+    assert _extend_split(**kw) == status
+
+
+def test_extend_splitkv_empty_is_a_noop():
+    assert _extend_split(B=0, q=None, k=None, v=None, o=None, qo_start=None, workspace=None,
+                         workspace_bytes=0) == attn.ATTN_OK
+    assert _extend_split(max_extend_len=0, workspace=None, workspace_bytes=0) == attn.ATTN_OK
+
+
+def test_extend_splitkv_plan_and_workspace():
+    f, w = attn.attn_extend_splitkv_num_splits, attn.attn_extend_splitkv_workspace_size
+    # a 512-token chunk after up to 32k prefix tokens, H32/8: 8 head groups x
+    # 8 query tiles of 64 rows = 64 units; 4 splits fill the 256 CUs once
+    assert f(1, 32, 8, 128, 512, 512, 2048) == 4
+    assert w(1, 32, 8, 128, 512, 512, 2048) == 4 * (512 * 32 * 128 * 4 + 512 * 32 * 4)
+    # a ragged batch of 8 long sequences already fills the GPU: no split
+    assert f(8, 32, 8, 128, 8192, 1872, 366) == 1
+    assert w(8, 32, 8, 128, 8192, 1872, 366) == 0
+    # fewer than 16 key tiles (no prefix, 300 new tokens): no split
+    assert f(1, 8, 2, 128, 300, 300, 0) == 1
+    # nothing to compute: one split, no workspace; invalid sizes: 0
+    assert f(0, 8, 2, 128, 300, 300, 8) == 1
+    assert w(0, 8, 2, 128, 300, 300, 8) == 0
+    assert f(1, 8, 3, 128, 300, 300, 8) == 0
+    assert f(1, 8, 2, 80, 300, 300, 8) == 0
+    assert f(1, 8, 2, 128, -1, 300, 8) == 0
+    assert w(1, 8, 2, 128, 300, 300, -1) == 0
 
 
 def test_extend_empty_is_a_noop():

@@ -58,7 +58,8 @@ def test_graph_capture_and_replay(gpu_lib):
 def test_graph_capture_backward_extend_fp8(gpu_lib):
     """The other entry points in one captured graph: forward with LSE,
     backward, extend after a paged prefix, fp8 prefill, grouped-query decode
-    and split-KV prefill, replayed three times against the eager results."""
+    and split-KV prefill and extend, replayed three times against the eager
+    results."""
     attn = gpu_lib
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev) for t in workloads.backward_inputs(1, 8, 200, 260, 128, "bf16",
@@ -89,7 +90,15 @@ def test_graph_capture_backward_extend_fp8(gpu_lib):
     sws = torch.empty(attn.attn_prefill_splitkv_workspace_size(1, 4, 100, 3000, 128),
                       dtype=torch.uint8, device=dev)
     o_split = torch.empty_like(qs)
-    outs = (o, lse, dq, dk, dv, o_ext, o8, o_dec, o_split)
+    x = workloads.extend_inputs(2, 8, 128, [1700, 300], [90, 40], "bf16", seed=38, h_kv=2)
+    gx = {n: getattr(x, n).to(dev) for n in ("q", "k", "v", "k_cache", "v_cache", "page_table",
+                                             "prefix_lens", "qo_start")}
+    xargs = (2, 8, 2, 128, x.q.shape[0], x.max_extend_len, x.page_table.shape[1])
+    assert attn.attn_extend_splitkv_num_splits(*xargs) > 1
+    xws = torch.empty(attn.attn_extend_splitkv_workspace_size(*xargs), dtype=torch.uint8,
+                      device=dev)
+    o_xsplit = torch.empty_like(gx["q"])
+    outs = (o, lse, dq, dk, dv, o_ext, o8, o_dec, o_split, o_xsplit)
 
     def work(stream=None):
         attn.prefill_with_lse(q, k, v, causal=True, layout="BSHD", out=o, lse=lse, stream=stream)
@@ -102,8 +111,13 @@ def test_graph_capture_backward_extend_fp8(gpu_lib):
         attn.paged_decode(gd["q"], gd["k_cache"], gd["v_cache"], gd["page_table"],
                           gd["seq_lens"], out=o_dec, workspace=dws, stream=stream)
         attn.prefill_splitkv(qs, ks, vs, causal=True, out=o_split, workspace=sws, stream=stream)
+        attn.extend_splitkv(gx["q"], gx["k"], gx["v"], gx["k_cache"], gx["v_cache"],
+                            gx["page_table"], gx["prefix_lens"], gx["qo_start"],
+                            max_extend_len=x.max_extend_len, out=o_xsplit, workspace=xws,
+                            stream=stream)
 
-    print("[case] graph capture of lse/backward/extend/fp8/gqa decode/split-kv", flush=True)
+    print("[case] graph capture of lse/backward/extend/fp8/gqa decode/split-kv prefill and "
+          "extend", flush=True)
     work()
     torch.cuda.synchronize()
     refs = [t.clone() for t in outs]

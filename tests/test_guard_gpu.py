@@ -133,3 +133,23 @@ def test_prefill_splitkv_stays_in_bounds(gpu_lib, layout, causal):
     torch.cuda.synchronize()
     assert bool((wbuf[:GUARD_BYTES] == SENTINEL).all()) and \
         bool((wbuf[wbuf.numel() - GUARD_BYTES:] == SENTINEL).all()), "workspace overrun"
+
+
+def test_extend_splitkv_stays_in_bounds(gpu_lib):
+    attn = gpu_lib
+    pl, el = [1300, 0, 2500, 17], [100, 33, 0, 150]
+    batch = workloads.extend_inputs(4, 8, 128, pl, el, "bf16", seed=98, h_kv=2)
+    g = {n: getattr(batch, n).cuda() for n in ("q", "k", "v", "k_cache", "v_cache",
+                                              "page_table", "prefix_lens", "qo_start")}
+    T, H, D = batch.q.shape
+    args = (4, H, 2, D, T, max(el), batch.page_table.shape[1])
+    assert attn.attn_extend_splitkv_num_splits(*args) > 1
+    print("[case] guard split-kv extend", flush=True)
+    buf, o = _guarded(tuple(batch.q.shape), torch.bfloat16)
+    wbuf, ws = _guarded((attn.attn_extend_splitkv_workspace_size(*args),), torch.uint8)
+    attn.extend_splitkv(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"], g["page_table"],
+                        g["prefix_lens"], g["qo_start"], out=o, workspace=ws)
+    _check(buf, o, "split-kv extend o")
+    torch.cuda.synchronize()
+    assert bool((wbuf[:GUARD_BYTES] == SENTINEL).all()) and \
+        bool((wbuf[wbuf.numel() - GUARD_BYTES:] == SENTINEL).all()), "workspace overrun"

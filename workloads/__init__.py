@@ -86,6 +86,11 @@ DECODE_CONFIGS = {
 EXTEND_CONFIGS = {
     9: dict(name="extend-gqa-b8", B=8, H=32, H_kv=8, D=128, dtype="bf16", page_size=16,
             min_prefix=0, max_prefix=8192, min_extend=256, max_extend=2048),
+    # one step of chunked prefill through the paged cache: a 512-token chunk
+    # of a long prompt after its first 32768 tokens, through attn_extend_splitkv
+    14: dict(name="chunk-extend-512-at-32k", B=1, H=32, H_kv=8, D=128, dtype="bf16",
+             page_size=16, min_prefix=32768, max_prefix=32768, min_extend=512, max_extend=512,
+             splitkv=True),
 }
 
 
