@@ -1,6 +1,6 @@
 """A seeded sweep of random shapes through prefill (with and without the LSE
-output), split-KV prefill, grouped-query decode, extend, the backward and
-fp8 prefill (with
+output), split-KV prefill, grouped-query decode, extend and split-KV
+extend, the backward and fp8 prefill (with
 the output in the input type or, in some draws, in fp32), each
 against the fp64 oracle at its bar.  The draws mix batch, head counts and
 grouping, lengths on and off tile boundaries (including Sq > Skv under the
@@ -84,6 +84,44 @@ def test_prefill_splitkv_random(gpu_lib, i):
     assert torch.isfinite(o.float()).all()
     ref = oracle.sdpa(q, k, v, causal=c["causal"], scale=c["scale"], layout=c["layout"])
     assert_parity(o.double().cpu().numpy(), ref, f"splitkv random {i}")
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_extend_splitkv_random(gpu_lib, i):
+    """Split-KV extend on random small batches (1-3 sequences, prefixes up
+    to 6k tokens, so that the plan splits), NaN in the cache's free slots,
+    the output and the workspace."""
+    r = np.random.default_rng(7000 + i)
+    H_kv = int(r.choice([1, 2]))
+    H = H_kv * int(r.choice([1, 2, 4]))
+    B = int(r.integers(1, 4))
+    pl = r.integers(0, 6000, B).tolist()
+    pl[0] = int(r.integers(1500, 6000))
+    el = r.integers(1, 300, B).tolist()
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["f16", "bf16"]))
+    scale = float(r.uniform(0.02, 0.3))
+    batch = workloads.extend_inputs(B, H, D, pl, el, dtype, seed=7500 + i, h_kv=H_kv,
+                                    fill=float("nan"))
+    T = batch.q.shape[0]
+    sizes = (B, H, H_kv, D, T, max(el), batch.page_table.shape[1])
+    n = gpu_lib.attn_extend_splitkv_num_splits(*sizes)
+    print(f"[case] extend splitkv random {i}: B{B} H{H}/{H_kv} D{D} {dtype} prefix {pl} "
+          f"new {el} splits {n}", flush=True)
+    assert n > 1
+    g = {m: getattr(batch, m).cuda() for m in ("q", "k", "v", "k_cache", "v_cache", "page_table",
+                                              "prefix_lens", "qo_start")}
+    out = torch.full(batch.q.shape, float("nan"), dtype=batch.q.dtype, device="cuda")
+    ws = torch.full((gpu_lib.attn_extend_splitkv_workspace_size(*sizes),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    o = gpu_lib.extend_splitkv(g["q"], g["k"], g["v"], g["k_cache"], g["v_cache"],
+                               g["page_table"], g["prefix_lens"], g["qo_start"], scale=scale,
+                               out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    ref = oracle.extend(batch.q, batch.k, batch.v, batch.k_cache, batch.v_cache,
+                        batch.page_table, batch.prefix_lens, batch.qo_start, scale=scale)
+    assert_parity(o.double().cpu().numpy(), ref, f"extend splitkv random {i}")
 
 
 @pytest.mark.parametrize("i", range(18))
